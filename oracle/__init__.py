@@ -1,0 +1,7 @@
+"""CPU oracle for the SVDQuant W4A4 linear layer (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package; the GPU library never does.
+"""
+from .svdq_oracle import *  # noqa: F401,F403
+from .svdq_oracle import INT4_GROUP, FP4_BLOCK, E2M1_GRID  # noqa: F401
