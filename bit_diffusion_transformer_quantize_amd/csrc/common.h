@@ -1,0 +1,82 @@
+// Device-side helpers shared by the gfx950 kernels of libsvdq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even.  Inputs here are
+// finite; NaN is not special-cased.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two fp32 -> one dword of two bf16 (lo in bits 0..15), RNE.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// INT4 code of v for a nonzero scale s: clamp(rint(fp32(v / s)), -8, 7).
+// The division is the IEEE-correctly-rounded fp32 quotient.
+__device__ __forceinline__ int int4_code(float v, float s) {
+  float q = __builtin_rintf(v / s);
+  q = fminf(fmaxf(q, -8.0f), 7.0f);
+  return (int)q;
+}
+
+// E2M1 magnitude index (0..7) of |y| < 8: nearest grid point of
+// {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even index, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_index(float a) {
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c;
+}
+
+// 4-bit E2M1 sign-magnitude code of y (sign taken from the sign bit, so -0
+// keeps it).
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  return e2m1_index(fabsf(y)) | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// E8M0 exponent for a block with absolute maximum a >= 0:
+// e = clamp(floor(log2 a) - 2, -127, 127), e = -127 for a == 0.  floor(log2 a)
+// is read from the exponent field; any a below 2^-125 clamps to -127.
+__device__ __forceinline__ int e8m0_exponent(float a) {
+  int eb = (int)((__float_as_uint(a) >> 23) & 0xFFu);
+  if (eb == 0) return -127;
+  int e = eb - 127 - 2;
+  return e < -127 ? -127 : e;
+}
+
+// 2^k as fp32 for -126 <= k <= 127.
+__device__ __forceinline__ float exp2i(int k) {
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// Nibble unpack of 8 two's-complement int4 codes (one dword, element 2j in
+// the low nibble of byte j) into int8 lanes holding 16*q: `even` gets the
+// even elements, `odd` the odd ones.  Products of two such bytes carry a
+// factor 256, removed with the scale.
+__device__ __forceinline__ void int4x8_to_int8x16(uint32_t w, uint32_t& even, uint32_t& odd) {
+  even = (w << 4) & 0xF0F0F0F0u;
+  odd = w & 0xF0F0F0F0u;
+}
+
+}  // namespace svdq

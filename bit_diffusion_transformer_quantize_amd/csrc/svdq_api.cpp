@@ -1,0 +1,178 @@
+// C ABI of libsvdq: argument validation (before any HIP call), the gfx950
+// capability check, and the kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/svdq.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+svdq_status check_desc(const svdq_desc* d) {
+  if (d == nullptr) return SVDQ_ERR_ARG;
+  if (d->mode != SVDQ_MODE_INT4 && d->mode != SVDQ_MODE_FP4) return SVDQ_ERR_ARG;
+  if ((d->flags & ~SVDQ_FLAG_OUT_F32) != 0u) return SVDQ_ERR_ARG;
+  if (d->K <= 0 || d->K % 128 != 0 || d->K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (d->N <= 0 || d->N % 128 != 0 || d->N > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (d->rank < 0 || d->rank > 256 || d->rank % 16 != 0) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+
+svdq_status check_rows(int64_t M) {
+  if (M < 1 || M > (int64_t(1) << 31)) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+
+// Required pointer: non-null and 16-byte aligned.
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+// Optional pointer: null, or 16-byte aligned.
+bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+svdq_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SVDQ_ERR_HIP;
+  if (dev < 0) return SVDQ_ERR_HIP;
+  if (dev < kMaxDevices) {
+    const int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return SVDQ_OK;
+    if (st == 2) return SVDQ_ERR_ARCH;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SVDQ_ERR_HIP;
+  const bool ok = svdq_arch_supported(prop.gcnArchName) != 0;
+  if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? SVDQ_OK : SVDQ_ERR_ARCH;
+}
+
+svdq_status from_hip(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP; }
+
+#define SVDQ_TRY(expr)                 \
+  do {                                 \
+    const svdq_status st_ = (expr);    \
+    if (st_ != SVDQ_OK) return st_;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* svdq_status_string(svdq_status s) {
+  switch (s) {
+    case SVDQ_OK: return "SVDQ_OK";
+    case SVDQ_ERR_ARG: return "SVDQ_ERR_ARG: null or misaligned pointer, or bad mode/flags";
+    case SVDQ_ERR_SHAPE: return "SVDQ_ERR_SHAPE: size outside the supported limits";
+    case SVDQ_ERR_ARCH: return "SVDQ_ERR_ARCH: current device is not gfx950";
+    case SVDQ_ERR_HIP: return "SVDQ_ERR_HIP: HIP runtime error";
+  }
+  return "SVDQ_ERR_UNKNOWN";
+}
+
+int svdq_arch_supported(const char* name) {
+  if (name == nullptr) return 0;
+  if (std::strncmp(name, "gfx950", 6) != 0) return 0;
+  const char c = name[6];
+  return (c == '\0' || c == ':') ? 1 : 0;
+}
+
+const char* svdq_version(void) { return "0.1.0"; }
+
+svdq_status svdq_calibrate_lambda(int64_t M, int32_t K, int32_t N, const uint16_t* X,
+                                  const uint16_t* W, float* lambda, void* stream) {
+  if (!ptr_ok(X) || !ptr_ok(W) || !ptr_ok(lambda)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_rows(M));
+  if (N < 1 || N > (1 << 24) || K <= 0 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_calibrate_lambda(M, K, N, X, W, lambda, (hipStream_t)stream));
+}
+
+svdq_status svdq_pack_weight(const svdq_desc* d, const uint16_t* W, const float* lambda,
+                             const uint16_t* lora_down, const uint16_t* lora_up,
+                             uint8_t* wcodes, void* wscales, void* stream) {
+  SVDQ_TRY(check_desc(d));
+  if (!ptr_ok(W) || !ptr_ok(lambda) || !ptr_ok(wcodes) || !ptr_ok(wscales)) return SVDQ_ERR_ARG;
+  if (d->rank > 0) {
+    if (!ptr_ok(lora_down) || !ptr_ok(lora_up)) return SVDQ_ERR_ARG;
+  } else if (lora_down != nullptr || lora_up != nullptr) {
+    return SVDQ_ERR_ARG;
+  }
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_pack_weight(d->mode, d->rank, d->N, d->K, W, lambda, lora_down,
+                                           lora_up, wcodes, wscales, (hipStream_t)stream));
+}
+
+svdq_status svdq_quantize_act(const svdq_desc* d, int64_t M, const uint16_t* X,
+                              const float* lambda, const uint16_t* lora_down, uint8_t* xcodes,
+                              void* xscales, float* T, void* stream) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows(M));
+  if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(xcodes) || !ptr_ok(xscales)) return SVDQ_ERR_ARG;
+  if (lora_down != nullptr) {
+    if (d->rank == 0 || !aligned16(lora_down) || !ptr_ok(T)) return SVDQ_ERR_ARG;
+  } else if (!opt_ok(T)) {
+    return SVDQ_ERR_ARG;
+  }
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_quantize_act(d->mode, d->rank, M, d->K, X, lambda, lora_down,
+                                            xcodes, xscales, T, (hipStream_t)stream));
+}
+
+svdq_status svdq_linear_workspace_size(const svdq_desc* d, int64_t M, size_t* bytes) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows(M));
+  if (bytes == nullptr) return SVDQ_ERR_ARG;
+  *bytes = 0;
+  return SVDQ_OK;
+}
+
+svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const uint8_t* xcodes,
+                                const void* xscales, const float* T, const uint8_t* wcodes,
+                                const void* wscales, const uint16_t* lora_up,
+                                const uint16_t* bias, void* Y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows(M));
+  if (!ptr_ok(xcodes) || !ptr_ok(xscales) || !ptr_ok(wcodes) || !ptr_ok(wscales) || !ptr_ok(Y))
+    return SVDQ_ERR_ARG;
+  if ((T == nullptr) != (lora_up == nullptr)) return SVDQ_ERR_ARG;
+  if (T != nullptr && (d->rank == 0 || !aligned16(T) || !aligned16(lora_up))) return SVDQ_ERR_ARG;
+  if (!opt_ok(bias)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_linear_forward(
+      d->mode, d->rank, (d->flags & SVDQ_FLAG_OUT_F32) != 0u, M, d->N, d->K, xcodes, xscales, T,
+      wcodes, wscales, lora_up, bias, Y, (hipStream_t)stream));
+}
+
+svdq_status svdq_lowrank_down(const svdq_desc* d, int64_t M, const uint16_t* X,
+                              const float* lambda, const uint16_t* lora_down, float* T,
+                              void* stream) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows(M));
+  if (d->rank == 0) return SVDQ_ERR_SHAPE;
+  if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(lora_down) || !ptr_ok(T)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_lowrank_down(d->rank, M, d->K, X, lambda, lora_down, T,
+                                            (hipStream_t)stream));
+}
+
+svdq_status svdq_lowrank_up(const svdq_desc* d, int64_t M, const float* T,
+                            const uint16_t* lora_up, void* Y, void* stream) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows(M));
+  if (d->rank == 0) return SVDQ_ERR_SHAPE;
+  if (!ptr_ok(T) || !ptr_ok(lora_up) || !ptr_ok(Y)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_lowrank_up(d->rank, (d->flags & SVDQ_FLAG_OUT_F32) != 0u, M,
+                                          d->N, T, lora_up, Y, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,250 @@
+"""Python binding of libsvdq (ctypes).  Argument marshalling only.
+
+Each function takes torch tensors on the current HIP device, checks dtype,
+shape, device and contiguity, allocates missing outputs with ``torch.empty``
+(PyTorch is used for device memory and the current stream, nothing else) and
+calls the C function of the same name on
+``torch.cuda.current_stream()``.  Every step of the layer runs in the
+library's kernels; if ``libsvdq.so`` is missing the import-time loader raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "svdq.h")
+
+SVDQ_MODE_INT4 = 0
+SVDQ_MODE_FP4 = 1
+SVDQ_FLAG_OUT_F32 = 0x1
+MODES = {"int4": SVDQ_MODE_INT4, "fp4": SVDQ_MODE_FP4}
+STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_ARG", 2: "SVDQ_ERR_SHAPE", 3: "SVDQ_ERR_ARCH",
+          4: "SVDQ_ERR_HIP"}
+
+
+class SvdqDesc(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}")
+        self.status = status
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_DESC = ctypes.POINTER(SvdqDesc)
+
+_SIGNATURES = {
+    "svdq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "svdq_arch_supported": (ctypes.c_int, [ctypes.c_char_p]),
+    "svdq_version": (ctypes.c_char_p, []),
+    "svdq_calibrate_lambda": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "svdq_pack_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_quantize_act": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_linear_workspace_size": (ctypes.c_int, [_DESC, _i64, ctypes.POINTER(ctypes.c_size_t)]),
+    "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, ctypes.c_size_t, _vp]),
+    "svdq_lowrank_down": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_lowrank_up": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsvdq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/svdq.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", text)))
+
+
+def desc(mode, K: int, N: int, rank: int, out_f32: bool = False) -> SvdqDesc:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    return SvdqDesc(m, K, N, rank, SVDQ_FLAG_OUT_F32 if out_f32 else 0)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise SvdqError(fn, st)
+
+
+def scale_dtype(mode) -> torch.dtype:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    return torch.float32 if m == SVDQ_MODE_INT4 else torch.uint8
+
+
+def scale_cols(mode, K: int) -> int:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    return K // 64 if m == SVDQ_MODE_INT4 else K // 32
+
+
+def svdq_status_string(status: int) -> str:
+    return load().svdq_status_string(status).decode()
+
+
+def svdq_arch_supported(name: str) -> bool:
+    return bool(load().svdq_arch_supported(name.encode()))
+
+
+def svdq_version() -> str:
+    return load().svdq_version().decode()
+
+
+def svdq_calibrate_lambda(X: torch.Tensor, W: torch.Tensor, lam: Optional[torch.Tensor] = None):
+    M, K = X.shape
+    N = W.shape[0]
+    _need(X, "X", torch.bfloat16, (M, K))
+    _need(W, "W", torch.bfloat16, (N, K))
+    if lam is None:
+        lam = torch.empty(K, dtype=torch.float32, device=X.device)
+    _need(lam, "lambda", torch.float32, (K,))
+    _check("svdq_calibrate_lambda",
+           load().svdq_calibrate_lambda(M, K, N, _p(X), _p(W), _p(lam), _stream()))
+    return lam
+
+
+def svdq_pack_weight(d: SvdqDesc, W, lam, lora_down=None, lora_up=None, wcodes=None, wscales=None):
+    N, K, r = d.N, d.K, d.rank
+    _need(W, "W", torch.bfloat16, (N, K))
+    _need(lam, "lambda", torch.float32, (K,))
+    _need(lora_down, "lora_down", torch.bfloat16, (r, K), optional=True)
+    _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=True)
+    if wcodes is None:
+        wcodes = torch.empty(N, K // 2, dtype=torch.uint8, device=W.device)
+    if wscales is None:
+        wscales = torch.empty(N, scale_cols(d.mode, K), dtype=scale_dtype(d.mode), device=W.device)
+    _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
+    _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
+    _check("svdq_pack_weight",
+           load().svdq_pack_weight(ctypes.byref(d), _p(W), _p(lam), _p(lora_down), _p(lora_up),
+                                   _p(wcodes), _p(wscales), _stream()))
+    return wcodes, wscales
+
+
+def svdq_quantize_act(d: SvdqDesc, X, lam, lora_down=None, xcodes=None, xscales=None, T=None):
+    M = X.shape[0]
+    K, r = d.K, d.rank
+    _need(X, "X", torch.bfloat16, (M, K))
+    _need(lam, "lambda", torch.float32, (K,))
+    _need(lora_down, "lora_down", torch.bfloat16, (r, K), optional=True)
+    if xcodes is None:
+        xcodes = torch.empty(M, K // 2, dtype=torch.uint8, device=X.device)
+    if xscales is None:
+        xscales = torch.empty(M, scale_cols(d.mode, K), dtype=scale_dtype(d.mode), device=X.device)
+    if lora_down is not None and T is None:
+        T = torch.empty(M, r, dtype=torch.float32, device=X.device)
+    _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
+    _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)))
+    _need(T, "T", torch.float32, (M, r), optional=True)
+    _check("svdq_quantize_act",
+           load().svdq_quantize_act(ctypes.byref(d), M, _p(X), _p(lam), _p(lora_down),
+                                    _p(xcodes), _p(xscales), _p(T), _stream()))
+    return xcodes, xscales, T
+
+
+def svdq_linear_workspace_size(d: SvdqDesc, M: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("svdq_linear_workspace_size",
+           load().svdq_linear_workspace_size(ctypes.byref(d), M, ctypes.byref(n)))
+    return n.value
+
+
+def svdq_linear_forward(d: SvdqDesc, xcodes, xscales, T, wcodes, wscales, lora_up=None,
+                        bias=None, Y=None, workspace=None):
+    M = xcodes.shape[0]
+    K, N, r = d.K, d.N, d.rank
+    out_dtype = torch.float32 if (d.flags & SVDQ_FLAG_OUT_F32) else torch.bfloat16
+    _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
+    _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)))
+    _need(T, "T", torch.float32, (M, r), optional=True)
+    _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
+    _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
+    _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=True)
+    _need(bias, "bias", torch.bfloat16, (N,), optional=True)
+    if Y is None:
+        Y = torch.empty(M, N, dtype=out_dtype, device=xcodes.device)
+    _need(Y, "Y", out_dtype, (M, N))
+    need = svdq_linear_workspace_size(d, M)
+    ws_bytes = 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=xcodes.device)
+        ws_bytes = workspace.numel()
+    _check("svdq_linear_forward",
+           load().svdq_linear_forward(ctypes.byref(d), M, _p(xcodes), _p(xscales), _p(T),
+                                      _p(wcodes), _p(wscales), _p(lora_up), _p(bias), _p(Y),
+                                      _p(workspace), ws_bytes, _stream()))
+    return Y
+
+
+def svdq_lowrank_down(d: SvdqDesc, X, lam, lora_down, T=None):
+    M = X.shape[0]
+    _need(X, "X", torch.bfloat16, (M, d.K))
+    _need(lam, "lambda", torch.float32, (d.K,))
+    _need(lora_down, "lora_down", torch.bfloat16, (d.rank, d.K))
+    if T is None:
+        T = torch.empty(M, d.rank, dtype=torch.float32, device=X.device)
+    _need(T, "T", torch.float32, (M, d.rank))
+    _check("svdq_lowrank_down",
+           load().svdq_lowrank_down(ctypes.byref(d), M, _p(X), _p(lam), _p(lora_down), _p(T),
+                                    _stream()))
+    return T
+
+
+def svdq_lowrank_up(d: SvdqDesc, T, lora_up, Y):
+    M = T.shape[0]
+    out_dtype = torch.float32 if (d.flags & SVDQ_FLAG_OUT_F32) else torch.bfloat16
+    _need(T, "T", torch.float32, (M, d.rank))
+    _need(lora_up, "lora_up", torch.bfloat16, (d.N, d.rank))
+    _need(Y, "Y", out_dtype, (M, d.N))
+    _check("svdq_lowrank_up",
+           load().svdq_lowrank_up(ctypes.byref(d), M, _p(T), _p(lora_up), _p(Y), _stream()))
+    return Y

@@ -1,0 +1,169 @@
+/*
+ * svdq.h -- C ABI of the SVDQuant W4A4 quantized linear layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (Nunchaku Lite page on axbrief.com, section "The Mechanics of
+ * 4-Bit Efficiency and SVDQuant"; Nunchaku troubleshooting page on
+ * apatero.com, section "O que e Nunchaku e como acelera modelos Qwen"):
+ * a per-input-channel smoothing factor lambda moves activation outliers into
+ * the weight, the smoothed weight W_hat = W diag(lambda) is split into a
+ * 16-bit rank-r branch L1 L2 (from its SVD) and a residual R that is stored
+ * in 4 bits, activations are quantized to 4 bits at run time, and
+ *
+ *     Y = deq(Q(X_hat) Q(R)^T) + (X_hat L1) L2 + bias,   X_hat = X / lambda.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     dense row-major, 16-byte aligned.  The caller allocates and frees every
+ *     buffer; the library allocates nothing and keeps no pointer after it
+ *     returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls validate on the host, enqueue their kernels on `stream` and
+ *     return; buffers must stay valid until that work completes.
+ *   - Validation runs before any HIP runtime call: on SVDQ_ERR_ARG or
+ *     SVDQ_ERR_SHAPE nothing is enqueued and outputs are untouched.  A device
+ *     that is not gfx950 gives SVDQ_ERR_ARCH.  A failed launch or an earlier
+ *     sticky HIP error gives SVDQ_ERR_HIP.  Faults inside kernels are
+ *     asynchronous and surface at the caller's next synchronisation.
+ *   - No call aborts the process or throws.
+ *
+ * Data formats (fixed by this library; the pages leave them open)
+ *   bf16   : uint16_t bit patterns.
+ *   lambda : float32 [K].
+ *   L1, L2 : the rank-r factors are passed in the weight layout of the two
+ *            linear maps they form, like nn.Linear weights:
+ *              lora_down = L1^T, bf16 [r][K]   (the K -> r map),
+ *              lora_up   = L2^T, bf16 [N][r]   (the r -> N map).
+ *   INT4   : codes are two's-complement nibbles -8..7, groups of 64 along K,
+ *            one float32 scale per (row, group) = fp32(absmax / 7); a code is
+ *            clamp(rint_half_even(fp32(v / scale)), -8, 7), 0 when scale = 0.
+ *   FP4    : codes are E2M1 sign-magnitude nibbles (bit 3 = sign, magnitudes
+ *            0, .5, 1, 1.5, 2, 3, 4, 6), blocks of 32 along K, one E8M0 byte
+ *            per (row, block) = e + 127 with e = clamp(floor(log2 absmax) - 2,
+ *            -127, 127) (byte 0 for an all-zero block); a code is the nearest
+ *            grid point to v * 2^-e, ties to the even code, saturating at 6.
+ *   Packing: two codes per byte, element 2j in the low nibble and 2j+1 in
+ *            the high nibble; rows are contiguous: codes [rows][K/2],
+ *            scales [rows][K/64] (INT4, float32) or [rows][K/32] (FP4, uint8).
+ *   T      : float32 [M][r], the down-projection X_hat L1.
+ *
+ * Shape limits: 1 <= M, K % 128 == 0, N % 128 == 0, rank % 16 == 0,
+ * 0 <= rank <= 256 (rank 0 = no low-rank branch).
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_MODE_INT4 = 0, /* int4 codes, group 64, fp32 scales            */
+  SVDQ_MODE_FP4 = 1   /* E2M1 codes, block 32, E8M0 scales (MXFP4)    */
+} svdq_mode;
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_ARG = 1,   /* null / misaligned pointer, bad mode or flags  */
+  SVDQ_ERR_SHAPE = 2, /* a size outside the limits above               */
+  SVDQ_ERR_ARCH = 3,  /* current device is not gfx950                  */
+  SVDQ_ERR_HIP = 4    /* HIP runtime error (launch or sticky error)    */
+} svdq_status;
+
+/* Y is written as float32 instead of bf16. */
+#define SVDQ_FLAG_OUT_F32 0x1u
+
+/* Static description of one quantized linear layer. */
+typedef struct {
+  int32_t mode;   /* svdq_mode                                   */
+  int32_t K;      /* input features                               */
+  int32_t N;      /* output features                              */
+  int32_t rank;   /* r, width of the 16-bit low-rank branch        */
+  uint32_t flags; /* SVDQ_FLAG_*                                  */
+} svdq_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* svdq_status_string(svdq_status s);
+
+/* 1 if a device architecture name (hipDeviceProp_t::gcnArchName, e.g.
+ * "gfx950:sramecc+:xnack-") is one this library runs on, else 0.  Pure host
+ * function; the capability check the pages describe for 4-bit kernels
+ * (axbrief.com page, section "Hardware Specialization and the Compression
+ * Workflow"). */
+int svdq_arch_supported(const char* gcn_arch_name);
+
+/* Library version, e.g. "0.1.0". */
+const char* svdq_version(void);
+
+/* Offline calibration of the smoothing factor (apatero.com page, section
+ * "O que e Nunchaku ...": outliers are moved from activations to weights).
+ *   lambda[k] = fp32(sqrt(fp64(max_m |X[m][k]|) / fp64(max_n |W[n][k]|))),
+ *   lambda[k] = 1 where either maximum is 0.
+ * X: bf16 [M][K] calibration activations; W: bf16 [N][K]; lambda: out [K].
+ * Limits: M >= 1, N >= 1, K % 128 == 0. */
+svdq_status svdq_calibrate_lambda(int64_t M, int32_t K, int32_t N, const uint16_t* X,
+                                  const uint16_t* W, float* lambda, void* stream);
+
+/* Offline weight packing (same two pages; the residual branch of W4A4).
+ *   W_hat[n][k] = fp32(W[n][k] * lambda[k]);
+ *   acc = 0; for i = 0..r-1: acc = fp32(acc + L1[k][i] * L2[i][n]);
+ *   R[n][k] = fp32(W_hat[n][k] - acc);   (no fused multiply-add anywhere)
+ *   R quantized row by row in desc->mode into wcodes [N][K/2] and wscales.
+ * W: bf16 [N][K]; lora_down: bf16 [r][K]; lora_up: bf16 [N][r] (both NULL
+ * when rank == 0).  Codes and scales are bit-identical to the definition. */
+svdq_status svdq_pack_weight(const svdq_desc* desc, const uint16_t* W, const float* lambda,
+                             const uint16_t* lora_down, const uint16_t* lora_up,
+                             uint8_t* wcodes, void* wscales, void* stream);
+
+/* Run-time activation side, one kernel (apatero.com page, section "O que e
+ * Nunchaku ...": the down-projection of the low-rank branch is fused into
+ * the quantization kernel and shares its activations).
+ *   X_hat[m][k] = bf16_RNE(fp32(X[m][k] / lambda[k]));
+ *   X_hat quantized row by row in desc->mode into xcodes [M][K/2], xscales;
+ *   T[m][i] = sum_k X_hat[m][k] * L1[k][i]   (fp32 accumulation)
+ * lora_down may be NULL (then T is not written and may be NULL); with
+ * rank == 0 both must be NULL.  Codes and scales are bit-identical to the
+ * definition; T is accurate to fp32 accumulation. */
+svdq_status svdq_quantize_act(const svdq_desc* desc, int64_t M, const uint16_t* X,
+                              const float* lambda, const uint16_t* lora_down,
+                              uint8_t* xcodes, void* xscales, float* T, void* stream);
+
+/* Bytes of device workspace svdq_linear_forward needs for this shape (may be
+ * 0).  The caller passes at least that much. */
+svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t* bytes);
+
+/* The W4A4 GEMM with the up-projection and bias in its epilogue (axbrief.com
+ * page, section "The Mechanics ...": 4-bit weights and activations;
+ * apatero.com page: the up-projection is fused into the 4-bit compute
+ * kernel).
+ *   INT4: Y0[m][n] = sum_g sx[m][g] sw[n][g] sum_{k in g} qx[m][k] qw[n][k]
+ *   FP4 : Y0[m][n] = sum_b 2^(ex[m][b] + ew[n][b]) sum_{k in b} fx[m][k] fw[n][k]
+ *   Y = Y0 + T L2 + bias, written as bf16 (RNE) or float32 (SVDQ_FLAG_OUT_F32).
+ * T and lora_up are both NULL or both set (NULL: no low-rank term); bias may
+ * be NULL.  Y: [M][N].  Accuracy: the integer/E2M1 block sums are exact, the
+ * rest is fp32 arithmetic. */
+svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const uint8_t* xcodes,
+                                const void* xscales, const float* T, const uint8_t* wcodes,
+                                const void* wscales, const uint16_t* lora_up,
+                                const uint16_t* bias, void* Y, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Unfused low-rank branch, for comparison with the fused schedule (the
+ * apatero.com page quotes the overhead of running the rank-32 branch as
+ * separate kernels).  svdq_lowrank_down re-reads X and writes
+ * T = bf16_RNE(fp32(X / lambda)) L1 (fp32 [M][r]); svdq_lowrank_up adds
+ * T L2 to an existing Y [M][N] (bf16 or float32 per desc->flags) in place. */
+svdq_status svdq_lowrank_down(const svdq_desc* desc, int64_t M, const uint16_t* X,
+                              const float* lambda, const uint16_t* lora_down, float* T,
+                              void* stream);
+svdq_status svdq_lowrank_up(const svdq_desc* desc, int64_t M, const float* T,
+                            const uint16_t* lora_up, void* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -1,0 +1,147 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before any HIP call (no GPU
+is needed for any of this; nothing here launches a kernel)."""
+import ctypes
+
+import pytest
+
+from bit_diffusion_transformer_quantize_amd import svdq as S
+
+ARG, SHAPE, HIP = 1, 2, 4
+A = 0x10000          # a 16-byte-aligned address that is never dereferenced
+MIS = 0x10008        # a misaligned one
+
+
+def _lib():
+    return S.load()
+
+
+def _d(mode=0, K=512, N=512, rank=16, flags=0):
+    return ctypes.byref(S.SvdqDesc(mode, K, N, rank, flags))
+
+
+def test_exports_every_header_symbol():
+    lib = _lib()
+    names = S.header_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    for code in range(5):
+        assert S.svdq_status_string(code).startswith(S.STATUS[code])
+    assert S.svdq_version() == "0.1.0"
+
+
+@pytest.mark.parametrize("name,ok", [("gfx950", True), ("gfx950:sramecc+:xnack-", True),
+                                     ("gfx9500", False), ("gfx942", False), ("gfx90a", False),
+                                     ("", False), ("gfx95", False)])
+def test_arch_predicate(name, ok):
+    assert S.svdq_arch_supported(name) is ok
+
+
+def test_arch_predicate_null():
+    assert _lib().svdq_arch_supported(None) == 0
+
+
+def test_workspace_size_is_host_only():
+    n = ctypes.c_size_t(123)
+    assert _lib().svdq_linear_workspace_size(_d(), 256, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert _lib().svdq_linear_workspace_size(_d(), 256, None) == ARG
+    assert _lib().svdq_linear_workspace_size(_d(K=96), 256, ctypes.byref(n)) == SHAPE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=2), ARG), (dict(mode=-1), ARG), (dict(flags=2), ARG),
+    (dict(K=0), SHAPE), (dict(K=64), SHAPE), (dict(K=100), SHAPE), (dict(K=1 << 21), SHAPE),
+    (dict(N=0), SHAPE), (dict(N=64), SHAPE), (dict(N=200), SHAPE),
+    (dict(rank=8), SHAPE), (dict(rank=-16), SHAPE), (dict(rank=272), SHAPE),
+])
+def test_desc_validation(kw, status):
+    lib = _lib()
+    d = _d(**kw)
+    assert lib.svdq_quantize_act(d, 256, A, A, A, A, A, A, None) == status
+    assert lib.svdq_pack_weight(d, A, A, A, A, A, A, None) == status
+    assert lib.svdq_linear_forward(d, 256, A, A, A, A, A, A, A, A, None, 0, None) == status
+    assert lib.svdq_lowrank_down(d, 256, A, A, A, A, None) == status
+    assert lib.svdq_lowrank_up(d, 256, A, A, A, None) == status
+
+
+def test_null_desc():
+    lib = _lib()
+    assert lib.svdq_quantize_act(None, 256, A, A, A, A, A, A, None) == ARG
+    assert lib.svdq_linear_forward(None, 256, A, A, A, A, A, A, A, A, None, 0, None) == ARG
+
+
+@pytest.mark.parametrize("M", [0, -1, 1 << 40])
+def test_rows_validation(M):
+    lib = _lib()
+    assert lib.svdq_quantize_act(_d(), M, A, A, A, A, A, A, None) == SHAPE
+    assert lib.svdq_linear_forward(_d(), M, A, A, A, A, A, A, A, A, None, 0, None) == SHAPE
+    assert lib.svdq_calibrate_lambda(M, 512, 512, A, A, A, None) == SHAPE
+
+
+def test_quantize_act_pointer_validation():
+    lib = _lib()
+    q = lib.svdq_quantize_act
+    assert q(_d(), 256, None, A, A, A, A, A, None) == ARG        # X null
+    assert q(_d(), 256, MIS, A, A, A, A, A, None) == ARG         # X misaligned
+    assert q(_d(), 256, A, None, A, A, A, A, None) == ARG        # lambda null
+    assert q(_d(), 256, A, A, A, None, A, A, None) == ARG        # codes null
+    assert q(_d(), 256, A, A, A, A, None, A, None) == ARG        # scales null
+    assert q(_d(), 256, A, A, A, A, A, None, None) == ARG        # lora_down without T
+    assert q(_d(), 256, A, A, MIS, A, A, A, None) == ARG         # lora_down misaligned
+    assert q(_d(rank=0), 256, A, A, A, A, A, A, None) == ARG     # lora_down with rank 0
+    assert q(_d(), 256, A, A, None, A, A, MIS, None) == ARG      # optional T misaligned
+
+
+def test_pack_weight_pointer_validation():
+    lib = _lib()
+    p = lib.svdq_pack_weight
+    assert p(_d(), None, A, A, A, A, A, None) == ARG
+    assert p(_d(), A, A, None, A, A, A, None) == ARG             # rank>0 needs lora_down
+    assert p(_d(), A, A, A, None, A, A, None) == ARG             # and lora_up
+    assert p(_d(rank=0), A, A, A, None, A, A, None) == ARG       # rank 0 forbids them
+    assert p(_d(), A, A, A, A, None, A, None) == ARG
+    assert p(_d(), A, A, A, A, A, MIS, None) == ARG
+
+
+def test_linear_forward_pointer_validation():
+    lib = _lib()
+    f = lib.svdq_linear_forward
+    assert f(_d(), 256, None, A, A, A, A, A, A, A, None, 0, None) == ARG
+    assert f(_d(), 256, A, A, A, A, A, None, A, A, None, 0, None) == ARG   # T without lora_up
+    assert f(_d(), 256, A, A, None, A, A, A, A, A, None, 0, None) == ARG   # lora_up without T
+    assert f(_d(rank=0), 256, A, A, A, A, A, A, A, A, None, 0, None) == ARG
+    assert f(_d(), 256, A, A, A, A, A, A, MIS, A, None, 0, None) == ARG    # bias misaligned
+    assert f(_d(), 256, A, A, A, A, A, A, A, None, None, 0, None) == ARG   # Y null
+
+
+def test_lowrank_pieces_validation():
+    lib = _lib()
+    assert lib.svdq_lowrank_down(_d(rank=0), 256, A, A, A, A, None) == SHAPE
+    assert lib.svdq_lowrank_up(_d(rank=0), 256, A, A, A, None) == SHAPE
+    assert lib.svdq_lowrank_down(_d(), 256, A, A, None, A, None) == ARG
+    assert lib.svdq_lowrank_up(_d(), 256, A, MIS, A, None) == ARG
+
+
+def test_calibrate_validation():
+    lib = _lib()
+    assert lib.svdq_calibrate_lambda(16, 512, 16, None, A, A, None) == ARG
+    assert lib.svdq_calibrate_lambda(16, 500, 16, A, A, A, None) == SHAPE
+    assert lib.svdq_calibrate_lambda(16, 512, 0, A, A, A, None) == SHAPE
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_has_gpu(), reason="only meaningful without a GPU: with one these "
+                    "valid-looking fake pointers would be launched on")
+def test_no_device_is_a_hip_error():
+    lib = _lib()
+    assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, None) == HIP
+    assert lib.svdq_linear_forward(_d(), 256, A, A, A, A, A, A, A, A, None, 0, None) == HIP
