@@ -79,4 +79,37 @@ __device__ __forceinline__ void int4x8_to_int8x16(uint32_t w, uint32_t& even, ui
   odd = w & 0xF0F0F0F0u;
 }
 
+// Eight two's-complement int4 codes (one dword, element 2j in the low nibble
+// of byte j) -> eight e4m3 bytes that hold q * 2^-9 exactly.  In e4m3 the
+// subnormal range is linear: byte |q| (0..8, exponent field 0 or 1) is
+// |q| * 2^-9, and bit 7 is the sign, so the byte is the sign-magnitude form of
+// q.  For a nibble value x (0..15) that is x when x < 8 and 0x90 - x
+// otherwise.  `even` receives elements 0,2,4,6 and `odd` elements 1,3,5,7.
+// The per-byte "x >= 8" masks come from v_perm_b32, whose selectors 8..11
+// replicate the top bit of bytes 1, 3, 5, 7 of its 64-bit source.
+__device__ __forceinline__ void int4x8_to_fp8x8(uint32_t w, uint32_t& even, uint32_t& odd) {
+  const uint32_t xe = w & 0x0F0F0F0Fu;
+  const uint32_t xo = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t ue = w << 4;  // bit 3 of each byte -> bit 7
+  const uint32_t me = __builtin_amdgcn_perm(ue << 8, ue, 0x090B080Au);
+  const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+  even = ((0x90909090u - xe) & me) | (xe & ~me);
+  odd = ((0x90909090u - xo) & mo) | (xo & ~mo);
+}
+
+// 16 int4 codes (two dwords) -> 16 e4m3 bytes {even(w0), even(w1), odd(w0),
+// odd(w1)}: the 16-byte chunk layout both operands of the INT4 GEMM use.
+__device__ __forceinline__ v4u int4x16_to_fp8x16(uint32_t w0, uint32_t w1) {
+  uint32_t e0, o0, e1, o1;
+  int4x8_to_fp8x8(w0, e0, o0);
+  int4x8_to_fp8x8(w1, e1, o1);
+  return v4u{e0, e1, o0, o1};
+}
+
+// 32 int4 codes (16 bytes) -> two such 16-byte chunks.
+__device__ __forceinline__ void int4x32_to_fp8x32(const v4u& w, v4u& lo, v4u& hi) {
+  lo = int4x16_to_fp8x16(w[0], w[1]);
+  hi = int4x16_to_fp8x16(w[2], w[3]);
+}
+
 }  // namespace svdq

@@ -26,8 +26,22 @@ svdq_status check_desc(const svdq_desc* d) {
   return SVDQ_OK;
 }
 
+#define SVDQ_TRY_INNER(expr)           \
+  do {                                 \
+    const svdq_status st_ = (expr);    \
+    if (st_ != SVDQ_OK) return st_;    \
+  } while (0)
+
 svdq_status check_rows(int64_t M) {
   if (M < 1 || M > (int64_t(1) << 31)) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+
+// Activation tensors are limited to 2^36 elements (kernels index 32-code
+// chunks with 32-bit integers).
+svdq_status check_rows_k(int64_t M, int32_t K) {
+  SVDQ_TRY_INNER(check_rows(M));
+  if (M * (int64_t)K > (int64_t(1) << 36)) return SVDQ_ERR_SHAPE;
   return SVDQ_OK;
 }
 
@@ -112,7 +126,7 @@ svdq_status svdq_quantize_act(const svdq_desc* d, int64_t M, const uint16_t* X,
                               const float* lambda, const uint16_t* lora_down, uint8_t* xcodes,
                               void* xscales, float* T, void* stream) {
   SVDQ_TRY(check_desc(d));
-  SVDQ_TRY(check_rows(M));
+  SVDQ_TRY(check_rows_k(M, d->K));
   if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(xcodes) || !ptr_ok(xscales)) return SVDQ_ERR_ARG;
   if (lora_down != nullptr) {
     if (d->rank == 0 || !aligned16(lora_down) || !ptr_ok(T)) return SVDQ_ERR_ARG;
@@ -126,9 +140,9 @@ svdq_status svdq_quantize_act(const svdq_desc* d, int64_t M, const uint16_t* X,
 
 svdq_status svdq_linear_workspace_size(const svdq_desc* d, int64_t M, size_t* bytes) {
   SVDQ_TRY(check_desc(d));
-  SVDQ_TRY(check_rows(M));
+  SVDQ_TRY(check_rows_k(M, d->K));
   if (bytes == nullptr) return SVDQ_ERR_ARG;
-  *bytes = 0;
+  *bytes = d->mode == SVDQ_MODE_INT4 ? svdq::int4_workspace_bytes(M, d->N, d->K) : 0;
   return SVDQ_OK;
 }
 
@@ -137,26 +151,33 @@ svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const uint8_t* xc
                                 const void* wscales, const uint16_t* lora_up,
                                 const uint16_t* bias, void* Y, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   SVDQ_TRY(check_desc(d));
-  SVDQ_TRY(check_rows(M));
+  SVDQ_TRY(check_rows_k(M, d->K));
   if (!ptr_ok(xcodes) || !ptr_ok(xscales) || !ptr_ok(wcodes) || !ptr_ok(wscales) || !ptr_ok(Y))
     return SVDQ_ERR_ARG;
   if ((T == nullptr) != (lora_up == nullptr)) return SVDQ_ERR_ARG;
   if (T != nullptr && (d->rank == 0 || !aligned16(T) || !aligned16(lora_up))) return SVDQ_ERR_ARG;
   if (!opt_ok(bias)) return SVDQ_ERR_ARG;
+  const bool f32 = (d->flags & SVDQ_FLAG_OUT_F32) != 0u;
+  if (d->mode == SVDQ_MODE_INT4) {
+    if (!ptr_ok(workspace) || workspace_bytes < svdq::int4_workspace_bytes(M, d->N, d->K))
+      return SVDQ_ERR_ARG;
+    SVDQ_TRY(check_device());
+    return from_hip(svdq::launch_int4_forward(
+        d->rank, f32, M, d->N, d->K, xcodes, static_cast<const float*>(xscales), T, wcodes,
+        static_cast<const float*>(wscales), lora_up, bias, Y, workspace, (hipStream_t)stream));
+  }
   SVDQ_TRY(check_device());
-  return from_hip(svdq::launch_linear_forward(
-      d->mode, d->rank, (d->flags & SVDQ_FLAG_OUT_F32) != 0u, M, d->N, d->K, xcodes, xscales, T,
-      wcodes, wscales, lora_up, bias, Y, (hipStream_t)stream));
+  return from_hip(svdq::launch_fp4_forward(
+      d->rank, f32, M, d->N, d->K, xcodes, static_cast<const uint8_t*>(xscales), T, wcodes,
+      static_cast<const uint8_t*>(wscales), lora_up, bias, Y, (hipStream_t)stream));
 }
 
 svdq_status svdq_lowrank_down(const svdq_desc* d, int64_t M, const uint16_t* X,
                               const float* lambda, const uint16_t* lora_down, float* T,
                               void* stream) {
   SVDQ_TRY(check_desc(d));
-  SVDQ_TRY(check_rows(M));
+  SVDQ_TRY(check_rows_k(M, d->K));
   if (d->rank == 0) return SVDQ_ERR_SHAPE;
   if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(lora_down) || !ptr_ok(T)) return SVDQ_ERR_ARG;
   SVDQ_TRY(check_device());
@@ -167,7 +188,7 @@ svdq_status svdq_lowrank_down(const svdq_desc* d, int64_t M, const uint16_t* X,
 svdq_status svdq_lowrank_up(const svdq_desc* d, int64_t M, const float* T,
                             const uint16_t* lora_up, void* Y, void* stream) {
   SVDQ_TRY(check_desc(d));
-  SVDQ_TRY(check_rows(M));
+  SVDQ_TRY(check_rows_k(M, d->K));
   if (d->rank == 0) return SVDQ_ERR_SHAPE;
   if (!ptr_ok(T) || !ptr_ok(lora_up) || !ptr_ok(Y)) return SVDQ_ERR_ARG;
   SVDQ_TRY(check_device());

@@ -131,8 +131,11 @@ svdq_status svdq_quantize_act(const svdq_desc* desc, int64_t M, const uint16_t* 
                               const float* lambda, const uint16_t* lora_down,
                               uint8_t* xcodes, void* xscales, float* T, void* stream);
 
-/* Bytes of device workspace svdq_linear_forward needs for this shape (may be
- * 0).  The caller passes at least that much. */
+/* Bytes of device workspace svdq_linear_forward needs for this shape: in INT4
+ * mode M*K bytes for an e4m3 copy of the activation codes plus 16 bytes per
+ * (64-group, row) of X (rows padded to a multiple of 256) and of W for the
+ * scale operands, each of the five parts rounded up to 256 bytes; 0 in FP4
+ * mode.  Pure host function. */
 svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t* bytes);
 
 /* The W4A4 GEMM with the up-projection and bias in its epilogue (axbrief.com
@@ -144,7 +147,12 @@ svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t*
  *   Y = Y0 + T L2 + bias, written as bf16 (RNE) or float32 (SVDQ_FLAG_OUT_F32).
  * T and lora_up are both NULL or both set (NULL: no low-rank term); bias may
  * be NULL.  Y: [M][N].  Accuracy: the integer/E2M1 block sums are exact, the
- * rest is fp32 arithmetic. */
+ * rest is fp32 arithmetic (INT4: the product of the two group scales carries
+ * a relative error below 2^-15).
+ * workspace: device buffer of at least svdq_linear_workspace_size bytes
+ * (16-byte aligned; may be NULL when that size is 0).  Its contents are
+ * scratch, overwritten by the call; calls that may run concurrently need
+ * separate workspaces. */
 svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const uint8_t* xcodes,
                                 const void* xscales, const float* T, const uint8_t* wcodes,
                                 const void* wscales, const uint16_t* lora_up,

@@ -47,8 +47,13 @@ def test_arch_predicate_null():
 
 def test_workspace_size_is_host_only():
     n = ctypes.c_size_t(123)
-    assert _lib().svdq_linear_workspace_size(_d(), 256, ctypes.byref(n)) == 0
-    assert n.value == 0
+    assert _lib().svdq_linear_workspace_size(_d(mode=1), 256, ctypes.byref(n)) == 0
+    assert n.value == 0                                   # FP4 needs none
+    assert _lib().svdq_linear_workspace_size(_d(mode=0, K=512, N=256), 300, ctypes.byref(n)) == 0
+    # INT4: e4m3 copy of the codes (M*K) + the scale operands: two halves of
+    # 8 B per group and row, X rows padded to a multiple of 256
+    al = lambda x: (x + 255) // 256 * 256
+    assert n.value == al(300 * 512) + 2 * al(8 * 512 * 8) + 2 * al(8 * 256 * 8)
     assert _lib().svdq_linear_workspace_size(_d(), 256, None) == ARG
     assert _lib().svdq_linear_workspace_size(_d(K=96), 256, ctypes.byref(n)) == SHAPE
 
@@ -117,6 +122,9 @@ def test_linear_forward_pointer_validation():
     assert f(_d(rank=0), 256, A, A, A, A, A, A, A, A, None, 0, None) == ARG
     assert f(_d(), 256, A, A, A, A, A, A, MIS, A, None, 0, None) == ARG    # bias misaligned
     assert f(_d(), 256, A, A, A, A, A, A, A, None, None, 0, None) == ARG   # Y null
+    assert f(_d(), 256, A, A, A, A, A, A, A, A, None, 1 << 30, None) == ARG  # INT4: no workspace
+    assert f(_d(), 256, A, A, A, A, A, A, A, A, MIS, 1 << 30, None) == ARG   # misaligned
+    assert f(_d(), 256, A, A, A, A, A, A, A, A, A, 1024, None) == ARG        # too small
 
 
 def test_lowrank_pieces_validation():
@@ -144,4 +152,5 @@ def _has_gpu():
 def test_no_device_is_a_hip_error():
     lib = _lib()
     assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, None) == HIP
-    assert lib.svdq_linear_forward(_d(), 256, A, A, A, A, A, A, A, A, None, 0, None) == HIP
+    assert lib.svdq_linear_forward(_d(), 256, A, A, A, A, A, A, A, A, A, 1 << 30, None) == HIP
+    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, A, A, A, A, A, None, 0, None) == HIP
