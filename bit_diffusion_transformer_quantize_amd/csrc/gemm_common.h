@@ -13,12 +13,13 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
 }
 
 // acc[tr][tc] += T[rows] L2[cols] for a TR x TC block of 32x32 tiles whose
-// top-left output is (mbase, nbase).  T (fp32) is split into a bf16 high and
-// low part, so the two bf16 MFMAs per 16-wide slice of the rank keep the
-// branch accurate to about 2^-16 of |T|.
+// top-left output is (mbase, nbase); rows >= M and columns >= N contribute
+// nothing (their outputs are never stored).  T (fp32) is split into a bf16
+// high and low part, so the two bf16 MFMAs per 16-wide slice of the rank
+// keep the branch accurate to about 2^-16 of |T|.
 template <int TR, int TC>
 __device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, int64_t M,
-                                                 int64_t mbase, int nbase, int lane,
+                                                 int N, int64_t mbase, int nbase, int lane,
                                                  const float* __restrict__ T,
                                                  const uint16_t* __restrict__ lora_up) {
   for (int rb = 0; rb < rank; rb += 16) {
@@ -44,7 +45,12 @@ __device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, 
 #pragma unroll
     for (int tc = 0; tc < TC; ++tc) {
       const int n = nbase + tc * 32 + (lane & 31);
-      bv[tc] = *reinterpret_cast<const v8bf*>(lora_up + (int64_t)n * rank + rb + (lane >> 5) * 8);
+      if (n < N) {
+        bv[tc] = *reinterpret_cast<const v8bf*>(lora_up + (int64_t)n * rank + rb + (lane >> 5) * 8);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bv[tc][i] = __builtin_bit_cast(__bf16, (uint16_t)0);
+      }
     }
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr)
@@ -56,7 +62,8 @@ __device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, 
   }
 }
 
-// Y[rows, cols] (=|+=) acc + bias, bf16 (RNE) or fp32.
+// Y[rows, cols] (=|+=) acc + bias, bf16 (RNE) or fp32; rows >= M and
+// columns >= N are skipped.
 template <int TR, int TC>
 __device__ __forceinline__ void store_tiles(const v16f (&acc)[TR][TC], int64_t M, int N,
                                             int64_t mbase, int nbase, int lane,
@@ -65,6 +72,7 @@ __device__ __forceinline__ void store_tiles(const v16f (&acc)[TR][TC], int64_t M
 #pragma unroll
   for (int tc = 0; tc < TC; ++tc) {
     const int n = nbase + tc * 32 + (lane & 31);
+    if (n >= N) continue;
     const float b = bias ? bf16_to_f32(bias[n]) : 0.f;
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr)

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(GM_THREADS) void fp4_gemm_kernel(
 
   const int64_t mbase = m0 + wm * 64;
   const int nbase = n0 + wn * 64;
-  if (T != nullptr) lowrank_up_tiles<2, 2>(acc, rank, M, mbase, nbase, lane, T, lora_up);
+  if (T != nullptr) lowrank_up_tiles<2, 2>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
   store_tiles<2, 2>(acc, M, N, mbase, nbase, lane, bias, out_f32 != 0, Y, false);
 }
 
@@ -154,15 +154,35 @@ __global__ __launch_bounds__(GM_THREADS) void lowrank_up_kernel(int64_t M, int N
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-  lowrank_up_tiles<2, 2>(acc, rank, M, mbase, nbase, lane, T, lora_up);
+  lowrank_up_tiles<2, 2>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
   store_tiles<2, 2>(acc, M, N, mbase, nbase, lane, nullptr, out_f32 != 0, Y, true);
+}
+
+// The FP4 weight image is the packed codes [N][K/2] followed, at the next
+// 256-byte boundary, by the E8M0 scales [N][K/32].
+static size_t fp4_scale_offset(int N, int K) {
+  return ((size_t)N * (K / 2) + 255) & ~size_t(255);
+}
+
+size_t fp4_weight_image_bytes(int N, int K) {
+  return fp4_scale_offset(N, K) + (size_t)N * (K / 32);
+}
+
+hipError_t launch_fp4_prepare_weight(int N, int K, const uint8_t* wcodes, const uint8_t* wscales,
+                                     void* wimage, hipStream_t s) {
+  uint8_t* img = reinterpret_cast<uint8_t*>(wimage);
+  hipError_t e = hipMemcpyAsync(img, wcodes, (size_t)N * (K / 2), hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  return hipMemcpyAsync(img + fp4_scale_offset(N, K), wscales, (size_t)N * (K / 32),
+                        hipMemcpyDeviceToDevice, s);
 }
 
 hipError_t launch_fp4_forward(int rank, bool out_f32, int64_t M, int N, int K,
                               const uint8_t* xcodes, const uint8_t* xscales, const float* T,
-                              const uint8_t* wcodes, const uint8_t* wscales,
-                              const uint16_t* lora_up, const uint16_t* bias, void* Y,
-                              hipStream_t s) {
+                              const void* wimage, const uint16_t* lora_up, const uint16_t* bias,
+                              void* Y, hipStream_t s) {
+  const uint8_t* wcodes = reinterpret_cast<const uint8_t*>(wimage);
+  const uint8_t* wscales = wcodes + fp4_scale_offset(N, K);
   const int64_t tiles = ((M + GM_BM - 1) / GM_BM) * (N / GM_BN);
   hipLaunchKernelGGL(fp4_gemm_kernel, dim3((unsigned)tiles), dim3(GM_THREADS), 0, s, M, N, K,
                      rank, (int)out_f32, xcodes, xscales, T, wcodes, wscales, lora_up, bias, Y);

@@ -51,9 +51,11 @@ _SIGNATURES = {
     "svdq_calibrate_lambda": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "svdq_pack_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "svdq_quantize_act": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_weight_image_size": (ctypes.c_int, [_DESC, ctypes.POINTER(ctypes.c_size_t)]),
+    "svdq_prepare_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp]),
     "svdq_linear_workspace_size": (ctypes.c_int, [_DESC, _i64, ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                           _vp, ctypes.c_size_t, _vp]),
+                                           ctypes.c_size_t, _vp]),
     "svdq_lowrank_down": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp]),
     "svdq_lowrank_up": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
 }
@@ -190,6 +192,27 @@ def svdq_quantize_act(d: SvdqDesc, X, lam, lora_down=None, xcodes=None, xscales=
     return xcodes, xscales, T
 
 
+def svdq_weight_image_size(d: SvdqDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("svdq_weight_image_size", load().svdq_weight_image_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def svdq_prepare_weight(d: SvdqDesc, wcodes, wscales, wimage=None):
+    """Prepared weight (opaque uint8 image) of packed codes and scales."""
+    N, K = d.N, d.K
+    _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
+    _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
+    nbytes = svdq_weight_image_size(d)
+    if wimage is None:
+        wimage = torch.empty(nbytes, dtype=torch.uint8, device=wcodes.device)
+    _need(wimage, "wimage", torch.uint8, (nbytes,))
+    _check("svdq_prepare_weight",
+           load().svdq_prepare_weight(ctypes.byref(d), _p(wcodes), _p(wscales), _p(wimage),
+                                      _stream()))
+    return wimage
+
+
 def svdq_linear_workspace_size(d: SvdqDesc, M: int) -> int:
     n = ctypes.c_size_t(0)
     _check("svdq_linear_workspace_size",
@@ -197,16 +220,15 @@ def svdq_linear_workspace_size(d: SvdqDesc, M: int) -> int:
     return n.value
 
 
-def svdq_linear_forward(d: SvdqDesc, xcodes, xscales, T, wcodes, wscales, lora_up=None,
-                        bias=None, Y=None, workspace=None):
+def svdq_linear_forward(d: SvdqDesc, xcodes, xscales, T, wimage, lora_up=None, bias=None,
+                        Y=None, workspace=None):
     M = xcodes.shape[0]
     K, N, r = d.K, d.N, d.rank
     out_dtype = torch.float32 if (d.flags & SVDQ_FLAG_OUT_F32) else torch.bfloat16
     _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
     _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)))
     _need(T, "T", torch.float32, (M, r), optional=True)
-    _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
-    _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
+    _need(wimage, "wimage", torch.uint8, (svdq_weight_image_size(d),))
     _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=True)
     _need(bias, "bias", torch.bfloat16, (N,), optional=True)
     if Y is None:
@@ -220,8 +242,8 @@ def svdq_linear_forward(d: SvdqDesc, xcodes, xscales, T, wcodes, wscales, lora_u
         ws_bytes = workspace.numel()
     _check("svdq_linear_forward",
            load().svdq_linear_forward(ctypes.byref(d), M, _p(xcodes), _p(xscales), _p(T),
-                                      _p(wcodes), _p(wscales), _p(lora_up), _p(bias), _p(Y),
-                                      _p(workspace), ws_bytes, _stream()))
+                                      _p(wimage), _p(lora_up), _p(bias), _p(Y), _p(workspace),
+                                      ws_bytes, _stream()))
     return Y
 
 

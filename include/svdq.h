@@ -47,8 +47,9 @@
  *            scales [rows][K/64] (INT4, float32) or [rows][K/32] (FP4, uint8).
  *   T      : float32 [M][r], the down-projection X_hat L1.
  *
- * Shape limits: 1 <= M, K % 128 == 0, N % 128 == 0, rank % 16 == 0,
- * 0 <= rank <= 256 (rank 0 = no low-rank branch).
+ * Shape limits: 1 <= M <= 2^31, M*K <= 2^36, K % 128 == 0, N % 128 == 0,
+ * K, N <= 2^20, rank % 16 == 0, 0 <= rank <= 256 (rank 0 = no low-rank
+ * branch); svdq_linear_forward also needs M*N <= 2^46.
  */
 #ifndef SVDQ_H
 #define SVDQ_H
@@ -131,11 +132,31 @@ svdq_status svdq_quantize_act(const svdq_desc* desc, int64_t M, const uint16_t* 
                               const float* lambda, const uint16_t* lora_down,
                               uint8_t* xcodes, void* xscales, float* T, void* stream);
 
+/* Bytes of the prepared weight of a layer (see svdq_prepare_weight).  Pure
+ * host function. */
+svdq_status svdq_weight_image_size(const svdq_desc* desc, size_t* bytes);
+
+/* Offline re-layout of the packed weight (codes and scales as written by
+ * svdq_pack_weight) into the operand layout the GEMM reads (like the
+ * one-time weight packing into the matrix-core layout the apatero.com page
+ * describes for the fused 4-bit kernel).  wimage: device buffer of
+ * svdq_weight_image_size bytes, written completely.
+ *   INT4: a group-major array of 2048-byte blocks, one per (64-group,
+ *         32 rows of W), holding the codes as 6-bit E2M3 fields (value q/8)
+ *         in MFMA lane order and the bf16 hi/lo split of the scales; rows
+ *         are padded to a multiple of 192 with zeros.
+ *   FP4 : the codes [N][K/2] followed, at the next 256-byte boundary, by the
+ *         E8M0 scales [N][K/32].
+ * The image depends only on (mode, N, K) and the codes and scales; it is
+ * an opaque operand of svdq_linear_forward. */
+svdq_status svdq_prepare_weight(const svdq_desc* desc, const uint8_t* wcodes,
+                                const void* wscales, void* wimage, void* stream);
+
 /* Bytes of device workspace svdq_linear_forward needs for this shape: in INT4
- * mode M*K bytes for an e4m3 copy of the activation codes plus 16 bytes per
- * (64-group, row) of X (rows padded to a multiple of 256) and of W for the
- * scale operands, each of the five parts rounded up to 256 bytes; 0 in FP4
- * mode.  Pure host function. */
+ * mode the activation operand image, 64 bytes per element of a 64-group
+ * row of X with rows padded to a multiple of 256 (K * Mp bytes, Mp = M
+ * rounded up to 256), rounded up to 256 bytes; 0 in FP4 mode.  Pure host
+ * function. */
 svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t* bytes);
 
 /* The W4A4 GEMM with the up-projection and bias in its epilogue (axbrief.com
@@ -145,6 +166,8 @@ svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t*
  *   INT4: Y0[m][n] = sum_g sx[m][g] sw[n][g] sum_{k in g} qx[m][k] qw[n][k]
  *   FP4 : Y0[m][n] = sum_b 2^(ex[m][b] + ew[n][b]) sum_{k in b} fx[m][k] fw[n][k]
  *   Y = Y0 + T L2 + bias, written as bf16 (RNE) or float32 (SVDQ_FLAG_OUT_F32).
+ * xcodes/xscales: the activation side as written by svdq_quantize_act;
+ * wimage: the prepared weight (svdq_prepare_weight) of the same desc.
  * T and lora_up are both NULL or both set (NULL: no low-rank term); bias may
  * be NULL.  Y: [M][N].  Accuracy: the integer/E2M1 block sums are exact, the
  * rest is fp32 arithmetic (INT4: the product of the two group scales carries
@@ -154,10 +177,9 @@ svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t*
  * scratch, overwritten by the call; calls that may run concurrently need
  * separate workspaces. */
 svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const uint8_t* xcodes,
-                                const void* xscales, const float* T, const uint8_t* wcodes,
-                                const void* wscales, const uint16_t* lora_up,
-                                const uint16_t* bias, void* Y, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                const void* xscales, const float* T, const void* wimage,
+                                const uint16_t* lora_up, const uint16_t* bias, void* Y,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Unfused low-rank branch, for comparison with the fused schedule (the
  * apatero.com page quotes the overhead of running the rank-32 branch as

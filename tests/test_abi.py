@@ -50,12 +50,34 @@ def test_workspace_size_is_host_only():
     assert _lib().svdq_linear_workspace_size(_d(mode=1), 256, ctypes.byref(n)) == 0
     assert n.value == 0                                   # FP4 needs none
     assert _lib().svdq_linear_workspace_size(_d(mode=0, K=512, N=256), 300, ctypes.byref(n)) == 0
-    # INT4: e4m3 copy of the codes (M*K) + the scale operands: two halves of
-    # 8 B per group and row, X rows padded to a multiple of 256
-    al = lambda x: (x + 255) // 256 * 256
-    assert n.value == al(300 * 512) + 2 * al(8 * 512 * 8) + 2 * al(8 * 256 * 8)
+    # INT4: the activation operand image, K bytes per row, rows padded to 256
+    assert n.value == 512 * 512
     assert _lib().svdq_linear_workspace_size(_d(), 256, None) == ARG
     assert _lib().svdq_linear_workspace_size(_d(K=96), 256, ctypes.byref(n)) == SHAPE
+
+
+def test_weight_image_size_is_host_only():
+    n = ctypes.c_size_t(0)
+    # INT4: K bytes per weight row, rows padded to a multiple of 192
+    assert _lib().svdq_weight_image_size(_d(mode=0, K=512, N=256), ctypes.byref(n)) == 0
+    assert n.value == 512 * 384
+    assert _lib().svdq_weight_image_size(_d(mode=0, K=3072, N=9216), ctypes.byref(n)) == 0
+    assert n.value == 3072 * 9216
+    # FP4: codes, then the scales at the next 256-byte boundary
+    assert _lib().svdq_weight_image_size(_d(mode=1, K=512, N=256), ctypes.byref(n)) == 0
+    assert n.value == 256 * 256 + 256 * 16
+    assert _lib().svdq_weight_image_size(_d(), None) == ARG
+    assert _lib().svdq_weight_image_size(_d(N=200), ctypes.byref(n)) == SHAPE
+
+
+def test_prepare_weight_validation():
+    p = _lib().svdq_prepare_weight
+    assert p(None, A, A, A, None) == ARG
+    assert p(_d(mode=3), A, A, A, None) == ARG
+    assert p(_d(K=96), A, A, A, None) == SHAPE
+    assert p(_d(), None, A, A, None) == ARG
+    assert p(_d(), A, MIS, A, None) == ARG
+    assert p(_d(), A, A, None, None) == ARG
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -69,7 +91,7 @@ def test_desc_validation(kw, status):
     d = _d(**kw)
     assert lib.svdq_quantize_act(d, 256, A, A, A, A, A, A, None) == status
     assert lib.svdq_pack_weight(d, A, A, A, A, A, A, None) == status
-    assert lib.svdq_linear_forward(d, 256, A, A, A, A, A, A, A, A, None, 0, None) == status
+    assert lib.svdq_linear_forward(d, 256, A, A, A, A, A, A, A, None, 0, None) == status
     assert lib.svdq_lowrank_down(d, 256, A, A, A, A, None) == status
     assert lib.svdq_lowrank_up(d, 256, A, A, A, None) == status
 
@@ -77,14 +99,14 @@ def test_desc_validation(kw, status):
 def test_null_desc():
     lib = _lib()
     assert lib.svdq_quantize_act(None, 256, A, A, A, A, A, A, None) == ARG
-    assert lib.svdq_linear_forward(None, 256, A, A, A, A, A, A, A, A, None, 0, None) == ARG
+    assert lib.svdq_linear_forward(None, 256, A, A, A, A, A, A, A, None, 0, None) == ARG
 
 
 @pytest.mark.parametrize("M", [0, -1, 1 << 40])
 def test_rows_validation(M):
     lib = _lib()
     assert lib.svdq_quantize_act(_d(), M, A, A, A, A, A, A, None) == SHAPE
-    assert lib.svdq_linear_forward(_d(), M, A, A, A, A, A, A, A, A, None, 0, None) == SHAPE
+    assert lib.svdq_linear_forward(_d(), M, A, A, A, A, A, A, A, None, 0, None) == SHAPE
     assert lib.svdq_calibrate_lambda(M, 512, 512, A, A, A, None) == SHAPE
 
 
@@ -116,15 +138,19 @@ def test_pack_weight_pointer_validation():
 def test_linear_forward_pointer_validation():
     lib = _lib()
     f = lib.svdq_linear_forward
-    assert f(_d(), 256, None, A, A, A, A, A, A, A, None, 0, None) == ARG
-    assert f(_d(), 256, A, A, A, A, A, None, A, A, None, 0, None) == ARG   # T without lora_up
-    assert f(_d(), 256, A, A, None, A, A, A, A, A, None, 0, None) == ARG   # lora_up without T
-    assert f(_d(rank=0), 256, A, A, A, A, A, A, A, A, None, 0, None) == ARG
-    assert f(_d(), 256, A, A, A, A, A, A, MIS, A, None, 0, None) == ARG    # bias misaligned
-    assert f(_d(), 256, A, A, A, A, A, A, A, None, None, 0, None) == ARG   # Y null
-    assert f(_d(), 256, A, A, A, A, A, A, A, A, None, 1 << 30, None) == ARG  # INT4: no workspace
-    assert f(_d(), 256, A, A, A, A, A, A, A, A, MIS, 1 << 30, None) == ARG   # misaligned
-    assert f(_d(), 256, A, A, A, A, A, A, A, A, A, 1024, None) == ARG        # too small
+    assert f(_d(), 256, None, A, A, A, A, A, A, None, 0, None) == ARG   # codes null
+    assert f(_d(), 256, A, A, A, None, A, A, A, None, 0, None) == ARG   # weight image null
+    assert f(_d(), 256, A, A, A, MIS, A, A, A, None, 0, None) == ARG    # misaligned
+    assert f(_d(), 256, A, A, A, A, None, A, A, None, 0, None) == ARG   # T without lora_up
+    assert f(_d(), 256, A, A, None, A, A, A, A, None, 0, None) == ARG   # lora_up without T
+    assert f(_d(rank=0), 256, A, A, A, A, A, A, A, None, 0, None) == ARG
+    assert f(_d(), 256, A, A, A, A, A, MIS, A, None, 0, None) == ARG    # bias misaligned
+    assert f(_d(), 256, A, A, A, A, A, A, None, None, 0, None) == ARG   # Y null
+    assert f(_d(), 256, A, A, A, A, A, A, A, None, 1 << 30, None) == ARG  # INT4: no workspace
+    assert f(_d(), 256, A, A, A, A, A, A, A, MIS, 1 << 30, None) == ARG   # misaligned
+    assert f(_d(), 256, A, A, A, A, A, A, A, A, 1024, None) == ARG        # too small
+    # output larger than 2^46 elements
+    assert f(_d(N=1 << 20), 1 << 27, A, A, A, A, A, A, A, A, 1 << 40, None) == SHAPE
 
 
 def test_lowrank_pieces_validation():
@@ -152,5 +178,6 @@ def _has_gpu():
 def test_no_device_is_a_hip_error():
     lib = _lib()
     assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, None) == HIP
-    assert lib.svdq_linear_forward(_d(), 256, A, A, A, A, A, A, A, A, A, 1 << 30, None) == HIP
-    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, A, A, A, A, A, None, 0, None) == HIP
+    assert lib.svdq_linear_forward(_d(), 256, A, A, A, A, A, A, A, A, 1 << 30, None) == HIP
+    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, A, A, A, A, None, 0, None) == HIP
+    assert lib.svdq_prepare_weight(_d(), A, A, A, None) == HIP

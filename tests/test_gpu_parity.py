@@ -163,13 +163,17 @@ def test_determinism_and_guard_bands(mode):
                                     ws_b[:N * sc].view(N, sc))
         xc, xs, T = S.svdq_quantize_act(d, Xd, lamd, ld, xc_b[:M * K // 2].view(M, K // 2),
                                         xs_b[:M * sc].view(M, sc), T_b[:M * r].view(M, r))
-        Y = S.svdq_linear_forward(d, xc, xs, T, wc, ws, lu, bd, Y_b[:M * N].view(M, N))
+        nimg, nws = S.svdq_weight_image_size(d), S.svdq_linear_workspace_size(d, M)
+        wi_b, wk_b = guarded(nimg, torch.uint8), guarded(max(nws, 16), torch.uint8)
+        wimg = S.svdq_prepare_weight(d, wc, ws, wi_b[:nimg])
+        Y = S.svdq_linear_forward(d, xc, xs, T, wimg, lu, bd, Y_b[:M * N].view(M, N),
+                                  wk_b[:nws] if nws else None)
         torch.cuda.synchronize()
         for buf, n in ((wc_b, N * K // 2), (ws_b, N * sc), (xc_b, M * K // 2), (xs_b, M * sc),
-                       (T_b, M * r), (Y_b, M * N)):
+                       (T_b, M * r), (Y_b, M * N), (wi_b, nimg), (wk_b, max(nws, 16))):
             tail = buf[n:].view(torch.uint8).cpu().numpy()
             assert np.all(tail == 0x5A), "write past the end of an output"
-        outs.append([np_(t.view(torch.uint8)) for t in (wc, ws, xc, xs, T, Y)])
+        outs.append([np_(t.view(torch.uint8)) for t in (wc, ws, xc, xs, T, Y, wimg)])
     for a, bb in zip(*outs):
         assert np.array_equal(a, bb), "non-deterministic output"
 
@@ -194,7 +198,7 @@ def test_unfused_schedule(mode):
     wc, ws = S.svdq_pack_weight(d, Wd, lamd, ld, lu)
     xc, xs, _ = S.svdq_quantize_act(d, Xd, lamd, None)
     T = S.svdq_lowrank_down(d, Xd, lamd, ld)
-    Y = S.svdq_linear_forward(d, xc, xs, None, wc, ws, None, bd)
+    Y = S.svdq_linear_forward(d, xc, xs, None, S.svdq_prepare_weight(d, wc, ws), None, bd)
     S.svdq_lowrank_up(d, T, lu, Y)
     torch.cuda.synchronize()
     assert np.array_equal(np_(xc), xc_o) and np.array_equal(np_(xs), xs_o)
