@@ -12,87 +12,163 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Eight fp32 values -> their bf16 high parts and bf16 low parts (of the
+// fp32 remainder), both RNE (v_cvt_pk_bf16_f32): hi + lo is within 2^-16
+// relative of the value.
+__device__ __forceinline__ void split_bf16x8(const v4f& a, const v4f& b, v8bf& hi, v8bf& lo) {
+  const float t[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const v2f x = {t[2 * j], t[2 * j + 1]};
+    const v2bf h = __builtin_convertvector(x, v2bf);
+    const v2f hf = __builtin_convertvector(h, v2f);
+    const v2f r = {x[0] - hf[0], x[1] - hf[1]};
+    const v2bf l = __builtin_convertvector(r, v2bf);
+    hi[2 * j] = h[0];
+    hi[2 * j + 1] = h[1];
+    lo[2 * j] = l[0];
+    lo[2 * j + 1] = l[1];
+  }
+}
+
 // acc[tr][tc] += T[rows] L2[cols] for a TR x TC block of 32x32 tiles whose
 // top-left output is (mbase, nbase); rows >= M and columns >= N contribute
 // nothing (their outputs are never stored).  T (fp32) is split into a bf16
 // high and low part, so the two bf16 MFMAs per 16-wide slice of the rank
-// keep the branch accurate to about 2^-16 of |T|.
+// keep the branch accurate to about 2^-16 of |T|.  The loads of slice
+// rb + 16 are issued before slice rb is computed; out-of-range rows and
+// columns read row 0 and are zeroed, so no load sits under a branch.
 template <int TR, int TC>
 __device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, int64_t M,
                                                  int N, int64_t mbase, int nbase, int lane,
                                                  const float* __restrict__ T,
                                                  const uint16_t* __restrict__ lora_up) {
+  const int koff = (lane >> 5) * 8;
+  const float* tp[TR];
+  bool tok[TR];
+#pragma unroll
+  for (int tr = 0; tr < TR; ++tr) {
+    const int64_t m = mbase + tr * 32 + (lane & 31);
+    tok[tr] = m < M;
+    tp[tr] = T + (tok[tr] ? m : 0) * rank + koff;
+  }
+  const uint16_t* lp[TC];
+  bool lok[TC];
+#pragma unroll
+  for (int tc = 0; tc < TC; ++tc) {
+    const int n = nbase + tc * 32 + (lane & 31);
+    lok[tc] = n < N;
+    lp[tc] = lora_up + (int64_t)(lok[tc] ? n : 0) * rank + koff;
+  }
+  v4f ta[TR][2];
+  v8bf la[TC];
+  auto fetch = [&](int rb) {
+#pragma unroll
+    for (int tr = 0; tr < TR; ++tr) {
+      ta[tr][0] = *reinterpret_cast<const v4f*>(tp[tr] + rb);
+      ta[tr][1] = *reinterpret_cast<const v4f*>(tp[tr] + rb + 4);
+    }
+#pragma unroll
+    for (int tc = 0; tc < TC; ++tc) la[tc] = *reinterpret_cast<const v8bf*>(lp[tc] + rb);
+  };
+  fetch(0);
   for (int rb = 0; rb < rank; rb += 16) {
     v8bf thi[TR], tlo[TR], bv[TC];
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr) {
-      const int64_t m = mbase + tr * 32 + (lane & 31);
-      v4f t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
-      if (m < M) {
-        const float* tp = T + m * rank + rb + (lane >> 5) * 8;
-        t0 = *reinterpret_cast<const v4f*>(tp);
-        t1 = *reinterpret_cast<const v4f*>(tp + 4);
-      }
-      const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t h = f32_to_bf16(tv[i]);
-        const uint32_t l = f32_to_bf16(tv[i] - bf16_to_f32(h));
-        thi[tr][i] = __builtin_bit_cast(__bf16, (uint16_t)h);
-        tlo[tr][i] = __builtin_bit_cast(__bf16, (uint16_t)l);
-      }
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+      split_bf16x8(tok[tr] ? ta[tr][0] : z, tok[tr] ? ta[tr][1] : z, thi[tr], tlo[tr]);
     }
 #pragma unroll
     for (int tc = 0; tc < TC; ++tc) {
-      const int n = nbase + tc * 32 + (lane & 31);
-      if (n < N) {
-        bv[tc] = *reinterpret_cast<const v8bf*>(lora_up + (int64_t)n * rank + rb + (lane >> 5) * 8);
-      } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bv[tc][i] = __builtin_bit_cast(__bf16, (uint16_t)0);
-      }
+      for (int i = 0; i < 8; ++i)
+        bv[tc][i] = lok[tc] ? la[tc][i] : __builtin_bit_cast(__bf16, (uint16_t)0);
+    }
+    if (rb + 16 < rank) fetch(rb + 16);
+#pragma unroll
+    for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc)
+        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(thi[tr], bv[tc], acc[tr][tc], 0, 0, 0);
+#pragma unroll
+    for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc)
+        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tlo[tr], bv[tc], acc[tr][tc], 0, 0, 0);
+  }
+}
+
+// acc[tr][tc][i] = bias[column] (0 without a bias or past N): the initial
+// value of a block of tiles whose first column is nbase.
+template <int TR, int TC>
+__device__ __forceinline__ void init_bias_tiles(v16f (&acc)[TR][TC], int N, int nbase, int lane,
+                                                const uint16_t* __restrict__ bias) {
+#pragma unroll
+  for (int tc = 0; tc < TC; ++tc) {
+    const int n = nbase + tc * 32 + (lane & 31);
+    float b = 0.f;
+    if (bias != nullptr) {  // uniform; the load itself is unconditional
+      b = bf16_to_f32(bias[n < N ? n : 0]);
+      b = n < N ? b : 0.f;
     }
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr)
 #pragma unroll
-      for (int tc = 0; tc < TC; ++tc) {
-        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(thi[tr], bv[tc], acc[tr][tc], 0, 0, 0);
-        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tlo[tr], bv[tc], acc[tr][tc], 0, 0, 0);
-      }
+      for (int i = 0; i < 16; ++i) acc[tr][tc][i] = b;
   }
 }
 
-// Y[rows, cols] (=|+=) acc + bias, bf16 (RNE) or fp32; rows >= M and
-// columns >= N are skipped.
-template <int TR, int TC>
-__device__ __forceinline__ void store_tiles(const v16f (&acc)[TR][TC], int64_t M, int N,
-                                            int64_t mbase, int nbase, int lane,
-                                            const uint16_t* __restrict__ bias, bool out_f32,
-                                            void* __restrict__ Y, bool accumulate) {
+// Y[rows, cols] (=|+=) acc + bias for one output type; rows >= M and
+// columns >= N are skipped.  Each (tile row, tile column) keeps one row
+// pointer; the 16 rows of a lane are scalar multiples of N away from it.
+template <int TR, int TC, bool ACCUM, typename OutT>
+__device__ __forceinline__ void store_tiles_as(const v16f (&acc)[TR][TC], int64_t M, int N,
+                                               int64_t mbase, int nbase, int lane,
+                                               const uint16_t* __restrict__ bias,
+                                               OutT* __restrict__ Y) {
+  const int64_t m_lane = mbase + 4 * (lane >> 5);
 #pragma unroll
   for (int tc = 0; tc < TC; ++tc) {
     const int n = nbase + tc * 32 + (lane & 31);
     if (n >= N) continue;
     const float b = bias ? bf16_to_f32(bias[n]) : 0.f;
 #pragma unroll
-    for (int tr = 0; tr < TR; ++tr)
+    for (int tr = 0; tr < TR; ++tr) {
+      const int64_t m_tile = m_lane + tr * 32;
+      OutT* yrow = Y + m_tile * N + n;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int64_t m = mbase + tr * 32 + acc_row(i, lane);
-        if (m < M) {
-          const int64_t o = m * N + n;
+        const int r = 8 * (i >> 2) + (i & 3);
+        if (m_tile + r < M) {
+          OutT* y = yrow + (int64_t)r * N;
           float v = acc[tr][tc][i] + b;
-          if (out_f32) {
-            float* y = reinterpret_cast<float*>(Y) + o;
-            *y = accumulate ? *y + v : v;
+          if constexpr (sizeof(OutT) == 4) {
+            *y = ACCUM ? *y + v : v;
           } else {
-            uint16_t* y = reinterpret_cast<uint16_t*>(Y) + o;
-            if (accumulate) v += bf16_to_f32(*y);
+            if (ACCUM) v += bf16_to_f32(*y);
             *y = (uint16_t)f32_to_bf16(v);
           }
         }
       }
+    }
   }
+}
+
+// Y[rows, cols] (=|+=) acc + bias, bf16 (RNE) or fp32.
+template <int TR, int TC, bool ACCUM>
+__device__ __forceinline__ void store_tiles(const v16f (&acc)[TR][TC], int64_t M, int N,
+                                            int64_t mbase, int nbase, int lane,
+                                            const uint16_t* __restrict__ bias, bool out_f32,
+                                            void* __restrict__ Y) {
+  if (out_f32)
+    store_tiles_as<TR, TC, ACCUM>(acc, M, N, mbase, nbase, lane, bias, reinterpret_cast<float*>(Y));
+  else
+    store_tiles_as<TR, TC, ACCUM>(acc, M, N, mbase, nbase, lane, bias,
+                                  reinterpret_cast<uint16_t*>(Y));
 }
 
 }  // namespace svdq

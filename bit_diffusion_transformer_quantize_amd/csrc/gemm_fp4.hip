@@ -133,7 +133,7 @@ __global__ __launch_bounds__(GM_THREADS) void fp4_gemm_kernel(
   const int64_t mbase = m0 + wm * 64;
   const int nbase = n0 + wn * 64;
   if (T != nullptr) lowrank_up_tiles<2, 2>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
-  store_tiles<2, 2>(acc, M, N, mbase, nbase, lane, bias, out_f32 != 0, Y, false);
+  store_tiles<2, 2, false>(acc, M, N, mbase, nbase, lane, bias, out_f32 != 0, Y);
 }
 
 // Stand-alone up-projection for the unfused schedule: Y += T L2.
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(GM_THREADS) void lowrank_up_kernel(int64_t M, int N
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
   lowrank_up_tiles<2, 2>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
-  store_tiles<2, 2>(acc, M, N, mbase, nbase, lane, nullptr, out_f32 != 0, Y, true);
+  store_tiles<2, 2, true>(acc, M, N, mbase, nbase, lane, nullptr, out_f32 != 0, Y);
 }
 
 // The FP4 weight image is the packed codes [N][K/2] followed, at the next

@@ -53,7 +53,7 @@ constexpr int I4_BN = 192;
 constexpr int I4_THREADS = 512;
 constexpr int I4_SCALE_BYTE = 127 + 3;  // E2M3 field q has value q/8
 constexpr int I4_GROUP_M = 2;           // tile rows walked together per XCD
-constexpr int I4_NSLOT = 4;
+constexpr int I4_NSLOT = 4;  // stage slots: DMA runs two groups ahead
 constexpr int IMG_BLOCK = 2048;                                // bytes per (group, 32 rows)
 constexpr int SLOT_A = (I4_BM / 32) * IMG_BLOCK;               // 16 KB of X
 constexpr int SLOT_BYTES = SLOT_A + (I4_BN / 32) * IMG_BLOCK;  // + 12 KB of W
@@ -206,10 +206,10 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   const int G = K >> 6;
 
   // ---- DMA plan: a stage is 28 chunks of 1 KB (16 of X, then 12 of W) that
-  // land at slot + 1 KB * chunk.  Wave w moves chunks w, w+8 (X) and w+16 (W),
-  // waves 0..3 also w+24 (W); waves 4..7 repeat their chunk w+16 instead (the
-  // same bytes to the same place), so that every wave issues four DMAs per
-  // stage and all waves wait with the same count.
+  // land at slot + 1 KB * chunk.  Wave w moves chunks w, w+8 (X) and w+16
+  // (W); waves 0..3 also w+24 (W), while waves 4..7 repeat their chunk w+16
+  // (the same bytes to the same place).  Every wave thus has four DMAs per
+  // group and waits with the same counts, with no branch in the loop.
   const uint8_t* xrun = ximg + (int64_t)tile_m * (I4_BM / 32) * IMG_BLOCK;
   const uint8_t* wrun = wimg + (int64_t)tile_n * (I4_BN / 32) * IMG_BLOCK;
   const int64_t xstride = (int64_t)x_tiles * IMG_BLOCK;  // bytes per group
@@ -219,8 +219,9 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   const int wave4 = wave < 4 ? wave + 24 : wave + 16;  // LDS chunk of the 4th DMA
   const uint32_t voff3 = (uint32_t)((wave4 - 16) * 1024 + lane * 16);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+  auto slot_of = [](int g) { return (g & (I4_NSLOT - 1)) * SLOT_BYTES; };
   auto dma = [&](int g) {
-    const uint32_t slot = lds_base + (uint32_t)((g & (I4_NSLOT - 1)) * SLOT_BYTES);
+    const uint32_t slot = lds_base + (uint32_t)slot_of(g);
     const uint8_t* xs = xrun + g * xstride;
     const uint8_t* ws = wrun + g * wstride;
     dma16(xs, voff0, slot + wave * 1024);
@@ -228,6 +229,13 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     dma16(ws, voff0, slot + (wave + 16) * 1024);
     dma16(ws, voff3, slot + wave4 * 1024);
   };
+  // wait until at most OG groups of this wave's DMA are still in flight
+  auto wait_dma = [&](auto og_tag) {
+    constexpr int OG = decltype(og_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * OG));  // vmcnt(4 OG)
+  };
+  using OG0 = std::integral_constant<int, 0>;
+  using OG1 = std::integral_constant<int, 1>;
 
   // ---- fragment offsets within a slot (see the image layout above)
   const int fa = (wm * 2) * IMG_BLOCK + h * 768 + l32 * 16;
@@ -252,87 +260,99 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     sb[tc] = *reinterpret_cast<const v4s*>(sp + fsb + tc * IMG_BLOCK);
   };
 
+  v16f zero;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) zero[i] = 0.f;
   v16f acc[2][3];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-  const v16f zero = acc[0][0];
   v16f p[2], sc[2];
 
   // tile t of a wave = (t / 3, t % 3); its P and S live in p/sc[t & 1]
-  auto mfma_tile = [&](int t) {
+  auto mfma_p = [&](int t) {
     const int tr = t / 3, tc = t % 3, b = t & 1;
     p[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[tr], bf[tc], zero, FP6_FMT, FP6_FMT,
                                                            0, I4_SCALE_BYTE, 0, I4_SCALE_BYTE);
+  };
+  auto mfma_s = [&](int t) {
+    const int tr = t / 3, tc = t % 3, b = t & 1;
     sc[b] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sa[tr], sb[tc], zero, 0, 0, 0);
   };
-  auto fma_tile = [&](int t) {
+  auto mfma_tile = [&](int t) {
+    mfma_p(t);
+    mfma_s(t);
+  };
+  // FMAs i0 .. i0+7 of tile t: acc += P * S
+  auto fma_half = [&](int t, int i0) {
     const int tr = t / 3, tc = t % 3, b = t & 1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[tr][tc][i] = fmaf(p[b][i], sc[b][i], acc[tr][tc][i]);
+    for (int i = i0; i < i0 + 8; ++i) acc[tr][tc][i] = fmaf(p[b][i], sc[b][i], acc[tr][tc][i]);
+  };
+  // One step: the MFMAs of tile `next` (if any) interleaved with the FMAs of
+  // tile `cur`, in the fixed order P MFMA, 8 FMAs, S MFMA, loads (of the
+  // fragments both MFMAs just read for the last time), 8 FMAs, so that each
+  // MFMA runs under a block of FMAs.
+  auto step = [&](int next, int cur, auto&& loads) {
+    if (next >= 0) mfma_p(next);
+    __builtin_amdgcn_sched_barrier(0);
+    fma_half(cur, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next >= 0) mfma_s(next);
+    loads();
+    __builtin_amdgcn_sched_barrier(0);
+    fma_half(cur, 8);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One group.  KIND 0: steady state (issues the DMA of group g+3);
-  // 1: no DMA left to issue, group g+2 still in flight; 2: nothing in
-  // flight; 3: last group (no next group to prepare).  Every kind is one
-  // basic block, so the sched_barriers fix the order of its steps.
+  // One group.  The DMA of group g+3 is issued in group g; at the barrier
+  // of group g the DMA of g+1 must have landed.  KIND 0: steady state
+  // (group g+2 may still be in flight; issue g+3); 1: g+2 is the last group
+  // (nothing to issue); 2: g+1 is the last (nothing in flight); 3: the last
+  // group (no next group to prepare).  Every kind is straight-line code and
+  // the sched_barriers fix the order of its steps.  Each fragment is
+  // reloaded for the next group in the step that issues its last MFMA.
   auto group = [&](int g, auto kind_tag) {
     constexpr int KIND = decltype(kind_tag)::value;
-    const uint8_t* nsp = lds + ((g + 1) & (I4_NSLOT - 1)) * SLOT_BYTES;
-    // step 0
-    mfma_tile(1);
-    fma_tile(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 1: A tile row 0 is free; the next group's slot must be ready
-    mfma_tile(2);
-    if constexpr (KIND != 3) {
-      if constexpr (KIND == 2)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): group g+2 may be in flight
-      asm volatile("s_barrier" ::: "memory");
-      if constexpr (KIND == 0) dma(g + 3);
-      load_a(nsp, 0);
-    }
-    fma_tile(1);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 2: B column 0 free
-    mfma_tile(3);
-    if constexpr (KIND != 3) load_b(nsp, 0);
-    fma_tile(2);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 3: B column 1 free
-    mfma_tile(4);
-    if constexpr (KIND != 3) load_b(nsp, 1);
-    fma_tile(3);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 4: A row 1 and B column 2 free
-    mfma_tile(5);
-    if constexpr (KIND != 3) {
-      load_a(nsp, 1);
-      load_b(nsp, 2);
-    }
-    fma_tile(4);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 5: first tile of the next group
-    if constexpr (KIND != 3) mfma_tile(0);
-    fma_tile(5);
-    __builtin_amdgcn_sched_barrier(0);
+    constexpr bool NEXT = KIND != 3;
+    const uint8_t* nsp = lds + slot_of(g + 1);
+    step(1, 0, [] {});
+    // A tile row 0 is free after tile 2's MFMAs; the next slot must be ready
+    step(2, 1, [&] {
+      if constexpr (NEXT) {
+        if constexpr (KIND <= 1) wait_dma(OG1{});
+        if constexpr (KIND == 2) wait_dma(OG0{});
+        asm volatile("s_barrier" ::: "memory");
+        if constexpr (KIND == 0) dma(g + 3);
+        load_a(nsp, 0);
+      }
+    });
+    step(3, 2, [&] {  // B column 0 free
+      if constexpr (NEXT) load_b(nsp, 0);
+    });
+    step(4, 3, [&] {  // B column 1 free
+      if constexpr (NEXT) load_b(nsp, 1);
+    });
+    step(5, 4, [&] {  // A row 1 and B column 2 free
+      if constexpr (NEXT) {
+        load_a(nsp, 1);
+        load_b(nsp, 2);
+      }
+    });
+    step(NEXT ? 0 : -1, 5, [] {});  // first tile of the next group
   };
-  using K0 = std::integral_constant<int, 0>;
-  using K1 = std::integral_constant<int, 1>;
-  using K2 = std::integral_constant<int, 2>;
-  using K3 = std::integral_constant<int, 3>;
 
-  // ---- prologue: groups 0..2 in flight, all fragments of group 0.  G is
+  // ---- prologue: the first groups in flight.  Meanwhile the accumulators start
+  // from the bias and the low-rank term T L2 (its loads overlap the DMA
+  // latency), so nothing but the store is left after the main loop.  G is
   // even (K % 128 == 0), so G >= 2.
+  const int64_t mbase = m0 + wm * 64;
+  const int nbase = n0 + wn * 96;
+  // The loads of T and L2 are issued after the DMAs, so waiting for them
+  // also waits for these DMAs (vmcnt counts in order).
   dma(0);
   dma(1);
   if (G > 2) dma(2);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  init_bias_tiles<2, 3>(acc, N, nbase, lane, bias);
+  if (T != nullptr) lowrank_up_tiles<2, 3>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
+  wait_dma(OG0{});
   asm volatile("s_barrier" ::: "memory");
   load_a(lds, 0);
   load_a(lds, 1);
@@ -341,16 +361,14 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   load_b(lds, 2);
   mfma_tile(0);
 
+  // G is even: either G >= 4 (the tail is kinds 1..3) or G == 2 (2, 3)
   int g = 0;
-  for (; g + 3 < G; ++g) group(g, K0{});
-  if (G > 2) group(g++, K1{});
-  group(g++, K2{});
-  group(g, K3{});
+  for (; g + 3 < G; ++g) group(g, std::integral_constant<int, 0>{});
+  if (G >= 4) group(g++, std::integral_constant<int, 1>{});
+  group(g++, std::integral_constant<int, 2>{});
+  group(g, std::integral_constant<int, 3>{});
 
-  const int64_t mbase = m0 + wm * 64;
-  const int nbase = n0 + wn * 96;
-  if (T != nullptr) lowrank_up_tiles<2, 3>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
-  store_tiles<2, 3>(acc, M, N, mbase, nbase, lane, bias, out_f32 != 0, Y, false);
+  store_tiles<2, 3, false>(acc, M, N, mbase, nbase, lane, nullptr, out_f32 != 0, Y);
 }
 
 hipError_t launch_int4_forward(int rank, bool out_f32, int64_t M, int N, int K,
