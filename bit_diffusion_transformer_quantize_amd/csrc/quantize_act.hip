@@ -4,21 +4,42 @@
 // The Nunchaku engine fuses the down-projection of the low-rank branch into
 // the quantization kernel so that both branches share one read of the
 // activations (apatero.com page, section "O que e Nunchaku e como acelera
-// modelos Qwen").  Here a workgroup owns 16 rows of X; its four waves take
-// 64-column tiles round-robin.  In a tile, lane l holds row l%16 and the 16
-// columns 16*(l/16) .. +15, which is also the A-operand layout of two
-// v_mfma_f32_16x16x32_bf16, so the smoothed bf16 values feed the MFMA
-// straight from registers.  Per-group absmax is a two-step xor-shuffle over
-// the four lanes that share a row.  The T partials of the four waves are
-// summed through LDS at the end.
+// modelos Qwen").  Here a workgroup owns 16 rows of X; its eight waves take
+// 64-column tiles round-robin, each prefetching its next tile.  In a tile,
+// lane l holds row l%16 and the 16 columns 16*(l/16) .. +15, which is also
+// the A-operand layout of two v_mfma_f32_16x16x32_bf16, so the smoothed
+// bf16 values feed the MFMA straight from registers.  Per-group absmax is a
+// xor-shuffle over the lanes that share a row.  The T partials of the eight
+// waves are summed through LDS at the end.
+//
+// Exact quotients without a division per element.  Both quotients of the
+// contract, fp32(x / lambda) and fp32(x_hat / s), divide a bf16 value
+// (8 significant bits) by an fp32 value (24 bits).  Such a quotient is never
+// an fp32 rounding midpoint (a 25-bit odd significand times a 24-bit one
+// cannot have only 8 significant bits) and, when it is not, it lies at least
+// about 2^-48 (relative) away from every midpoint, while fp64(a * fp64(1/b))
+// is within 2^-52 of a/b.  So fp32(fp64(a * fp64(1/b))) is exactly the
+// correctly rounded fp32(a / b) (checked on the host for every bf16 a against
+// 20000 fp32 b, subnormals and all-ones significands included).  The fp64
+// reciprocals of lambda are computed once per workgroup into LDS, the one of
+// s once per lane and group.
 #include "common.h"
 #include "kernels.h"
 
 namespace svdq {
 
 constexpr int QA_ROWS = 16;
-constexpr int QA_WAVES = 4;
+constexpr int QA_WAVES = 8;
 constexpr int QA_THREADS = 64 * QA_WAVES;
+constexpr int QA_KCHUNK = 4096;  // columns whose reciprocals of lambda sit in LDS at once
+
+// LDS: the reciprocal table during the main loop, the T partials afterwards.
+template <int RB>
+struct QaLds {
+  static constexpr int kRcp = QA_KCHUNK * 8;
+  static constexpr int kRed = QA_WAVES * (RB > 0 ? RB : 1) * 4 * 64 * 4;
+  static constexpr int kBytes = kRcp > kRed ? kRcp : kRed;
+};
 
 // MODE 0 = INT4, 1 = FP4.  RB = rank / 16 (0 = no down-projection).
 // CODES = false skips the quantizer (stand-alone down-projection).
@@ -27,107 +48,128 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
     int64_t M, int K, const uint16_t* __restrict__ X, const float* __restrict__ lambda,
     const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ xcodes,
     void* __restrict__ xscales, float* __restrict__ T) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<RB>::kBytes];
+  double* rlam = reinterpret_cast<double*>(smem);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int j = lane >> 4;
   const int64_t row = (int64_t)blockIdx.x * QA_ROWS + r16;
   const bool row_ok = row < M;
-  const int ntiles = K >> 6;
   const uint16_t* xrow = X + (row_ok ? row : 0) * (int64_t)K;
 
   v4f tacc[RB > 0 ? RB : 1];
 #pragma unroll
   for (int b = 0; b < (RB > 0 ? RB : 1); ++b) tacc[b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int t = wave; t < ntiles; t += QA_WAVES) {
-    const int k0 = t * 64 + j * 16;
-    v4u xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-    if (row_ok) {
-      xa = *reinterpret_cast<const v4u*>(xrow + k0);
-      xb = *reinterpret_cast<const v4u*>(xrow + k0 + 8);
-    }
-    const v4f l0 = *reinterpret_cast<const v4f*>(lambda + k0);
-    const v4f l1 = *reinterpret_cast<const v4f*>(lambda + k0 + 4);
-    const v4f l2 = *reinterpret_cast<const v4f*>(lambda + k0 + 8);
-    const v4f l3 = *reinterpret_cast<const v4f*>(lambda + k0 + 12);
-    const float lam[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
-                           l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
-    const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+  for (int kc = 0; kc < K; kc += QA_KCHUNK) {
+    const int kn = min(QA_KCHUNK, K - kc);
+    __syncthreads();  // the previous chunk is done with the table
+    for (int c = threadIdx.x; c < kn; c += QA_THREADS) rlam[c] = 1.0 / (double)lambda[kc + c];
+    __syncthreads();
+    const int ntiles = kn >> 6;
+    auto load_x = [&](int t, v4u& xa, v4u& xb) {
+      xa = v4u{0u, 0u, 0u, 0u};
+      xb = v4u{0u, 0u, 0u, 0u};
+      if (row_ok && t < ntiles) {
+        const uint16_t* p = xrow + kc + t * 64 + j * 16;
+        xa = *reinterpret_cast<const v4u*>(p);
+        xb = *reinterpret_cast<const v4u*>(p + 8);
+      }
+    };
+    v4u na, nb;
+    load_x(wave, na, nb);
+    for (int t = wave; t < ntiles; t += QA_WAVES) {
+      const v4u xa = na, xb = nb;
+      load_x(t + QA_WAVES, na, nb);  // next tile of this wave
+      const int kl = t * 64 + j * 16;  // column within the chunk
+      const int k0 = kc + kl;          // column within the row
+      const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
 
-    // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
-    uint32_t hb[16];
-    float xh[16];
-    float amax = 0.f;
+      // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
+      uint32_t hb[16];
+      float xh[16];
+      float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t xbits = (xw[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      const float q = bf16_to_f32(xbits) / lam[i];
-      hb[i] = f32_to_bf16(q);
-      xh[i] = bf16_to_f32(hb[i]);
-      amax = fmaxf(amax, fabsf(xh[i]));
-    }
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t xbits = (xw[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        const float q = (float)((double)bf16_to_f32(xbits) * rlam[kl + i]);
+        hb[i] = f32_to_bf16(q);
+        xh[i] = bf16_to_f32(hb[i]);
+        amax = fmaxf(amax, fabsf(xh[i]));
+      }
 
-    if constexpr (CODES) {
-      if constexpr (MODE == 0) {
-        // INT4: group of 64 = the four lanes sharing this row.
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float s = amax / 7.0f;
-        uint32_t w0 = 0, w1 = 0;
-        if (s != 0.f) {
+      if constexpr (CODES) {
+        if constexpr (MODE == 0) {
+          // INT4: group of 64 = the four lanes sharing this row.
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const float s = amax / 7.0f;
+          uint32_t w0 = 0, w1 = 0;
+          if (s != 0.f) {
+            const double rs = 1.0 / (double)s;
+            uint32_t c[16];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) w0 |= ((uint32_t)int4_code(xh[i], s) & 0xFu) << (4 * i);
+            for (int i = 0; i < 16; ++i) {
+              float q = __builtin_rintf((float)((double)xh[i] * rs));  // = rint(fp32(xh / s))
+              q = fminf(fmaxf(q, -8.0f), 7.0f);
+              c[i] = (uint32_t)(int)q & 0xFu;
+            }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) w1 |= ((uint32_t)int4_code(xh[8 + i], s) & 0xFu) << (4 * i);
-        }
-        if (row_ok) {
-          *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
-          if (j == 0) reinterpret_cast<float*>(xscales)[row * (int64_t)(K >> 6) + t] = s;
-        }
-      } else {
-        // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        const int e = e8m0_exponent(amax);
-        const float sc = exp2i(-e);
-        uint32_t w0 = 0, w1 = 0;
+            for (int i = 0; i < 8; ++i) {
+              w0 |= c[i] << (4 * i);
+              w1 |= c[8 + i] << (4 * i);
+            }
+          }
+          if (row_ok) {
+            *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
+            if (j == 0) reinterpret_cast<float*>(xscales)[row * (int64_t)(K >> 6) + (k0 >> 6)] = s;
+          }
+        } else {
+          // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          const int e = e8m0_exponent(amax);
+          const float sc = exp2i(-e);
+          uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w0 |= e2m1_code(xh[i] * sc) << (4 * i);
+          for (int i = 0; i < 8; ++i) w0 |= e2m1_code(xh[i] * sc) << (4 * i);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w1 |= e2m1_code(xh[8 + i] * sc) << (4 * i);
-        if (row_ok) {
-          *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
-          if ((j & 1) == 0)
-            reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 5) + 2 * t + (j >> 1)] =
-                (uint8_t)(e + 127);
+          for (int i = 0; i < 8; ++i) w1 |= e2m1_code(xh[8 + i] * sc) << (4 * i);
+          if (row_ok) {
+            *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
+            if ((j & 1) == 0)
+              reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 5) + (k0 >> 5)] =
+                  (uint8_t)(e + 127);
+          }
         }
       }
-    }
 
-    if constexpr (RB > 0) {
-      // T += X_hat[16 rows, 64 cols] . L1[64 cols, 16*RB]: element i of this
-      // lane is column k0 + i; the B operand takes the same columns of
-      // lora_down (= L1^T) rows.
-      v8bf a0, a1;
+      if constexpr (RB > 0) {
+        // T += X_hat[16 rows, 64 cols] . L1[64 cols, 16*RB]: element i of
+        // this lane is column k0 + i; the B operand takes the same columns of
+        // lora_down (= L1^T) rows.
+        v8bf a0, a1;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a0[i] = __builtin_bit_cast(__bf16, (uint16_t)hb[i]);
-        a1[i] = __builtin_bit_cast(__bf16, (uint16_t)hb[8 + i]);
-      }
+        for (int i = 0; i < 8; ++i) {
+          a0[i] = __builtin_bit_cast(__bf16, (uint16_t)hb[i]);
+          a1[i] = __builtin_bit_cast(__bf16, (uint16_t)hb[8 + i]);
+        }
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const uint16_t* ld = lora_down + (int64_t)(b * 16 + r16) * K + k0;
-        const v8bf b0 = *reinterpret_cast<const v8bf*>(ld);
-        const v8bf b1 = *reinterpret_cast<const v8bf*>(ld + 8);
-        tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, tacc[b], 0, 0, 0);
-        tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, tacc[b], 0, 0, 0);
+        for (int b = 0; b < RB; ++b) {
+          const uint16_t* ld = lora_down + (int64_t)(b * 16 + r16) * K + k0;
+          const v8bf b0 = *reinterpret_cast<const v8bf*>(ld);
+          const v8bf b1 = *reinterpret_cast<const v8bf*>(ld + 8);
+          tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, tacc[b], 0, 0, 0);
+          tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, tacc[b], 0, 0, 0);
+        }
       }
     }
   }
 
   if constexpr (RB > 0) {
-    // Sum the four waves' partial T tiles through LDS.
-    __shared__ float red[QA_WAVES][RB][4][64];
+    // Sum the eight waves' partial T tiles through LDS (in a fixed order).
+    __syncthreads();  // the table is no longer read
+    float(*red)[RB][4][64] = reinterpret_cast<float(*)[RB][4][64]>(smem);
 #pragma unroll
     for (int b = 0; b < RB; ++b)
 #pragma unroll
@@ -138,7 +180,9 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
       const int b = idx / 256;
       const int q = (idx / 64) & 3;
       const int l = idx & 63;
-      const float v = red[0][b][q][l] + red[1][b][q][l] + red[2][b][q][l] + red[3][b][q][l];
+      float v = red[0][b][q][l];
+#pragma unroll
+      for (int w = 1; w < QA_WAVES; ++w) v += red[w][b][q][l];
       // MFMA 16x16 output: lane l, element q -> row 4*(l/16)+q, column l%16.
       const int64_t m = (int64_t)blockIdx.x * QA_ROWS + 4 * (l >> 4) + q;
       if (m < M) T[m * rank + b * 16 + (l & 15)] = v;
