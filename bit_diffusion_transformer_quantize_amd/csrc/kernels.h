@@ -24,8 +24,9 @@ hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down, float* T,
                                hipStream_t s);
 
-// Device workspace the INT4 forward needs: the activation operand image.
+// Device workspace the forward needs: the activation operand image.
 size_t int4_workspace_bytes(int64_t M, int K);
+size_t fp4_workspace_bytes(int64_t M, int K);
 
 // Bytes of the prepared (kernel-layout) weight of each mode, and the
 // launchers that build it from packed codes and scales.
@@ -44,7 +45,7 @@ hipError_t launch_int4_forward(int rank, bool out_f32, int64_t M, int N, int K,
 hipError_t launch_fp4_forward(int rank, bool out_f32, int64_t M, int N, int K,
                               const uint8_t* xcodes, const uint8_t* xscales, const float* T,
                               const void* wimage, const uint16_t* lora_up, const uint16_t* bias,
-                              void* Y, hipStream_t s);
+                              void* Y, void* workspace, hipStream_t s);
 
 hipError_t launch_lowrank_up(int rank, bool out_f32, int64_t M, int N, const float* T,
                              const uint16_t* lora_up, void* Y, hipStream_t s);

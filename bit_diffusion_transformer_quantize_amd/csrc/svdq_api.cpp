@@ -162,7 +162,8 @@ svdq_status svdq_linear_workspace_size(const svdq_desc* d, int64_t M, size_t* by
   SVDQ_TRY(check_desc(d));
   SVDQ_TRY(check_rows_k(M, d->K));
   if (bytes == nullptr) return SVDQ_ERR_ARG;
-  *bytes = d->mode == SVDQ_MODE_INT4 ? svdq::int4_workspace_bytes(M, d->K) : 0;
+  *bytes = d->mode == SVDQ_MODE_INT4 ? svdq::int4_workspace_bytes(M, d->K)
+                                     : svdq::fp4_workspace_bytes(M, d->K);
   return SVDQ_OK;
 }
 
@@ -179,18 +180,17 @@ svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const uint8_t* xc
   if (T != nullptr && (d->rank == 0 || !aligned16(T) || !aligned16(lora_up))) return SVDQ_ERR_ARG;
   if (!opt_ok(bias)) return SVDQ_ERR_ARG;
   const bool f32 = (d->flags & SVDQ_FLAG_OUT_F32) != 0u;
-  if (d->mode == SVDQ_MODE_INT4) {
-    if (!ptr_ok(workspace) || workspace_bytes < svdq::int4_workspace_bytes(M, d->K))
-      return SVDQ_ERR_ARG;
-    SVDQ_TRY(check_device());
+  const size_t need = d->mode == SVDQ_MODE_INT4 ? svdq::int4_workspace_bytes(M, d->K)
+                                                : svdq::fp4_workspace_bytes(M, d->K);
+  if (!ptr_ok(workspace) || workspace_bytes < need) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_device());
+  if (d->mode == SVDQ_MODE_INT4)
     return from_hip(svdq::launch_int4_forward(d->rank, f32, M, d->N, d->K, xcodes,
                                               static_cast<const float*>(xscales), T, wimage,
                                               lora_up, bias, Y, workspace, (hipStream_t)stream));
-  }
-  SVDQ_TRY(check_device());
   return from_hip(svdq::launch_fp4_forward(d->rank, f32, M, d->N, d->K, xcodes,
                                            static_cast<const uint8_t*>(xscales), T, wimage,
-                                           lora_up, bias, Y, (hipStream_t)stream));
+                                           lora_up, bias, Y, workspace, (hipStream_t)stream));
 }
 
 svdq_status svdq_lowrank_down(const svdq_desc* d, int64_t M, const uint16_t* X,

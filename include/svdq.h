@@ -145,17 +145,20 @@ svdq_status svdq_weight_image_size(const svdq_desc* desc, size_t* bytes);
  *         32 rows of W), holding the codes as 6-bit E2M3 fields (value q/8)
  *         in MFMA lane order and the bf16 hi/lo split of the scales; rows
  *         are padded to a multiple of 192 with zeros.
- *   FP4 : the codes [N][K/2] followed, at the next 256-byte boundary, by the
- *         E8M0 scales [N][K/32].
+ *   FP4 : a group-major array of 1024-byte code blocks, one per (64-group,
+ *         32 rows of W), each lane's 16 bytes being the packed codes of one
+ *         row and 32-block, followed by the 64-byte blocks of the E8M0
+ *         scales in the same lane order; rows are padded to a multiple of
+ *         256 with zeros.
  * The image depends only on (mode, N, K) and the codes and scales; it is
  * an opaque operand of svdq_linear_forward. */
 svdq_status svdq_prepare_weight(const svdq_desc* desc, const uint8_t* wcodes,
                                 const void* wscales, void* wimage, void* stream);
 
-/* Bytes of device workspace svdq_linear_forward needs for this shape: in INT4
- * mode the activation operand image, 64 bytes per element of a 64-group
- * row of X with rows padded to a multiple of 256 (K * Mp bytes, Mp = M
- * rounded up to 256), rounded up to 256 bytes; 0 in FP4 mode.  Pure host
+/* Bytes of device workspace svdq_linear_forward needs for this shape: the
+ * activation operand image, in the layout of the prepared weight, with rows
+ * padded to Mp = M rounded up to 256: K * Mp bytes in INT4 mode and
+ * K * Mp * 17 / 32 bytes in FP4 mode, rounded up to 256 bytes.  Pure host
  * function. */
 svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t* bytes);
 
@@ -173,7 +176,7 @@ svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t*
  * rest is fp32 arithmetic (INT4: the product of the two group scales carries
  * a relative error below 2^-15).
  * workspace: device buffer of at least svdq_linear_workspace_size bytes
- * (16-byte aligned; may be NULL when that size is 0).  Its contents are
+ * (16-byte aligned).  Its contents are
  * scratch, overwritten by the call; calls that may run concurrently need
  * separate workspaces. */
 svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const uint8_t* xcodes,

@@ -47,8 +47,9 @@ def test_arch_predicate_null():
 
 def test_workspace_size_is_host_only():
     n = ctypes.c_size_t(123)
+    # FP4: the activation image, 17/32 bytes per element, rows padded to 256
     assert _lib().svdq_linear_workspace_size(_d(mode=1), 256, ctypes.byref(n)) == 0
-    assert n.value == 0                                   # FP4 needs none
+    assert n.value == 512 * 256 * 17 // 32
     assert _lib().svdq_linear_workspace_size(_d(mode=0, K=512, N=256), 300, ctypes.byref(n)) == 0
     # INT4: the activation operand image, K bytes per row, rows padded to 256
     assert n.value == 512 * 512
@@ -63,9 +64,11 @@ def test_weight_image_size_is_host_only():
     assert n.value == 512 * 384
     assert _lib().svdq_weight_image_size(_d(mode=0, K=3072, N=9216), ctypes.byref(n)) == 0
     assert n.value == 3072 * 9216
-    # FP4: codes, then the scales at the next 256-byte boundary
+    # FP4: 1 KB of codes and 64 B of scales per (64-group, 32 rows), rows padded to 256
     assert _lib().svdq_weight_image_size(_d(mode=1, K=512, N=256), ctypes.byref(n)) == 0
-    assert n.value == 256 * 256 + 256 * 16
+    assert n.value == 8 * 8 * (1024 + 64)
+    assert _lib().svdq_weight_image_size(_d(mode=1, K=3072, N=21504), ctypes.byref(n)) == 0
+    assert n.value == 48 * 672 * (1024 + 64)
     assert _lib().svdq_weight_image_size(_d(), None) == ARG
     assert _lib().svdq_weight_image_size(_d(N=200), ctypes.byref(n)) == SHAPE
 
@@ -179,5 +182,5 @@ def test_no_device_is_a_hip_error():
     lib = _lib()
     assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, None) == HIP
     assert lib.svdq_linear_forward(_d(), 256, A, A, A, A, A, A, A, A, 1 << 30, None) == HIP
-    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, A, A, A, A, None, 0, None) == HIP
+    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, A, A, A, A, A, 1 << 30, None) == HIP
     assert lib.svdq_prepare_weight(_d(), A, A, A, None) == HIP
