@@ -38,10 +38,12 @@ __device__ __forceinline__ void split_bf16x8(const v4f& a, const v4f& b, v8bf& h
 // top-left output is (mbase, nbase); rows >= M and columns >= N contribute
 // nothing (their outputs are never stored).  T (fp32) is split into a bf16
 // high and low part, so the two bf16 MFMAs per 16-wide slice of the rank
-// keep the branch accurate to about 2^-16 of |T|.  The loads of slice
-// rb + 16 are issued before slice rb is computed; out-of-range rows and
+// keep the branch accurate to about 2^-16 of |T|.  Out-of-range rows and
 // columns read row 0 and are zeroed, so no load sits under a branch.
-template <int TR, int TC>
+// With DB the first two slices are fetched together and each buffer is
+// refilled as soon as it has been consumed; without it (for callers short
+// of registers) each slice is fetched right before it is used.
+template <int TR, int TC, bool DB = true>
 __device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, int64_t M,
                                                  int N, int64_t mbase, int nbase, int lane,
                                                  const float* __restrict__ T,
@@ -63,32 +65,32 @@ __device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, 
     lok[tc] = n < N;
     lp[tc] = lora_up + (int64_t)(lok[tc] ? n : 0) * rank + koff;
   }
-  v4f ta[TR][2];
-  v8bf la[TC];
-  auto fetch = [&](int rb) {
+  v4f ta[DB ? 2 : 1][TR][2];
+  v8bf la[DB ? 2 : 1][TC];
+  auto fetch = [&](int buf, int rb) {
+    if constexpr (!DB) buf = 0;
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr) {
-      ta[tr][0] = *reinterpret_cast<const v4f*>(tp[tr] + rb);
-      ta[tr][1] = *reinterpret_cast<const v4f*>(tp[tr] + rb + 4);
+      ta[buf][tr][0] = *reinterpret_cast<const v4f*>(tp[tr] + rb);
+      ta[buf][tr][1] = *reinterpret_cast<const v4f*>(tp[tr] + rb + 4);
     }
 #pragma unroll
-    for (int tc = 0; tc < TC; ++tc) la[tc] = *reinterpret_cast<const v8bf*>(lp[tc] + rb);
+    for (int tc = 0; tc < TC; ++tc) la[buf][tc] = *reinterpret_cast<const v8bf*>(lp[tc] + rb);
   };
-  fetch(0);
-  for (int rb = 0; rb < rank; rb += 16) {
+  auto compute = [&](int buf) {
+    if constexpr (!DB) buf = 0;
     v8bf thi[TR], tlo[TR], bv[TC];
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr) {
       const v4f z = {0.f, 0.f, 0.f, 0.f};
-      split_bf16x8(tok[tr] ? ta[tr][0] : z, tok[tr] ? ta[tr][1] : z, thi[tr], tlo[tr]);
+      split_bf16x8(tok[tr] ? ta[buf][tr][0] : z, tok[tr] ? ta[buf][tr][1] : z, thi[tr], tlo[tr]);
     }
 #pragma unroll
     for (int tc = 0; tc < TC; ++tc) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        bv[tc][i] = lok[tc] ? la[tc][i] : __builtin_bit_cast(__bf16, (uint16_t)0);
+        bv[tc][i] = lok[tc] ? la[buf][tc][i] : __builtin_bit_cast(__bf16, (uint16_t)0);
     }
-    if (rb + 16 < rank) fetch(rb + 16);
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr)
 #pragma unroll
@@ -99,6 +101,25 @@ __device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, 
 #pragma unroll
       for (int tc = 0; tc < TC; ++tc)
         acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tlo[tr], bv[tc], acc[tr][tc], 0, 0, 0);
+  };
+  // slices rb (buffer 0) and rb + 16 (buffer 1) per iteration; each
+  // buffer's next slice is fetched as soon as it has been consumed
+  if constexpr (DB) {
+    fetch(0, 0);
+    if (16 < rank) fetch(1, 16);
+    for (int rb = 0; rb < rank; rb += 32) {
+      compute(0);
+      if (rb + 32 < rank) fetch(0, rb + 32);
+      if (rb + 16 < rank) {
+        compute(1);
+        if (rb + 48 < rank) fetch(1, rb + 48);
+      }
+    }
+  } else {
+    for (int rb = 0; rb < rank; rb += 16) {
+      fetch(0, rb);
+      compute(0);
+    }
   }
 }
 
@@ -131,27 +152,33 @@ __device__ __forceinline__ void store_tiles_as(const v16f (&acc)[TR][TC], int64_
                                                const uint16_t* __restrict__ bias,
                                                OutT* __restrict__ Y) {
   const int64_t m_lane = mbase + 4 * (lane >> 5);
+  auto put = [&](OutT* y, float v) {
+    if constexpr (sizeof(OutT) == 4) {
+      *y = ACCUM ? *y + v : v;
+    } else {
+      if (ACCUM) v += bf16_to_f32(*y);
+      *y = (uint16_t)f32_to_bf16(v);
+    }
+  };
 #pragma unroll
   for (int tc = 0; tc < TC; ++tc) {
     const int n = nbase + tc * 32 + (lane & 31);
-    if (n >= N) continue;
+    const bool cols_full = nbase + tc * 32 + 32 <= N;  // wave-uniform
+    if (!cols_full && n >= N) continue;
     const float b = bias ? bf16_to_f32(bias[n]) : 0.f;
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr) {
       const int64_t m_tile = m_lane + tr * 32;
       OutT* yrow = Y + m_tile * N + n;
+      if (cols_full && mbase + tr * 32 + 32 <= M) {  // whole tile inside: no per-element test
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + (i & 3);
-        if (m_tile + r < M) {
-          OutT* y = yrow + (int64_t)r * N;
-          float v = acc[tr][tc][i] + b;
-          if constexpr (sizeof(OutT) == 4) {
-            *y = ACCUM ? *y + v : v;
-          } else {
-            if (ACCUM) v += bf16_to_f32(*y);
-            *y = (uint16_t)f32_to_bf16(v);
-          }
+        for (int i = 0; i < 16; ++i)
+          put(yrow + (int64_t)(8 * (i >> 2) + (i & 3)) * N, acc[tr][tc][i] + b);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + (i & 3);
+          if (m_tile + r < M) put(yrow + (int64_t)r * N, acc[tr][tc][i] + b);
         }
       }
     }

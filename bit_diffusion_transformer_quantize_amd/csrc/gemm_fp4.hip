@@ -214,7 +214,7 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   dma(1);
   if (G > 2) dma(2);
   init_bias_tiles<2, 4>(acc, N, nbase, lane, bias);
-  if (T != nullptr) lowrank_up_tiles<2, 4>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
+  if (T != nullptr) lowrank_up_tiles<2, 4, false>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
   wait_dma(std::integral_constant<int, 0>{});
   asm volatile("s_barrier" ::: "memory");
   Frags f0, f1;
