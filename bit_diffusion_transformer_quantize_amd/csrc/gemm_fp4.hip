@@ -25,9 +25,10 @@
 // scales) copied by the global->LDS DMA.
 //
 // Pipeline: a 512-thread workgroup computes 256 x 256 outputs; each of its 8
-// waves owns 64 x 128 (2 x 4 tiles).  One stage = one 64-group; LDS holds a
-// ring of 4 stage slots, the DMA runs two groups ahead and the fragments of
-// the next group are read while the MFMAs of the current one run.
+// waves owns 64 x 128 (2 x 4 tiles).  One stage = two 64-groups; LDS holds a
+// ring of 4 stage slots, the DMA runs two stages ahead, and the fragments of
+// the next group are read while the MFMAs of the current one run, so there
+// is one barrier per two groups.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -45,7 +46,8 @@ constexpr int F4_SCALE_BLOCK = 64;
 constexpr int F4_SL_BCODES = 8 * F4_CODE_BLOCK;             // W codes after 8 KB of X codes
 constexpr int F4_SL_XSCALES = 16 * F4_CODE_BLOCK;           // then 512 B of X scales
 constexpr int F4_SL_WSCALES = F4_SL_XSCALES + 8 * F4_SCALE_BLOCK;
-constexpr int F4_SLOT = F4_SL_WSCALES + 8 * F4_SCALE_BLOCK;  // 17408 bytes
+constexpr int F4_GRP = F4_SL_WSCALES + 8 * F4_SCALE_BLOCK;  // 17408 bytes per group
+constexpr int F4_SLOT = 2 * F4_GRP;                          // a stage holds two groups
 constexpr int FP4_FMT = 4;                                   // f8f6f4 format code of E2M1
 
 typedef __attribute__((address_space(3))) void lds_void_f4;
@@ -166,16 +168,22 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   const uint32_t voff_s = (uint32_t)((sch & 1) * 256 + lane * 4);
   const bool s_w = sch >= 2;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_f4*)lds;
-  auto dma = [&](int g) {
-    const uint32_t slot = lds_base + (uint32_t)((g & (F4_NSLOT - 1)) * F4_SLOT);
+  // DMA of one group into its half of its stage slot
+  auto dma_group = [&](int g) {
+    const uint32_t slot =
+        lds_base + (uint32_t)(((g >> 1) & (F4_NSLOT - 1)) * F4_SLOT + (g & 1) * F4_GRP);
     dma16_f4(xrun + g * xstride, voff_c, slot + wave * 1024);
     dma16_f4(wrun + g * wstride, voff_c, slot + F4_SL_BCODES + wave * 1024);
     const uint8_t* sb = s_w ? wsrun + g * wsstride : xsrun + g * xsstride;
     dma4_f4(sb, voff_s, slot + F4_SL_XSCALES + sch * 256);
   };
+  auto dma = [&](int st) {  // one stage = groups 2 st, 2 st + 1
+    dma_group(2 * st);
+    dma_group(2 * st + 1);
+  };
   auto wait_dma = [&](auto og_tag) {
     constexpr int OG = decltype(og_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * OG));  // vmcnt(3 OG)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (6 * OG));  // vmcnt(6 OG): 6 DMAs per stage
   };
 
   // ---- fragments: lane-linear reads within a slot
@@ -188,7 +196,7 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
     int sa[2], sb[4];
   };
   auto load_frags = [&](Frags& f, int g) {
-    const uint8_t* sp = lds + (g & (F4_NSLOT - 1)) * F4_SLOT;
+    const uint8_t* sp = lds + ((g >> 1) & (F4_NSLOT - 1)) * F4_SLOT + (g & 1) * F4_GRP;
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr) {
       const v4u x = *reinterpret_cast<const v4u*>(sp + fa + tr * F4_CODE_BLOCK);
@@ -207,12 +215,13 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   const int64_t mbase = m0 + wm * 64;
   const int nbase = n0 + wn * 128;
 
-  // ---- prologue: groups 0..2 in flight; the accumulators start from the
+  // ---- prologue: stages 0..2 in flight; the accumulators start from the
   // bias and the low-rank term T L2 (their loads are issued after the DMAs,
   // so waiting for them also waits for the DMAs: vmcnt counts in order).
+  const int S = G >> 1;  // stages (G is even)
   dma(0);
-  dma(1);
-  if (G > 2) dma(2);
+  if (S > 1) dma(1);
+  if (S > 2) dma(2);
   init_bias_tiles<2, 4>(acc, N, nbase, lane, bias);
   if (T != nullptr) lowrank_up_tiles<2, 4, false>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
   wait_dma(std::integral_constant<int, 0>{});
@@ -220,17 +229,21 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   Frags f0, f1;
   load_frags(f0, 0);
 
-  // One group: make the next slot ready (own DMA + barrier), issue the DMA
-  // three groups ahead, read the next fragments, then the 8 MFMAs.
+  // One group g (of stage st = g / 2): prepare the next group's fragments,
+  // then the 8 MFMAs.  KIND -1: the next group is in the same slot (even g);
+  // for odd g the next group starts stage st+1, whose DMA must have landed
+  // (own wait + barrier): KIND 0 also issues the DMA of stage st+3; 1: stage
+  // st+2 is the last (nothing to issue); 2: st+1 is the last (nothing in
+  // flight); 3: the last group of all.
   auto group = [&](int g, Frags& cur, Frags& nxt, auto kind_tag) {
-    constexpr int KIND = decltype(kind_tag)::value;  // as in the INT4 kernel
-    if constexpr (KIND != 3) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    if constexpr (KIND >= 0 && KIND <= 2) {
       if constexpr (KIND <= 1) wait_dma(std::integral_constant<int, 1>{});
       if constexpr (KIND == 2) wait_dma(std::integral_constant<int, 0>{});
       asm volatile("s_barrier" ::: "memory");
-      if constexpr (KIND == 0) dma(g + 3);
-      load_frags(nxt, g + 1);
+      if constexpr (KIND == 0) dma((g >> 1) + 3);
     }
+    if constexpr (KIND != 3) load_frags(nxt, g + 1);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out before the MFMAs
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
@@ -240,26 +253,31 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
             cur.a[tr], cur.b[tc], acc[tr][tc], FP4_FMT, FP4_FMT, 0, cur.sa[tr], 0, cur.sb[tc]);
     __builtin_amdgcn_sched_barrier(0);
   };
+  using KE = std::integral_constant<int, -1>;
   using K0 = std::integral_constant<int, 0>;
   using K1 = std::integral_constant<int, 1>;
   using K2 = std::integral_constant<int, 2>;
   using K3 = std::integral_constant<int, 3>;
 
-  // G is even: the steady part runs in pairs (fragment sets alternate); the
-  // tail is kinds 1 (if G >= 4), 2 and 3.
-  int g = 0;
-  for (; g + 4 < G; g += 2) {
-    group(g, f0, f1, K0{});
-    group(g + 1, f1, f0, K0{});
+  // f0 holds the first group of every stage.  The tail is kinds 1 (if at
+  // least 3 stages), 2 (if at least 2) and 3.
+  int st = 0;
+  for (; st + 3 < S; ++st) {
+    group(2 * st, f0, f1, KE{});
+    group(2 * st + 1, f1, f0, K0{});
   }
-  // here G - g is 2 or 4 (G even); g is even, so f0 holds group g
-  if (G - g == 4) {
-    group(g, f0, f1, K0{});
-    group(g + 1, f1, f0, K1{});
-    g += 2;
+  if (S - st == 3) {
+    group(2 * st, f0, f1, KE{});
+    group(2 * st + 1, f1, f0, K1{});
+    ++st;
   }
-  group(g, f0, f1, K2{});
-  group(g + 1, f1, f0, K3{});
+  if (S - st == 2) {
+    group(2 * st, f0, f1, KE{});
+    group(2 * st + 1, f1, f0, K2{});
+    ++st;
+  }
+  group(2 * st, f0, f1, KE{});
+  group(2 * st + 1, f1, f0, K3{});
 
   store_tiles<2, 4, false>(acc, M, N, mbase, nbase, lane, nullptr, out_f32 != 0, Y);
 }
