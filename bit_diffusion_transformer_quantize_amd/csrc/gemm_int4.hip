@@ -1,6 +1,7 @@
 // INT4-mode W4A4 GEMM of the SVDQuant linear on gfx950.
 //
-//   Y0[m][n] = sum_g sx[m][g] sw[n][g] P_g[m][n],   P_g = sum_{k in g} qx qw
+//   Y = sum_g sx[m][g] sw[n][g] P_g[m][n] + T L2 + bias,
+//   P_g = sum_{k in g} qx[m][k] qw[n][k]
 //
 // Per 32x32 output tile and 64-element group g:
 //   * P_g is one v_mfma_scale_f32_32x32x64_f8f6f4 on FP6 (E2M3) operands.  In
@@ -15,35 +16,37 @@
 //     exact product of the split scales, within 2^-16 of sx*sw.
 //   * acc += P_g * S_g is the one VALU FMA per output and group, inherent to
 //     two-sided per-group fp32 scales.
+// The low-rank term (the up-projection of the 16-bit branch, fused into the
+// 4-bit kernel as on the apatero.com page, section "O que e Nunchaku e como
+// acelera modelos Qwen") is T L2 with T split into bf16 high and low parts:
+// two v_mfma_f32_32x32x16_bf16 per 16 ranks accumulate it straight into acc.
 //
-// Operand images.  Both operands reach the kernel as a group-major "image"
-// of 2048-byte blocks, one per (group g, 32-row tile), laid out exactly as
-// the MFMA lanes read them:
-//   [0, 768)     K half 0 (elements 0..31 of the group): 32 rows x 24 bytes,
-//                the first 16 bytes of each row at 16*row, the last 8 at
-//                512 + 8*row (so b128 and b64 reads are lane-linear);
-//   [768, 1536)  K half 1, same layout;
-//   [1536, 2048) the 8-byte bf16 scale operand of each of the 64 lanes.
-// A row's 32 fields of 6 bits are packed little-endian (field j at bit 6j).
-// The activation image is built per call by the prep kernel (workspace);
-// the weight image is built once by svdq_prepare_weight.  A workgroup's
-// stage is then two contiguous runs of the images (16 KB of X, 12 KB of W)
-// that the global->LDS DMA copies verbatim.
+// Both operands come as images (image.h) laid out in MFMA lane order, and
+// everything the kernel reads (codes, scale operands, T, L2, bias) reaches
+// LDS through global->LDS DMA of contiguous runs.  The kernel is persistent:
+// each workgroup walks a stream of stages over its tiles; per tile the
+// stream holds P "pre" stages (the bias and one 16-rank slice of T and L2
+// each) and then G code stages (one 64-group each).  Every stage is one LDS
+// ring slot and every wave issues exactly four DMAs per stage, so the DMA
+// engine simply runs two stages ahead, across tile boundaries: the next
+// tile's bias, low-rank slices and first groups arrive while the current
+// tile finishes.
 //
-// Pipeline: a 512-thread workgroup computes 256 x 192 outputs; each of its 8
-// waves (two per SIMD) owns 64 x 96 (2 x 3 tiles).  One stage = one group;
-// LDS holds a ring of 4 stage slots.  Within a group the MFMAs of tile t+1
-// are issued before the FMAs of tile t, and every fragment register is
-// reloaded for the next group right after its last MFMA has been issued, so
-// no wave waits for LDS at a group boundary.  Once per group every wave
-// waits for its own DMA of the next group, joins the barrier, and issues the
-// DMA of the group three ahead.
-// Workgroups are renumbered so that each XCD (own L2) walks a band of
-// I4_GROUP_M row tiles of X across all weight columns.
+// Compute: a 512-thread workgroup computes 256 x 192 outputs; each of its 8
+// waves (two per SIMD) owns 64 x 96 (2 x 3 MFMA tiles).  The weight is the A
+// operand and the activations the B operand of every MFMA, so a lane's
+// accumulator holds one output row and quads of consecutive columns, which
+// the epilogue stores 16 bytes at a time.  Within a group the
+// MFMAs of tile t+1 are issued before the FMAs of tile t in the fixed order
+// P MFMA, 8 FMAs, S MFMA, 8 FMAs, and each fragment register is reloaded for
+// the next group right after its last MFMA.
+// Tiles are ordered so that the workgroups of one XCD (own L2) walk a band
+// of I4_GROUP_M row tiles of X across all weight columns.
 #include <algorithm>
 #include <type_traits>
 
 #include "gemm_common.h"
+#include "image.h"
 #include "kernels.h"
 
 namespace svdq {
@@ -53,39 +56,30 @@ constexpr int I4_BN = 192;
 constexpr int I4_THREADS = 512;
 constexpr int I4_SCALE_BYTE = 127 + 3;  // E2M3 field q has value q/8
 constexpr int I4_GROUP_M = 2;           // tile rows walked together per XCD
-constexpr int I4_NSLOT = 4;  // stage slots: DMA runs two groups ahead
-constexpr int IMG_BLOCK = 2048;                                // bytes per (group, 32 rows)
-constexpr int SLOT_A = (I4_BM / 32) * IMG_BLOCK;               // 16 KB of X
-constexpr int SLOT_BYTES = SLOT_A + (I4_BN / 32) * IMG_BLOCK;  // + 12 KB of W
-constexpr int FP6_FMT = 2;                                     // f8f6f4 format code of E2M3
+constexpr int I4_NSLOT = 4;
+constexpr int SLOT_A = (I4_BM / 32) * I4_BLOCK;               // 16 KB of X
+constexpr int SLOT_BYTES = SLOT_A + (I4_BN / 32) * I4_BLOCK;  // + 12 KB of W
+// pre-stage layout inside a slot: T hi/lo blocks, L2 blocks, the bias run
+constexpr int PRE_L2 = (I4_BM / 32) * LR_XBLOCK;              // 16 KB
+constexpr int PRE_BIAS = PRE_L2 + (I4_BN / 32) * LR_WBLOCK;   // 22 KB
+static_assert(PRE_BIAS + 1024 <= SLOT_BYTES, "pre-stage fits a slot");
+constexpr int FP6_FMT = 2;  // f8f6f4 format code of E2M3
+// vector memory operations of one full output tile's bf16 stores per wave
+// (2 per 32x32 tile; the fp32 form issues more, which only waits longer)
+constexpr int I4_NST = 2 * 2 * 3;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-
-static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// Rows of the activation image are padded to the workgroup's 256 rows and
-// columns of the weight image to its 192 columns (zero codes and scales).
-static inline int64_t pad_rows(int64_t M) { return (M + I4_BM - 1) / I4_BM * I4_BM; }
-static inline int64_t pad_cols(int64_t N) { return (N + I4_BN - 1) / I4_BN * I4_BN; }
-static inline size_t image_bytes(int64_t rows_padded, int K) {
-  return (size_t)(K / 64) * (size_t)(rows_padded / 32) * IMG_BLOCK;
-}
-
-size_t int4_workspace_bytes(int64_t M, int K) { return align256(image_bytes(pad_rows(M), K)); }
-
-size_t int4_weight_image_bytes(int N, int K) { return image_bytes(pad_cols(N), K); }
 
 // Global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4 with a
 // scalar base): lane i reads sbase + voff and writes LDS bytes
 // [lds_addr + 16 i, +16).  Written as a small asm block (it has no register
 // outputs) so that the compiler neither drains it at barriers nor serialises
 // consecutive DMAs; the kernel waits for it with explicit s_waitcnt vmcnt.
-// The base is wave-uniform by construction; readfirstlane makes that explicit
-// so that it is kept in scalar registers.
+// The base is wave-uniform by construction; readfirstlane makes that
+// explicit (each half zero-extended: readfirstlane returns a signed int).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   const uint64_t b = reinterpret_cast<uint64_t>(sbase);
-  // (readfirstlane returns a signed int: zero-extend each half explicitly)
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint64_t sb = ((uint64_t)hi << 32) | lo;
@@ -95,92 +89,57 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
-// ---------------------------------------------------------------- images
-// 32 two's-complement int4 codes (16 bytes, element 2j in the low nibble of
-// byte j) -> 32 E2M3 sign-magnitude fields of 6 bits (value q/8) packed into
-// six dwords.  For a nibble x the field is x when x < 8 and 0x20 | (16 - x)
-// = 0x30 - x otherwise.
-__device__ __forceinline__ void int4x32_to_fp6x32(const v4u& w, uint32_t (&o)[6]) {
-  uint64_t bits[3] = {0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t x = (w[j >> 3] >> (4 * (j & 7))) & 15u;
-    const uint64_t f = x < 8u ? x : 0x30u - x;
-    const int b = 6 * j;
-    bits[b >> 6] |= f << (b & 63);
-    if ((b & 63) > 58) bits[(b >> 6) + 1] |= f >> (64 - (b & 63));
+// Global -> LDS DMA of 4 bytes per lane (global_load_lds_dword): lane i
+// reads sbase + voff and writes LDS bytes [lds_addr + 4 i, +4).
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+// Output tile coordinates of band-ordered tile number L.
+struct TileXY {
+  int tm, tn;
+};
+
+__device__ __forceinline__ TileXY tile_xy(int L, int num_m, int num_n) {
+  const int band = L / (I4_GROUP_M * num_n);
+  const int first_m = band * I4_GROUP_M;
+  const int gm = min(num_m - first_m, I4_GROUP_M);
+  const int in_band = L - band * I4_GROUP_M * num_n;
+  return TileXY{first_m + in_band % gm, in_band / gm};
+}
+
+// Band-ordered tile number of the k-th tile of workgroup b: with the grid
+// and the tile count both multiples of 8, the workgroups of XCD b%8 share a
+// contiguous eighth of the tiles; otherwise tiles go round-robin.
+__device__ __forceinline__ int tile_number(int b, int k, int nwg, int ntiles) {
+  if ((nwg & 7) == 0 && (ntiles & 7) == 0) {
+    const int per = ntiles >> 3, nw = nwg >> 3;
+    return (b & 7) * per + (b >> 3) + k * nw;
   }
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    o[2 * i] = (uint32_t)bits[i];
-    o[2 * i + 1] = (uint32_t)(bits[i] >> 32);
+  return b + k * nwg;
+}
+
+__device__ __forceinline__ int tiles_of(int b, int nwg, int ntiles) {
+  if ((nwg & 7) == 0 && (ntiles & 7) == 0) {
+    const int per = ntiles >> 3, nw = nwg >> 3, w = b >> 3;
+    return w < per ? (per - w + nw - 1) / nw : 0;
   }
+  return b < ntiles ? (ntiles - b + nwg - 1) / nwg : 0;
 }
 
-// One wave per (group, 32-row tile) block of an operand image.  Rows R .. RP-1
-// are zero.  XSIDE selects the scale-operand pattern:
-//   X: lanes 0..31 {hi | lo << 16, hi}, lanes 32..63 {lo, 0}
-//   W: lanes 0..31 {hi | hi << 16, lo}, lanes 32..63 {lo, 0}
-// so that K slots 0..3 of the outer-product MFMA hold hi*hi, lo*hi, hi*lo, 0
-// and slot 4 lo*lo.
-template <bool XSIDE>
-__global__ __launch_bounds__(256) void int4_image_kernel(int64_t R, int64_t RP, int K,
-                                                         const uint8_t* __restrict__ codes,
-                                                         const float* __restrict__ scales,
-                                                         uint8_t* __restrict__ image) {
-  const int G = K >> 6;
-  const int64_t RT = RP >> 5;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= (int64_t)G * RT) return;
-  const int g = (int)(blk / RT);
-  const int64_t r = (blk - (int64_t)g * RT) * 32 + (threadIdx.x & 31);
-  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-  uint8_t* out = image + blk * IMG_BLOCK;
-  v4u w = {0u, 0u, 0u, 0u};
-  float sv = 0.f;
-  if (r < R) {
-    w = *reinterpret_cast<const v4u*>(codes + r * (K >> 1) + g * 32 + h * 16);
-    sv = scales[r * G + g];
-  }
-  uint32_t o[6];
-  int4x32_to_fp6x32(w, o);
-  *reinterpret_cast<v4u*>(out + h * 768 + l32 * 16) = v4u{o[0], o[1], o[2], o[3]};
-  *reinterpret_cast<v2u*>(out + h * 768 + 512 + l32 * 8) = v2u{o[4], o[5]};
-  const uint32_t hb = f32_to_bf16(sv);
-  const uint32_t lb = f32_to_bf16(sv - bf16_to_f32(hb));
-  v2u so;
-  if (h == 0)
-    so = XSIDE ? v2u{hb | (lb << 16), hb} : v2u{hb | (hb << 16), lb};
-  else
-    so = v2u{lb, 0u};
-  *reinterpret_cast<v2u*>(out + 1536 + lane * 8) = so;
-}
-
-static hipError_t launch_image(bool xside, int64_t R, int64_t RP, int K, const uint8_t* codes,
-                               const float* scales, uint8_t* image, hipStream_t s) {
-  const int64_t blocks = ((int64_t)(K / 64) * (RP / 32) + 3) / 4;
-  if (xside)
-    hipLaunchKernelGGL(int4_image_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, R, RP,
-                       K, codes, scales, image);
-  else
-    hipLaunchKernelGGL(int4_image_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, R,
-                       RP, K, codes, scales, image);
-  return hipGetLastError();
-}
-
-hipError_t launch_int4_prepare_weight(int N, int K, const uint8_t* wcodes, const float* wscales,
-                                      void* wimage, hipStream_t s) {
-  return launch_image(false, N, pad_cols(N), K, wcodes, wscales,
-                      reinterpret_cast<uint8_t*>(wimage), s);
-}
-
-// ---------------------------------------------------------------- GEMM
 __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     int64_t M, int N, int K, int rank, int out_f32, const uint8_t* __restrict__ ximg,
-    int x_tiles, const uint8_t* __restrict__ wimg, int w_tiles, const float* __restrict__ T,
-    const uint16_t* __restrict__ lora_up, const uint16_t* __restrict__ bias,
-    void* __restrict__ Y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[I4_NSLOT * SLOT_BYTES];
+    int64_t x_rt, int64_t x_lr, const uint8_t* __restrict__ wimg, int64_t w_ct, int64_t w_lr,
+    int64_t w_bias, void* __restrict__ Y) {
+  // the ring, then a 256-byte pad that only dummy DMAs write
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[I4_NSLOT * SLOT_BYTES + 256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,76 +148,126 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // tile order: XCD-contiguous ranges, grouped by I4_GROUP_M tile rows
-  const int num_m = x_tiles / (I4_BM / 32);
-  const int num_n = w_tiles / (I4_BN / 32);
-  const int nb = gridDim.x;
-  int L = blockIdx.x;
-  if ((nb & 7) == 0) L = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
-  const int band = L / (I4_GROUP_M * num_n);
-  const int first_m = band * I4_GROUP_M;
-  const int gm = min(num_m - first_m, I4_GROUP_M);
-  const int in_band = L - band * I4_GROUP_M * num_n;
-  const int tile_m = first_m + in_band % gm;
-  const int tile_n = in_band / gm;
-  const int64_t m0 = (int64_t)tile_m * I4_BM;
-  const int n0 = tile_n * I4_BN;
+  const int num_m = (int)(x_rt / (I4_BM / 32));
+  const int num_n = (int)(w_ct / (I4_BN / 32));
+  const int ntiles = num_m * num_n;
+  const int nwg = gridDim.x;
+  const int b = blockIdx.x;
+  const int my_tiles = tiles_of(b, nwg, ntiles);
+  if (my_tiles == 0) return;  // uniform per workgroup: no barrier is reached
   const int G = K >> 6;
+  const int R16 = rank >> 4;
+  // pre-stages per tile: the bias rides in the first, one 16-rank slice of
+  // the low-rank branch in each of the first R16; at least four, so that
+  // the first four positions of every tile (whose waits differ) are all
+  // pre-stages and every code stage waits the same way
+  const int P = R16 > 4 ? R16 : 4;
+  const int SPT = P + G;            // stages per tile
+  const int total = my_tiles * SPT;
 
-  // ---- DMA plan: a stage is 28 chunks of 1 KB (16 of X, then 12 of W) that
-  // land at slot + 1 KB * chunk.  Wave w moves chunks w, w+8 (X) and w+16
-  // (W); waves 0..3 also w+24 (W), while waves 4..7 repeat their chunk w+16
-  // (the same bytes to the same place).  Every wave thus has four DMAs per
-  // group and waits with the same counts, with no branch in the loop.
-  const uint8_t* xrun = ximg + (int64_t)tile_m * (I4_BM / 32) * IMG_BLOCK;
-  const uint8_t* wrun = wimg + (int64_t)tile_n * (I4_BN / 32) * IMG_BLOCK;
-  const int64_t xstride = (int64_t)x_tiles * IMG_BLOCK;  // bytes per group
-  const int64_t wstride = (int64_t)w_tiles * IMG_BLOCK;
-  const uint32_t voff0 = (uint32_t)(wave * 1024 + lane * 16);
-  const uint32_t voff1 = voff0 + 8 * 1024;
-  const int wave4 = wave < 4 ? wave + 24 : wave + 16;  // LDS chunk of the 4th DMA
-  const uint32_t voff3 = (uint32_t)((wave4 - 16) * 1024 + lane * 16);
+  // ---- DMA, generic form: stream position q (the heads and tails of
+  // tiles).  Wave w moves chunk slots w, w+8, w+16, w+24 of the stage (1 KB
+  // each, landing at slot + 1 KB * chunk).
+  //   code stage: chunks 0..15 X codes, 16..27 W codes, 28..31 repeat 16..19
+  //   pre stage:  chunks 0..15 T hi/lo, 16..21 L2, 22 the bias run,
+  //               23..31 repeat 14..22 (a pre stage past the rank: every
+  //               chunk is the bias run)
+  // A repeated chunk writes the same bytes to the same place.
+  const uint32_t voff = (uint32_t)(lane * 16);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
-  auto slot_of = [](int g) { return (g & (I4_NSLOT - 1)) * SLOT_BYTES; };
-  auto dma = [&](int g) {
-    const uint32_t slot = lds_base + (uint32_t)slot_of(g);
-    const uint8_t* xs = xrun + g * xstride;
-    const uint8_t* ws = wrun + g * wstride;
-    dma16(xs, voff0, slot + wave * 1024);
-    dma16(xs, voff1, slot + (wave + 8) * 1024);
-    dma16(ws, voff0, slot + (wave + 16) * 1024);
-    dma16(ws, voff3, slot + wave4 * 1024);
+  TileXY cur_t = tile_xy(tile_number(b, 0, nwg, ntiles), num_m, num_n);
+  TileXY nxt_t = my_tiles > 1 ? tile_xy(tile_number(b, 1, nwg, ntiles), num_m, num_n) : cur_t;
+  int cur_base = 0;  // stream position of the current tile's first stage
+  auto dma_stage = [&](int q) {
+    const int qq = min(q, total - 1);  // past the end: re-read the last stage
+    int j = qq - cur_base;
+    const bool in_next = j >= SPT;
+    j = in_next ? j - SPT : j;
+    const int tm = in_next ? nxt_t.tm : cur_t.tm;
+    const int tn = in_next ? nxt_t.tn : cur_t.tn;
+    const bool pre = j < P;
+    const bool lr = pre && j < R16;
+    const int g = pre ? 0 : j - P;
+    const int jl = lr ? j : 0;
+    const uint8_t* xc = ximg + ((int64_t)g * x_rt + tm * (I4_BM / 32)) * I4_BLOCK;
+    const uint8_t* wc = wimg + ((int64_t)g * w_ct + tn * (I4_BN / 32)) * I4_BLOCK;
+    const uint8_t* tl = ximg + x_lr + ((int64_t)jl * x_rt + tm * (I4_BM / 32)) * LR_XBLOCK;
+    const uint8_t* ll = wimg + w_lr + ((int64_t)jl * w_ct + tn * (I4_BN / 32)) * LR_WBLOCK;
+    const uint8_t* bs = wimg + w_bias + (int64_t)tn * (I4_BN / 32) * BIAS_BLOCK;
+    const uint32_t slot = lds_base + (uint32_t)((q & (I4_NSLOT - 1)) * SLOT_BYTES);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = wave + 8 * i;
+      // code stage
+      const int cc = c >= 28 ? c - 12 : c;
+      const uint8_t* csrc = cc < 16 ? xc + cc * 1024 : wc + (cc - 16) * 1024;
+      // pre stage
+      const int pc = lr ? (c >= 23 ? c - 9 : c) : 22;
+      const uint8_t* psrc = pc < 16 ? tl + pc * 1024 : (pc < 22 ? ll + (pc - 16) * 1024 : bs);
+      const uint8_t* src = pre ? psrc : csrc;
+      const int dst = (pre ? pc : cc) * 1024;
+      dma16(src, voff, slot + (uint32_t)dst);
+    }
   };
-  // wait until at most OG groups of this wave's DMA are still in flight
-  auto wait_dma = [&](auto og_tag) {
-    constexpr int OG = decltype(og_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * OG));  // vmcnt(4 OG)
+  // ---- DMA, body form: a code stage of the current tile from running
+  // pointers (xrun, wrun: the X and W code blocks of the target group),
+  // moving the chunks the generic form gives this wave: X chunks w and
+  // w + 8, W chunks w and c3.
+  const int c3 = wave < 4 ? wave + 8 : wave - 4;
+  const uint32_t dx0 = (uint32_t)wave * 1024, dx1 = dx0 + 8 * 1024;
+  const uint32_t dw2 = SLOT_A + dx0, dw3 = SLOT_A + (uint32_t)c3 * 1024;
+  const int64_t xstep = x_rt * I4_BLOCK, wstep = w_ct * I4_BLOCK;
+  const uint8_t* xrun = ximg;
+  const uint8_t* wrun = wimg;
+  auto dma_code = [&](int q) {
+    const uint32_t slot = lds_base + (uint32_t)((q & (I4_NSLOT - 1)) * SLOT_BYTES);
+    dma16(xrun + dx0, voff, slot + dx0);
+    dma16(xrun + dx1, voff, slot + dx1);
+    dma16(wrun + dx0, voff, slot + dw2);
+    dma16(wrun + (dw3 - SLOT_A), voff, slot + dw3);
+    xrun += xstep;
+    wrun += wstep;
   };
-  using OG0 = std::integral_constant<int, 0>;
-  using OG1 = std::integral_constant<int, 1>;
+  // Waits for this wave's DMA of the stage about to be read.  Vector memory
+  // operations of a wave complete in issue order on gfx9, so the wait names
+  // how many younger operations may still be in flight: in the body of a
+  // tile the next stage's four DMAs (vmcnt(4)); at the first four stages of
+  // a tile (j = 0..3) up to three younger stages plus the I4_NST output
+  // stores of the previous tile, issued behind them (before the first tile,
+  // I4_NST dummy DMAs into the pad stand in for them).
+  auto wait_stage = [] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); };
+  auto wait_head2 = [] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + I4_NST)); };  // j = 2, 3
+  auto wait_at = [&](int j) {
+    if (j == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12 + I4_NST));
+    else if (j == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + I4_NST));
+    else if (j < 4) wait_head2();
+    else wait_stage();
+  };
+  auto barrier = [] { asm volatile("s_barrier" ::: "memory"); };
 
-  // ---- fragment offsets within a slot (see the image layout above)
-  const int fa = (wm * 2) * IMG_BLOCK + h * 768 + l32 * 16;
-  const int fa8 = (wm * 2) * IMG_BLOCK + h * 768 + 512 + l32 * 8;
-  const int fsa = (wm * 2) * IMG_BLOCK + 1536 + lane * 8;
-  const int fb = SLOT_A + (wn * 3) * IMG_BLOCK + h * 768 + l32 * 16;
-  const int fb8 = SLOT_A + (wn * 3) * IMG_BLOCK + h * 768 + 512 + l32 * 8;
-  const int fsb = SLOT_A + (wn * 3) * IMG_BLOCK + 1536 + lane * 8;
+  // ---- fragments within a slot (see the image layout)
+  const int fa = (wm * 2) * I4_BLOCK + h * 768 + l32 * 16;
+  const int fa8 = (wm * 2) * I4_BLOCK + h * 768 + 512 + l32 * 8;
+  const int fsa = (wm * 2) * I4_BLOCK + 1536 + lane * 8;
+  const int fb = SLOT_A + (wn * 3) * I4_BLOCK + h * 768 + l32 * 16;
+  const int fb8 = SLOT_A + (wn * 3) * I4_BLOCK + h * 768 + 512 + l32 * 8;
+  const int fsb = SLOT_A + (wn * 3) * I4_BLOCK + 1536 + lane * 8;
 
   v8i af[2], bf[3];
   v4s sa[2], sb[3];
   auto load_a = [&](const uint8_t* sp, int tr) {
-    const v4u x = *reinterpret_cast<const v4u*>(sp + fa + tr * IMG_BLOCK);
-    const v2u y = *reinterpret_cast<const v2u*>(sp + fa8 + tr * IMG_BLOCK);
+    const v4u x = *reinterpret_cast<const v4u*>(sp + fa + tr * I4_BLOCK);
+    const v2u y = *reinterpret_cast<const v2u*>(sp + fa8 + tr * I4_BLOCK);
     af[tr] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
-    sa[tr] = *reinterpret_cast<const v4s*>(sp + fsa + tr * IMG_BLOCK);
+    sa[tr] = *reinterpret_cast<const v4s*>(sp + fsa + tr * I4_BLOCK);
   };
   auto load_b = [&](const uint8_t* sp, int tc) {
-    const v4u x = *reinterpret_cast<const v4u*>(sp + fb + tc * IMG_BLOCK);
-    const v2u y = *reinterpret_cast<const v2u*>(sp + fb8 + tc * IMG_BLOCK);
+    const v4u x = *reinterpret_cast<const v4u*>(sp + fb + tc * I4_BLOCK);
+    const v2u y = *reinterpret_cast<const v2u*>(sp + fb8 + tc * I4_BLOCK);
     bf[tc] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
-    sb[tc] = *reinterpret_cast<const v4s*>(sp + fsb + tc * IMG_BLOCK);
+    sb[tc] = *reinterpret_cast<const v4s*>(sp + fsb + tc * I4_BLOCK);
   };
+  auto slot_ptr = [&](int q) { return lds + (q & (I4_NSLOT - 1)) * SLOT_BYTES; };
 
   v16f zero;
 #pragma unroll
@@ -268,28 +277,23 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
 
   // tile t of a wave = (t / 3, t % 3); its P and S live in p/sc[t & 1]
   auto mfma_p = [&](int t) {
-    const int tr = t / 3, tc = t % 3, b = t & 1;
-    p[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[tr], bf[tc], zero, FP6_FMT, FP6_FMT,
-                                                           0, I4_SCALE_BYTE, 0, I4_SCALE_BYTE);
+    const int tr = t / 3, tc = t % 3, bb = t & 1;
+    p[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[tc], af[tr], zero, FP6_FMT, FP6_FMT,
+                                                            0, I4_SCALE_BYTE, 0, I4_SCALE_BYTE);
   };
   auto mfma_s = [&](int t) {
-    const int tr = t / 3, tc = t % 3, b = t & 1;
-    sc[b] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sa[tr], sb[tc], zero, 0, 0, 0);
-  };
-  auto mfma_tile = [&](int t) {
-    mfma_p(t);
-    mfma_s(t);
+    const int tr = t / 3, tc = t % 3, bb = t & 1;
+    sc[bb] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sb[tc], sa[tr], zero, 0, 0, 0);
   };
   // FMAs i0 .. i0+7 of tile t: acc += P * S
   auto fma_half = [&](int t, int i0) {
-    const int tr = t / 3, tc = t % 3, b = t & 1;
+    const int tr = t / 3, tc = t % 3, bb = t & 1;
 #pragma unroll
-    for (int i = i0; i < i0 + 8; ++i) acc[tr][tc][i] = fmaf(p[b][i], sc[b][i], acc[tr][tc][i]);
+    for (int i = i0; i < i0 + 8; ++i) acc[tr][tc][i] = fmaf(p[bb][i], sc[bb][i], acc[tr][tc][i]);
   };
   // One step: the MFMAs of tile `next` (if any) interleaved with the FMAs of
   // tile `cur`, in the fixed order P MFMA, 8 FMAs, S MFMA, loads (of the
-  // fragments both MFMAs just read for the last time), 8 FMAs, so that each
-  // MFMA runs under a block of FMAs.
+  // fragments both MFMAs just read for the last time), 8 FMAs.
   auto step = [&](int next, int cur, auto&& loads) {
     if (next >= 0) mfma_p(next);
     __builtin_amdgcn_sched_barrier(0);
@@ -302,26 +306,34 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One group.  The DMA of group g+3 is issued in group g; at the barrier
-  // of group g the DMA of g+1 must have landed.  KIND 0: steady state
-  // (group g+2 may still be in flight; issue g+3); 1: g+2 is the last group
-  // (nothing to issue); 2: g+1 is the last (nothing in flight); 3: the last
-  // group (no next group to prepare).  Every kind is straight-line code and
-  // the sched_barriers fix the order of its steps.  Each fragment is
-  // reloaded for the next group in the step that issues its last MFMA.
-  auto group = [&](int g, auto kind_tag) {
-    constexpr int KIND = decltype(kind_tag)::value;
-    constexpr bool NEXT = KIND != 3;
-    const uint8_t* nsp = lds + slot_of(g + 1);
+  // One code group at stream position q.  NEXT: the next position is the
+  // tile's next group, read progressively during this one (its wait,
+  // barrier and DMA issue sit in step 1, after the first fragment has been
+  // freed); otherwise this is the tile's last group.  The DMA it issues
+  // (position q + 3, code group g + 3) takes the body form while that is a
+  // code stage of this tile and the generic form otherwise.  The last group
+  // instead ends the tile's use of the ring at step 1 (every fragment of
+  // its stage is in registers once tile 2's MFMAs have issued: LDS reads
+  // return in order), moves the DMA window to the next tile and issues that
+  // tile's third and fourth positions, ahead of the output stores.
+  auto group = [&](int q, int g, auto next_tag, int k) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const uint8_t* nsp = slot_ptr(q + 1);
     step(1, 0, [] {});
-    // A tile row 0 is free after tile 2's MFMAs; the next slot must be ready
-    step(2, 1, [&] {
+    step(2, 1, [&] {  // A tile row 0 is free
       if constexpr (NEXT) {
-        if constexpr (KIND <= 1) wait_dma(OG1{});
-        if constexpr (KIND == 2) wait_dma(OG0{});
-        asm volatile("s_barrier" ::: "memory");
-        if constexpr (KIND == 0) dma(g + 3);
+        wait_stage();
+        barrier();
+        if (g + 3 < G) dma_code(q + 3);
+        else dma_stage(q + 3);
         load_a(nsp, 0);
+      } else if (k + 1 < my_tiles) {
+        barrier();
+        cur_base = (k + 1) * SPT;
+        cur_t = nxt_t;
+        if (k + 2 < my_tiles) nxt_t = tile_xy(tile_number(b, k + 2, nwg, ntiles), num_m, num_n);
+        dma_stage(q + 3);
+        dma_stage(q + 4);
       }
     });
     step(3, 2, [&] {  // B column 0 free
@@ -339,52 +351,110 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     step(NEXT ? 0 : -1, 5, [] {});  // first tile of the next group
   };
 
-  // ---- prologue: the first groups in flight.  Meanwhile the accumulators start
-  // from the bias and the low-rank term T L2 (its loads overlap the DMA
-  // latency), so nothing but the store is left after the main loop.  G is
-  // even (K % 128 == 0), so G >= 2.
-  const int64_t mbase = m0 + wm * 64;
-  const int nbase = n0 + wn * 96;
-  // The loads of T and L2 are issued after the DMAs, so waiting for them
-  // also waits for these DMAs (vmcnt counts in order).
-  dma(0);
-  dma(1);
-  if (G > 2) dma(2);
-  init_bias_tiles<2, 3>(acc, N, nbase, lane, bias);
-  if (T != nullptr) lowrank_up_tiles<2, 3>(acc, rank, M, N, mbase, nbase, lane, T, lora_up);
-  wait_dma(OG0{});
-  asm volatile("s_barrier" ::: "memory");
-  load_a(lds, 0);
-  load_a(lds, 1);
-  load_b(lds, 0);
-  load_b(lds, 1);
-  load_b(lds, 2);
-  mfma_tile(0);
+  // ---- pre-stage fragments: T hi/lo (A), L2 (B), the bias
+  const int pta = (wm * 2) * LR_XBLOCK + lane * 16;
+  const int plb = PRE_L2 + (wn * 3) * LR_WBLOCK + lane * 16;
+  const int pbias = PRE_BIAS + 2 * (wn * 3) * 32;
 
-  // G is even: either G >= 4 (the tail is kinds 1..3) or G == 2 (2, 3)
-  int g = 0;
-  for (; g + 3 < G; ++g) group(g, std::integral_constant<int, 0>{});
-  if (G >= 4) group(g++, std::integral_constant<int, 1>{});
-  group(g++, std::integral_constant<int, 2>{});
-  group(g, std::integral_constant<int, 3>{});
+  // ---- the stream.  Reading position t issues position t + 2, except at
+  // the first two positions of a tile: their two successors were issued at
+  // the end of the previous tile (or here), before its output stores.
+  dma_stage(0);
+  dma_stage(1);
+  dma_stage(2);
+  dma_stage(3);
+#pragma unroll
+  for (int i = 0; i < I4_NST; ++i) dma4(wimg, voff >> 2, lds_base + I4_NSLOT * SLOT_BYTES);
+  int q = 0;  // next stream position to read
+#pragma nounroll
+  for (int k = 0; k < my_tiles; ++k) {
+    // the body DMAs start at code group 3
+    xrun = ximg + ((int64_t)3 * x_rt + cur_t.tm * (I4_BM / 32)) * I4_BLOCK;
+    wrun = wimg + ((int64_t)3 * w_ct + cur_t.tn * (I4_BN / 32)) * I4_BLOCK;
+    // pre-stages: the bias, then the low-rank slices accumulate into acc
+#pragma nounroll
+    for (int jp = 0; jp < P; ++jp, ++q) {
+      wait_at(jp);
+      barrier();
+      if (jp >= 2) dma_stage(q + 2);
+      const uint8_t* sp = slot_ptr(q);
+      if (jp == 0) init_bias_t<2, 3>(acc, sp + pbias, lane);
+      if (jp < R16) {
+        v8bf thi[2], tlo[2], lb[3];
+#pragma unroll
+        for (int tr = 0; tr < 2; ++tr) {
+          thi[tr] = *reinterpret_cast<const v8bf*>(sp + pta + tr * LR_XBLOCK);
+          tlo[tr] = *reinterpret_cast<const v8bf*>(sp + pta + tr * LR_XBLOCK + 1024);
+        }
+#pragma unroll
+        for (int tc = 0; tc < 3; ++tc)
+          lb[tc] = *reinterpret_cast<const v8bf*>(sp + plb + tc * LR_WBLOCK);
+#pragma unroll
+        for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+          for (int tc = 0; tc < 3; ++tc) {
+            acc[tr][tc] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[tc], thi[tr], acc[tr][tc], 0, 0, 0);
+            acc[tr][tc] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[tc], tlo[tr], acc[tr][tc], 0, 0, 0);
+          }
+      }
+    }
+    // the first code group: all its fragments, then its first tile's MFMAs
+    wait_at(P);
+    barrier();
+    dma_stage(q + 2);
+    {
+      const uint8_t* sp = slot_ptr(q);
+      load_a(sp, 0);
+      load_a(sp, 1);
+      load_b(sp, 0);
+      load_b(sp, 1);
+      load_b(sp, 2);
+    }
+    mfma_p(0);
+    mfma_s(0);
+    // group g reads position P + g + 1 and issues P + g + 3 (code group g + 3)
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    const int64_t mbase = (int64_t)cur_t.tm * I4_BM + wm * 64;
+    const int nbase = cur_t.tn * I4_BN + wn * 96;
+    int g = 0;
+#pragma nounroll
+    for (; g + 1 < G; ++g, ++q) group(q, g, T_{}, k);
+    group(q, g, F_{}, k);
+    ++q;
 
-  store_tiles<2, 3, false>(acc, M, N, mbase, nbase, lane, nullptr, out_f32 != 0, Y);
+    store_tiles_t<2, 3>(acc, M, N, mbase, nbase, lane, out_f32 != 0, Y);
+    // an edge tile may issue fewer stores than the waits above count on
+    if (!(mbase + 64 <= M && nbase + 96 <= N)) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  // the DMAs past the end of the stream must land before LDS is released
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-hipError_t launch_int4_forward(int rank, bool out_f32, int64_t M, int N, int K,
-                               const uint8_t* xcodes, const float* xscales, const float* T,
-                               const void* wimage, const uint16_t* lora_up,
-                               const uint16_t* bias, void* Y, void* workspace, hipStream_t s) {
-  const int64_t Mp = pad_rows(M);
-  const int64_t Np = pad_cols(N);
-  uint8_t* ximg = reinterpret_cast<uint8_t*>(workspace);
-  hipError_t e = launch_image(true, M, Mp, K, xcodes, xscales, ximg, s);
-  if (e != hipSuccess) return e;
-  const int64_t tiles = (Mp / I4_BM) * (Np / I4_BN);
-  hipLaunchKernelGGL(int4_gemm_kernel, dim3((unsigned)tiles), dim3(I4_THREADS), 0, s, M, N, K,
-                     rank, (int)out_f32, ximg, (int)(Mp / 32),
-                     reinterpret_cast<const uint8_t*>(wimage), (int)(Np / 32), T, lora_up, bias,
-                     Y);
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cus[dev] > 0) return cus[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cus[dev] = n;
+  return n;
+}
+
+hipError_t launch_int4_forward(bool out_f32, int64_t M, int N, int K, int rank,
+                               const void* ximage, const void* wimage, void* Y, hipStream_t s) {
+  const ActImage a = act_image(0, M, K, rank);
+  const WeightImage w = weight_image(0, N, K, rank);
+  const int64_t tiles = (a.RT / (I4_BM / 32)) * (w.CT / (I4_BN / 32));
+  const int64_t grid = std::min<int64_t>(tiles, device_cus());
+  hipLaunchKernelGGL(int4_gemm_kernel, dim3((unsigned)grid), dim3(I4_THREADS), 0, s, M, N, K,
+                     rank, (int)out_f32, reinterpret_cast<const uint8_t*>(ximage), a.RT,
+                     (int64_t)a.lr, reinterpret_cast<const uint8_t*>(wimage), w.CT, (int64_t)w.lr,
+                     (int64_t)w.bias, Y);
   return hipGetLastError();
 }
 

@@ -23,7 +23,16 @@
 // 20000 fp32 b, subnormals and all-ones significands included).  The fp64
 // reciprocals of lambda are computed once per workgroup into LDS, the one of
 // s once per lane and group.
+//
+// Outputs: the codes, scales and T in the documented row-major layouts
+// (each optional) and/or the activation operand image the GEMM reads
+// (image.h): the same codes re-encoded in MFMA lane order (INT4 as 6-bit
+// E2M3 fields with the bf16-split scale operands, FP4 as stored with one
+// scale byte per lane) and T split into bf16 high and low parts.  With an
+// image the grid also covers the padding rows up to a multiple of 256, which
+// come out as zeros.
 #include "common.h"
+#include "image.h"
 #include "kernels.h"
 
 namespace svdq {
@@ -41,13 +50,41 @@ struct QaLds {
   static constexpr int kBytes = kRcp > kRed ? kRcp : kRed;
 };
 
+// 16 INT4 codes (nibbles 0..15, two's complement) -> 16 E2M3 fields of
+// 6 bits (sign-magnitude, value q/8) packed little-endian into 96 bits.
+__device__ __forceinline__ void fp6_fields16(const uint32_t (&c)[16], uint32_t& d0, uint32_t& d1,
+                                             uint32_t& d2) {
+  uint64_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint64_t f = c[i] < 8u ? c[i] : 0x30u - c[i];
+    const int b = 6 * i;
+    if (b < 64) {
+      lo |= f << b;
+      if (b > 58) hi |= f >> (64 - b);
+    } else {
+      hi |= f << (b - 64);
+    }
+  }
+  d0 = (uint32_t)lo;
+  d1 = (uint32_t)(lo >> 32);
+  d2 = (uint32_t)hi;
+}
+
+// Where a lane writes the activation image: null img = no image.
+struct QaImage {
+  uint8_t* img;
+  int64_t RT;
+  size_t scale, lr;
+};
+
 // MODE 0 = INT4, 1 = FP4.  RB = rank / 16 (0 = no down-projection).
 // CODES = false skips the quantizer (stand-alone down-projection).
 template <int MODE, int RB, bool CODES>
 __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
     int64_t M, int K, const uint16_t* __restrict__ X, const float* __restrict__ lambda,
     const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ xcodes,
-    void* __restrict__ xscales, float* __restrict__ T) {
+    void* __restrict__ xscales, float* __restrict__ T, QaImage qi) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<RB>::kBytes];
   double* rlam = reinterpret_cast<double*>(smem);
   const int lane = threadIdx.x & 63;
@@ -56,6 +93,8 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
   const int j = lane >> 4;
   const int64_t row = (int64_t)blockIdx.x * QA_ROWS + r16;
   const bool row_ok = row < M;
+  const int64_t irt = row >> 5;     // image row tile and lane slot of this row
+  const int irr = (int)(row & 31);
   const uint16_t* xrow = X + (row_ok ? row : 0) * (int64_t)K;
 
   v4f tacc[RB > 0 ? RB : 1];
@@ -105,25 +144,49 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
           amax = fmaxf(amax, __shfl_xor(amax, 16));
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           const float s = amax / 7.0f;
-          uint32_t w0 = 0, w1 = 0;
+          uint32_t c[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) c[i] = 0u;
           if (s != 0.f) {
             const double rs = 1.0 / (double)s;
-            uint32_t c[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               float q = __builtin_rintf((float)((double)xh[i] * rs));  // = rint(fp32(xh / s))
               q = fminf(fmaxf(q, -8.0f), 7.0f);
               c[i] = (uint32_t)(int)q & 0xFu;
             }
+          }
+          if (xcodes != nullptr && row_ok) {
+            uint32_t w0 = 0, w1 = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               w0 |= c[i] << (4 * i);
               w1 |= c[8 + i] << (4 * i);
             }
-          }
-          if (row_ok) {
             *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
             if (j == 0) reinterpret_cast<float*>(xscales)[row * (int64_t)(K >> 6) + (k0 >> 6)] = s;
+          }
+          if (qi.img != nullptr) {
+            // this lane's 16 fields are fields 0..15 (j even) or 16..31 (j odd)
+            // of K half j/2 of group k0/64
+            uint8_t* blk = qi.img + ((int64_t)(k0 >> 6) * qi.RT + irt) * I4_BLOCK;
+            uint8_t* half = blk + (j >> 1) * 768;
+            uint32_t d0, d1, d2;
+            fp6_fields16(c, d0, d1, d2);
+            if ((j & 1) == 0) {
+              *reinterpret_cast<v2u*>(half + 16 * irr) = v2u{d0, d1};
+              *reinterpret_cast<uint32_t*>(half + 16 * irr + 8) = d2;
+            } else {
+              *reinterpret_cast<uint32_t*>(half + 16 * irr + 12) = d0;
+              *reinterpret_cast<v2u*>(half + 512 + 8 * irr) = v2u{d1, d2};
+            }
+            // scale operand, X pattern: slot irr {hi | lo << 16, hi}, slot 32 + irr {lo, 0}
+            if (j < 2) {
+              const uint32_t hb = f32_to_bf16(s);
+              const uint32_t lb = f32_to_bf16(s - bf16_to_f32(hb));
+              const v2u so = j == 0 ? v2u{hb | (lb << 16), hb} : v2u{lb, 0u};
+              *reinterpret_cast<v2u*>(blk + 1536 + 8 * (32 * j + irr)) = so;
+            }
           }
         } else {
           // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
@@ -135,11 +198,18 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
           for (int i = 0; i < 8; ++i) w0 |= e2m1_code(xh[i] * sc) << (4 * i);
 #pragma unroll
           for (int i = 0; i < 8; ++i) w1 |= e2m1_code(xh[8 + i] * sc) << (4 * i);
-          if (row_ok) {
+          if (xcodes != nullptr && row_ok) {
             *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
             if ((j & 1) == 0)
               reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 5) + (k0 >> 5)] =
                   (uint8_t)(e + 127);
+          }
+          if (qi.img != nullptr) {
+            // lane slot 32 h + row of the (group, row tile) block, h = j/2
+            const int64_t b = (int64_t)(k0 >> 6) * qi.RT + irt;
+            const int slot = 32 * (j >> 1) + irr;
+            *reinterpret_cast<v2u*>(qi.img + b * F4_CBLOCK + 16 * slot + 8 * (j & 1)) = v2u{w0, w1};
+            if ((j & 1) == 0) qi.img[qi.scale + b * F4_SBLOCK + slot] = (uint8_t)(e + 127);
           }
         }
       }
@@ -175,17 +245,42 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) red[wave][b][q][lane] = tacc[b][q];
     __syncthreads();
+    // One thread per (row, 8 consecutive ranks): the 8 partial sums of a
+    // row and rank chunk are 8 consecutive lanes of one MFMA output register
+    // (lane l, element q -> row 4 (l/16) + q, column l%16).
     const int rank = RB * 16;
-    for (int idx = threadIdx.x; idx < RB * 4 * 64; idx += QA_THREADS) {
-      const int b = idx / 256;
-      const int q = (idx / 64) & 3;
-      const int l = idx & 63;
-      float v = red[0][b][q][l];
+    for (int idx = threadIdx.x; idx < QA_ROWS * (rank / 8); idx += QA_THREADS) {
+      const int mr = idx / (rank / 8);
+      const int c8 = idx - mr * (rank / 8);
+      const int b = c8 >> 1, q = mr & 3, l0 = 16 * (mr >> 2) + 8 * (c8 & 1);
+      float v[8];
 #pragma unroll
-      for (int w = 1; w < QA_WAVES; ++w) v += red[w][b][q][l];
-      // MFMA 16x16 output: lane l, element q -> row 4*(l/16)+q, column l%16.
-      const int64_t m = (int64_t)blockIdx.x * QA_ROWS + 4 * (l >> 4) + q;
-      if (m < M) T[m * rank + b * 16 + (l & 15)] = v;
+      for (int i = 0; i < 8; ++i) v[i] = red[0][b][q][l0 + i];
+#pragma unroll
+      for (int w = 1; w < QA_WAVES; ++w)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += red[w][b][q][l0 + i];
+      const int64_t m = (int64_t)blockIdx.x * QA_ROWS + mr;
+      if (T != nullptr && m < M) {
+        float* tp = T + m * rank + 8 * c8;
+        *reinterpret_cast<v4f*>(tp) = v4f{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<v4f*>(tp + 4) = v4f{v[4], v[5], v[6], v[7]};
+      }
+      if (qi.img != nullptr) {
+        // slice b, lane slot 32 (c8 & 1) + row: hi at 16 slot, lo at 1024 + 16 slot
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+          hi[i] = h0 | (h1 << 16);
+          lo[i] = f32_to_bf16(v[2 * i] - bf16_to_f32(h0)) |
+                  (f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1)) << 16);
+        }
+        uint8_t* blk = qi.img + qi.lr + ((int64_t)b * qi.RT + (m >> 5)) * LR_XBLOCK;
+        const int slot = 32 * (c8 & 1) + (int)(m & 31);
+        *reinterpret_cast<v4u*>(blk + 16 * slot) = v4u{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<v4u*>(blk + 1024 + 16 * slot) = v4u{lo[0], lo[1], lo[2], lo[3]};
+      }
     }
   }
 }
@@ -193,11 +288,11 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
 template <int MODE, bool CODES>
 static hipError_t launch_qa_rank(int rb, dim3 grid, hipStream_t s, int64_t M, int K,
                                  const uint16_t* X, const float* lam, const uint16_t* ld,
-                                 uint8_t* xc, void* xs, float* T) {
+                                 uint8_t* xc, void* xs, float* T, QaImage qi) {
 #define SVDQ_QA_CASE(R)                                                                   \
   case R:                                                                                 \
     hipLaunchKernelGGL((quantize_act_kernel<MODE, R, CODES>), grid, dim3(QA_THREADS), 0, \
-                       s, M, K, X, lam, ld, xc, xs, T);                                   \
+                       s, M, K, X, lam, ld, xc, xs, T, qi);                               \
     break;
   switch (rb) {
     SVDQ_QA_CASE(0) SVDQ_QA_CASE(1) SVDQ_QA_CASE(2) SVDQ_QA_CASE(3) SVDQ_QA_CASE(4)
@@ -211,14 +306,28 @@ static hipError_t launch_qa_rank(int rb, dim3 grid, hipStream_t s, int64_t M, in
   return hipGetLastError();
 }
 
+size_t act_image_bytes(int mode, int64_t M, int K, int rank) {
+  return act_image(mode, M, K, rank).bytes;
+}
+
 hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down,
-                               uint8_t* xcodes, void* xscales, float* T, hipStream_t s) {
-  const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
+                               uint8_t* xcodes, void* xscales, float* T, void* ximage,
+                               hipStream_t s) {
+  QaImage qi{nullptr, 0, 0, 0};
+  int64_t rows = M;
+  if (ximage != nullptr) {
+    const ActImage a = act_image(mode, M, K, rank);
+    qi = QaImage{reinterpret_cast<uint8_t*>(ximage), a.RT, a.scale, a.lr};
+    rows = a.RT * 32;  // cover the padding rows too
+  }
+  const dim3 grid((unsigned)((rows + QA_ROWS - 1) / QA_ROWS));
   const int rb = lora_down ? rank / 16 : 0;
   if (mode == 0)
-    return launch_qa_rank<0, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes, xscales, T);
-  return launch_qa_rank<1, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes, xscales, T);
+    return launch_qa_rank<0, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes, xscales, T,
+                                   qi);
+  return launch_qa_rank<1, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes, xscales, T,
+                                 qi);
 }
 
 hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
@@ -226,7 +335,7 @@ hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                hipStream_t s) {
   const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
   return launch_qa_rank<0, false>(rank / 16, grid, s, M, K, X, lambda, lora_down, nullptr,
-                                  nullptr, T);
+                                  nullptr, T, QaImage{nullptr, 0, 0, 0});
 }
 
 }  // namespace svdq

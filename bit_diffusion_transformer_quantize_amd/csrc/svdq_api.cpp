@@ -122,75 +122,67 @@ svdq_status svdq_pack_weight(const svdq_desc* d, const uint16_t* W, const float*
                                            lora_up, wcodes, wscales, (hipStream_t)stream));
 }
 
-svdq_status svdq_quantize_act(const svdq_desc* d, int64_t M, const uint16_t* X,
-                              const float* lambda, const uint16_t* lora_down, uint8_t* xcodes,
-                              void* xscales, float* T, void* stream) {
+svdq_status svdq_act_image_size(const svdq_desc* d, int64_t M, size_t* bytes) {
   SVDQ_TRY(check_desc(d));
   SVDQ_TRY(check_rows_k(M, d->K));
-  if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(xcodes) || !ptr_ok(xscales)) return SVDQ_ERR_ARG;
-  if (lora_down != nullptr) {
-    if (d->rank == 0 || !aligned16(lora_down) || !ptr_ok(T)) return SVDQ_ERR_ARG;
-  } else if (!opt_ok(T)) {
-    return SVDQ_ERR_ARG;
+  if (bytes == nullptr) return SVDQ_ERR_ARG;
+  *bytes = svdq::act_image_bytes(d->mode, M, d->K, d->rank);
+  return SVDQ_OK;
+}
+
+svdq_status svdq_quantize_act(const svdq_desc* d, int64_t M, const uint16_t* X,
+                              const float* lambda, const uint16_t* lora_down, uint8_t* xcodes,
+                              void* xscales, float* T, void* ximage, void* stream) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows_k(M, d->K));
+  if (!ptr_ok(X) || !ptr_ok(lambda)) return SVDQ_ERR_ARG;
+  if ((xcodes == nullptr) != (xscales == nullptr)) return SVDQ_ERR_ARG;
+  if (!opt_ok(xcodes) || !opt_ok(xscales) || !opt_ok(T) || !opt_ok(ximage)) return SVDQ_ERR_ARG;
+  if (xcodes == nullptr && T == nullptr && ximage == nullptr) return SVDQ_ERR_ARG;
+  if (d->rank == 0) {
+    if (lora_down != nullptr || T != nullptr) return SVDQ_ERR_ARG;
+  } else {
+    // the low-rank part of the image and T both come from lora_down
+    if ((T != nullptr || ximage != nullptr) && !ptr_ok(lora_down)) return SVDQ_ERR_ARG;
+    if (T == nullptr && ximage == nullptr && lora_down != nullptr) return SVDQ_ERR_ARG;
   }
   SVDQ_TRY(check_device());
   return from_hip(svdq::launch_quantize_act(d->mode, d->rank, M, d->K, X, lambda, lora_down,
-                                            xcodes, xscales, T, (hipStream_t)stream));
+                                            xcodes, xscales, T, ximage, (hipStream_t)stream));
 }
 
 svdq_status svdq_weight_image_size(const svdq_desc* d, size_t* bytes) {
   SVDQ_TRY(check_desc(d));
   if (bytes == nullptr) return SVDQ_ERR_ARG;
-  *bytes = d->mode == SVDQ_MODE_INT4 ? svdq::int4_weight_image_bytes(d->N, d->K)
-                                     : svdq::fp4_weight_image_bytes(d->N, d->K);
+  *bytes = svdq::weight_image_bytes(d->mode, d->N, d->K, d->rank);
   return SVDQ_OK;
 }
 
 svdq_status svdq_prepare_weight(const svdq_desc* d, const uint8_t* wcodes, const void* wscales,
-                                void* wimage, void* stream) {
+                                const uint16_t* lora_up, const uint16_t* bias, void* wimage,
+                                void* stream) {
   SVDQ_TRY(check_desc(d));
-  if (!ptr_ok(wcodes) || !ptr_ok(wscales) || !ptr_ok(wimage)) return SVDQ_ERR_ARG;
+  if (!ptr_ok(wcodes) || !ptr_ok(wscales) || !ptr_ok(wimage) || !opt_ok(bias)) return SVDQ_ERR_ARG;
+  if (d->rank > 0 ? !ptr_ok(lora_up) : lora_up != nullptr) return SVDQ_ERR_ARG;
   SVDQ_TRY(check_device());
-  if (d->mode == SVDQ_MODE_INT4)
-    return from_hip(svdq::launch_int4_prepare_weight(
-        d->N, d->K, wcodes, static_cast<const float*>(wscales), wimage, (hipStream_t)stream));
-  return from_hip(svdq::launch_fp4_prepare_weight(
-      d->N, d->K, wcodes, static_cast<const uint8_t*>(wscales), wimage, (hipStream_t)stream));
+  return from_hip(svdq::launch_prepare_weight(d->mode, d->N, d->K, d->rank, wcodes, wscales,
+                                              lora_up, bias, wimage, (hipStream_t)stream));
 }
 
-svdq_status svdq_linear_workspace_size(const svdq_desc* d, int64_t M, size_t* bytes) {
-  SVDQ_TRY(check_desc(d));
-  SVDQ_TRY(check_rows_k(M, d->K));
-  if (bytes == nullptr) return SVDQ_ERR_ARG;
-  *bytes = d->mode == SVDQ_MODE_INT4 ? svdq::int4_workspace_bytes(M, d->K)
-                                     : svdq::fp4_workspace_bytes(M, d->K);
-  return SVDQ_OK;
-}
-
-svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const uint8_t* xcodes,
-                                const void* xscales, const float* T, const void* wimage,
-                                const uint16_t* lora_up, const uint16_t* bias, void* Y,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const void* ximage,
+                                const void* wimage, void* Y, void* stream) {
   SVDQ_TRY(check_desc(d));
   SVDQ_TRY(check_rows_k(M, d->K));
   // outputs are limited to 2^46 elements (tile counts stay 32-bit)
   if (M > (int64_t(1) << 46) / d->N) return SVDQ_ERR_SHAPE;
-  if (!ptr_ok(xcodes) || !ptr_ok(xscales) || !ptr_ok(wimage) || !ptr_ok(Y)) return SVDQ_ERR_ARG;
-  if ((T == nullptr) != (lora_up == nullptr)) return SVDQ_ERR_ARG;
-  if (T != nullptr && (d->rank == 0 || !aligned16(T) || !aligned16(lora_up))) return SVDQ_ERR_ARG;
-  if (!opt_ok(bias)) return SVDQ_ERR_ARG;
+  if (!ptr_ok(ximage) || !ptr_ok(wimage) || !ptr_ok(Y)) return SVDQ_ERR_ARG;
   const bool f32 = (d->flags & SVDQ_FLAG_OUT_F32) != 0u;
-  const size_t need = d->mode == SVDQ_MODE_INT4 ? svdq::int4_workspace_bytes(M, d->K)
-                                                : svdq::fp4_workspace_bytes(M, d->K);
-  if (!ptr_ok(workspace) || workspace_bytes < need) return SVDQ_ERR_ARG;
   SVDQ_TRY(check_device());
   if (d->mode == SVDQ_MODE_INT4)
-    return from_hip(svdq::launch_int4_forward(d->rank, f32, M, d->N, d->K, xcodes,
-                                              static_cast<const float*>(xscales), T, wimage,
-                                              lora_up, bias, Y, workspace, (hipStream_t)stream));
-  return from_hip(svdq::launch_fp4_forward(d->rank, f32, M, d->N, d->K, xcodes,
-                                           static_cast<const uint8_t*>(xscales), T, wimage,
-                                           lora_up, bias, Y, workspace, (hipStream_t)stream));
+    return from_hip(svdq::launch_int4_forward(f32, M, d->N, d->K, d->rank, ximage, wimage, Y,
+                                              (hipStream_t)stream));
+  return from_hip(svdq::launch_fp4_forward(f32, M, d->N, d->K, d->rank, ximage, wimage, Y,
+                                           (hipStream_t)stream));
 }
 
 svdq_status svdq_lowrank_down(const svdq_desc* d, int64_t M, const uint16_t* X,

@@ -50,12 +50,11 @@ _SIGNATURES = {
     "svdq_version": (ctypes.c_char_p, []),
     "svdq_calibrate_lambda": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "svdq_pack_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "svdq_quantize_act": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_act_image_size": (ctypes.c_int, [_DESC, _i64, ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_weight_image_size": (ctypes.c_int, [_DESC, ctypes.POINTER(ctypes.c_size_t)]),
-    "svdq_prepare_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp]),
-    "svdq_linear_workspace_size": (ctypes.c_int, [_DESC, _i64, ctypes.POINTER(ctypes.c_size_t)]),
-    "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                           ctypes.c_size_t, _vp]),
+    "svdq_quantize_act": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_prepare_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
     "svdq_lowrank_down": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp]),
     "svdq_lowrank_up": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
 }
@@ -171,25 +170,11 @@ def svdq_pack_weight(d: SvdqDesc, W, lam, lora_down=None, lora_up=None, wcodes=N
     return wcodes, wscales
 
 
-def svdq_quantize_act(d: SvdqDesc, X, lam, lora_down=None, xcodes=None, xscales=None, T=None):
-    M = X.shape[0]
-    K, r = d.K, d.rank
-    _need(X, "X", torch.bfloat16, (M, K))
-    _need(lam, "lambda", torch.float32, (K,))
-    _need(lora_down, "lora_down", torch.bfloat16, (r, K), optional=True)
-    if xcodes is None:
-        xcodes = torch.empty(M, K // 2, dtype=torch.uint8, device=X.device)
-    if xscales is None:
-        xscales = torch.empty(M, scale_cols(d.mode, K), dtype=scale_dtype(d.mode), device=X.device)
-    if lora_down is not None and T is None:
-        T = torch.empty(M, r, dtype=torch.float32, device=X.device)
-    _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
-    _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)))
-    _need(T, "T", torch.float32, (M, r), optional=True)
-    _check("svdq_quantize_act",
-           load().svdq_quantize_act(ctypes.byref(d), M, _p(X), _p(lam), _p(lora_down),
-                                    _p(xcodes), _p(xscales), _p(T), _stream()))
-    return xcodes, xscales, T
+def svdq_act_image_size(d: SvdqDesc, M: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("svdq_act_image_size",
+           load().svdq_act_image_size(ctypes.byref(d), M, ctypes.byref(n)))
+    return n.value
 
 
 def svdq_weight_image_size(d: SvdqDesc) -> int:
@@ -198,52 +183,63 @@ def svdq_weight_image_size(d: SvdqDesc) -> int:
     return n.value
 
 
-def svdq_prepare_weight(d: SvdqDesc, wcodes, wscales, wimage=None):
-    """Prepared weight (opaque uint8 image) of packed codes and scales."""
-    N, K = d.N, d.K
+def svdq_quantize_act(d: SvdqDesc, X, lam, lora_down=None, xcodes=None, xscales=None, T=None,
+                      ximage=None, image=True, codes=False):
+    """Quantize X; returns (xcodes, xscales, T, ximage), each None when not written.
+
+    ``image`` asks for the activation image (allocated when ``ximage`` is
+    None), ``codes`` for the row-major codes and scales (allocated when
+    missing); buffers passed in are always written.  T is written when it is
+    passed in (it needs lora_down)."""
+    M = X.shape[0]
+    K, r = d.K, d.rank
+    _need(X, "X", torch.bfloat16, (M, K))
+    _need(lam, "lambda", torch.float32, (K,))
+    _need(lora_down, "lora_down", torch.bfloat16, (r, K), optional=True)
+    if codes and xcodes is None:
+        xcodes = torch.empty(M, K // 2, dtype=torch.uint8, device=X.device)
+    if codes and xscales is None:
+        xscales = torch.empty(M, scale_cols(d.mode, K), dtype=scale_dtype(d.mode), device=X.device)
+    if image and ximage is None:
+        ximage = torch.empty(svdq_act_image_size(d, M), dtype=torch.uint8, device=X.device)
+    _need(xcodes, "xcodes", torch.uint8, (M, K // 2), optional=True)
+    _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)), optional=True)
+    _need(T, "T", torch.float32, (M, r), optional=True)
+    if ximage is not None:
+        _need(ximage, "ximage", torch.uint8, (svdq_act_image_size(d, M),))
+    _check("svdq_quantize_act",
+           load().svdq_quantize_act(ctypes.byref(d), M, _p(X), _p(lam), _p(lora_down),
+                                    _p(xcodes), _p(xscales), _p(T), _p(ximage), _stream()))
+    return xcodes, xscales, T, ximage
+
+
+def svdq_prepare_weight(d: SvdqDesc, wcodes, wscales, lora_up=None, bias=None, wimage=None):
+    """Prepared weight (opaque uint8 image) of packed codes and scales, L2 and the bias."""
+    N, K, r = d.N, d.K, d.rank
     _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
     _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
+    _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=True)
+    _need(bias, "bias", torch.bfloat16, (N,), optional=True)
     nbytes = svdq_weight_image_size(d)
     if wimage is None:
         wimage = torch.empty(nbytes, dtype=torch.uint8, device=wcodes.device)
     _need(wimage, "wimage", torch.uint8, (nbytes,))
     _check("svdq_prepare_weight",
-           load().svdq_prepare_weight(ctypes.byref(d), _p(wcodes), _p(wscales), _p(wimage),
-                                      _stream()))
+           load().svdq_prepare_weight(ctypes.byref(d), _p(wcodes), _p(wscales), _p(lora_up),
+                                      _p(bias), _p(wimage), _stream()))
     return wimage
 
 
-def svdq_linear_workspace_size(d: SvdqDesc, M: int) -> int:
-    n = ctypes.c_size_t(0)
-    _check("svdq_linear_workspace_size",
-           load().svdq_linear_workspace_size(ctypes.byref(d), M, ctypes.byref(n)))
-    return n.value
-
-
-def svdq_linear_forward(d: SvdqDesc, xcodes, xscales, T, wimage, lora_up=None, bias=None,
-                        Y=None, workspace=None):
-    M = xcodes.shape[0]
-    K, N, r = d.K, d.N, d.rank
+def svdq_linear_forward(d: SvdqDesc, M: int, ximage, wimage, Y=None):
     out_dtype = torch.float32 if (d.flags & SVDQ_FLAG_OUT_F32) else torch.bfloat16
-    _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
-    _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)))
-    _need(T, "T", torch.float32, (M, r), optional=True)
+    _need(ximage, "ximage", torch.uint8, (svdq_act_image_size(d, M),))
     _need(wimage, "wimage", torch.uint8, (svdq_weight_image_size(d),))
-    _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=True)
-    _need(bias, "bias", torch.bfloat16, (N,), optional=True)
     if Y is None:
-        Y = torch.empty(M, N, dtype=out_dtype, device=xcodes.device)
-    _need(Y, "Y", out_dtype, (M, N))
-    need = svdq_linear_workspace_size(d, M)
-    ws_bytes = 0
-    if need:
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=xcodes.device)
-        ws_bytes = workspace.numel()
+        Y = torch.empty(M, d.N, dtype=out_dtype, device=ximage.device)
+    _need(Y, "Y", out_dtype, (M, d.N))
     _check("svdq_linear_forward",
-           load().svdq_linear_forward(ctypes.byref(d), M, _p(xcodes), _p(xscales), _p(T),
-                                      _p(wimage), _p(lora_up), _p(bias), _p(Y), _p(workspace),
-                                      ws_bytes, _stream()))
+           load().svdq_linear_forward(ctypes.byref(d), M, _p(ximage), _p(wimage), _p(Y),
+                                      _stream()))
     return Y
 
 

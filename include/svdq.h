@@ -119,70 +119,73 @@ svdq_status svdq_pack_weight(const svdq_desc* desc, const uint16_t* W, const flo
                              const uint16_t* lora_down, const uint16_t* lora_up,
                              uint8_t* wcodes, void* wscales, void* stream);
 
+/* Operand images.  The GEMM reads both sides of the layer as "images": the
+ * codes and scales re-laid in the lane order of the gfx950 matrix
+ * instructions, together with the low-rank factor (T on the activation
+ * side, L2 on the weight side) and, on the weight side, the bias, so that
+ * one kernel streams everything it needs with contiguous copies.  The
+ * layouts are internal to the library (they depend only on desc and M);
+ * callers allocate the sizes below and treat the contents as opaque.
+ *   INT4 code blocks: per (64-group, 32 rows) 2048 bytes: the codes as 6-bit
+ *        E2M3 fields (value q/8) and the bf16 hi/lo split of the scales.
+ *   FP4  code blocks: per (64-group, 32 rows) 1024 bytes of E2M1 codes and
+ *        64 bytes of E8M0 scales.
+ *   Low-rank blocks: per (16 ranks, 32 rows) T as bf16 hi + lo (2048 bytes);
+ *        per (16 ranks, 32 columns) L2 as bf16 (1024 bytes).
+ *   Bias: 64 bytes per 32 columns, then 1024 bytes of zero padding.
+ * Rows of the activation image are padded to a multiple of 256 and columns
+ * of the weight image to 192 (INT4) or 256 (FP4); padding is zero. */
+
+/* Bytes of the activation image for M rows.  Pure host function. */
+svdq_status svdq_act_image_size(const svdq_desc* desc, int64_t M, size_t* bytes);
+
+/* Bytes of the prepared weight of a layer.  Pure host function. */
+svdq_status svdq_weight_image_size(const svdq_desc* desc, size_t* bytes);
+
 /* Run-time activation side, one kernel (apatero.com page, section "O que e
  * Nunchaku ...": the down-projection of the low-rank branch is fused into
  * the quantization kernel and shares its activations).
  *   X_hat[m][k] = bf16_RNE(fp32(X[m][k] / lambda[k]));
- *   X_hat quantized row by row in desc->mode into xcodes [M][K/2], xscales;
- *   T[m][i] = sum_k X_hat[m][k] * L1[k][i]   (fp32 accumulation)
- * lora_down may be NULL (then T is not written and may be NULL); with
- * rank == 0 both must be NULL.  Codes and scales are bit-identical to the
- * definition; T is accurate to fp32 accumulation. */
+ *   X_hat quantized row by row in desc->mode (codes, scales);
+ *   T[m][i] = sum_k X_hat[m][k] * L1[k][i]   (fp32 accumulation).
+ * Outputs, each optional (NULL = not written), at least one present:
+ *   xcodes [M][K/2] and xscales (both or neither): the codes and scales in
+ *     the documented row-major layout;
+ *   T [M][r] float32: the down-projection (needs lora_down);
+ *   ximage: the activation image (svdq_act_image_size bytes) that
+ *     svdq_linear_forward reads; with rank > 0 it includes T, so lora_down
+ *     is then required.
+ * With rank == 0, lora_down and T must be NULL.  Codes and scales are
+ * bit-identical to the definition; T is accurate to fp32 accumulation. */
 svdq_status svdq_quantize_act(const svdq_desc* desc, int64_t M, const uint16_t* X,
-                              const float* lambda, const uint16_t* lora_down,
-                              uint8_t* xcodes, void* xscales, float* T, void* stream);
+                              const float* lambda, const uint16_t* lora_down, uint8_t* xcodes,
+                              void* xscales, float* T, void* ximage, void* stream);
 
-/* Bytes of the prepared weight of a layer (see svdq_prepare_weight).  Pure
- * host function. */
-svdq_status svdq_weight_image_size(const svdq_desc* desc, size_t* bytes);
-
-/* Offline re-layout of the packed weight (codes and scales as written by
- * svdq_pack_weight) into the operand layout the GEMM reads (like the
- * one-time weight packing into the matrix-core layout the apatero.com page
- * describes for the fused 4-bit kernel).  wimage: device buffer of
- * svdq_weight_image_size bytes, written completely.
- *   INT4: a group-major array of 2048-byte blocks, one per (64-group,
- *         32 rows of W), holding the codes as 6-bit E2M3 fields (value q/8)
- *         in MFMA lane order and the bf16 hi/lo split of the scales; rows
- *         are padded to a multiple of 192 with zeros.
- *   FP4 : a group-major array of 1024-byte code blocks, one per (64-group,
- *         32 rows of W), each lane's 16 bytes being the packed codes of one
- *         row and 32-block, followed by the 64-byte blocks of the E8M0
- *         scales in the same lane order; rows are padded to a multiple of
- *         256 with zeros.
- * The image depends only on (mode, N, K) and the codes and scales; it is
- * an opaque operand of svdq_linear_forward. */
+/* Offline: the prepared weight of a layer (the one-time packing of the
+ * weights into the kernel layout, as the apatero.com page describes for the
+ * fused 4-bit kernel) from the codes and scales of svdq_pack_weight, the
+ * low-rank factor lora_up (bf16 [N][r]; required when rank > 0, NULL when
+ * rank == 0) and the bias (bf16 [N], or NULL for none).  wimage: device
+ * buffer of svdq_weight_image_size bytes, written completely. */
 svdq_status svdq_prepare_weight(const svdq_desc* desc, const uint8_t* wcodes,
-                                const void* wscales, void* wimage, void* stream);
+                                const void* wscales, const uint16_t* lora_up,
+                                const uint16_t* bias, void* wimage, void* stream);
 
-/* Bytes of device workspace svdq_linear_forward needs for this shape: the
- * activation operand image, in the layout of the prepared weight, with rows
- * padded to Mp = M rounded up to 256: K * Mp bytes in INT4 mode and
- * K * Mp * 17 / 32 bytes in FP4 mode, rounded up to 256 bytes.  Pure host
- * function. */
-svdq_status svdq_linear_workspace_size(const svdq_desc* desc, int64_t M, size_t* bytes);
-
-/* The W4A4 GEMM with the up-projection and bias in its epilogue (axbrief.com
+/* The W4A4 GEMM with the up-projection and the bias fused (axbrief.com
  * page, section "The Mechanics ...": 4-bit weights and activations;
  * apatero.com page: the up-projection is fused into the 4-bit compute
- * kernel).
+ * kernel).  From the activation image of M rows and the prepared weight of
+ * the same desc:
  *   INT4: Y0[m][n] = sum_g sx[m][g] sw[n][g] sum_{k in g} qx[m][k] qw[n][k]
  *   FP4 : Y0[m][n] = sum_b 2^(ex[m][b] + ew[n][b]) sum_{k in b} fx[m][k] fw[n][k]
- *   Y = Y0 + T L2 + bias, written as bf16 (RNE) or float32 (SVDQ_FLAG_OUT_F32).
- * xcodes/xscales: the activation side as written by svdq_quantize_act;
- * wimage: the prepared weight (svdq_prepare_weight) of the same desc.
- * T and lora_up are both NULL or both set (NULL: no low-rank term); bias may
- * be NULL.  Y: [M][N].  Accuracy: the integer/E2M1 block sums are exact, the
- * rest is fp32 arithmetic (INT4: the product of the two group scales carries
- * a relative error below 2^-15).
- * workspace: device buffer of at least svdq_linear_workspace_size bytes
- * (16-byte aligned).  Its contents are
- * scratch, overwritten by the call; calls that may run concurrently need
- * separate workspaces. */
-svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const uint8_t* xcodes,
-                                const void* xscales, const float* T, const void* wimage,
-                                const uint16_t* lora_up, const uint16_t* bias, void* Y,
-                                void* workspace, size_t workspace_bytes, void* stream);
+ *   Y = Y0 + T L2 + bias (T L2 only when rank > 0), written [M][N] as bf16
+ *   (RNE) or float32 (SVDQ_FLAG_OUT_F32).
+ * Accuracy: the integer/E2M1 block sums are exact, the rest is fp32
+ * arithmetic (INT4: the product of the two group scales carries a relative
+ * error below 2^-15; T and L2 enter as bf16 hi/lo splits, within 2^-16).
+ * One kernel; no workspace. */
+svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const void* ximage,
+                                const void* wimage, void* Y, void* stream);
 
 /* Unfused low-rank branch, for comparison with the fused schedule (the
  * apatero.com page quotes the overhead of running the rank-32 branch as

@@ -44,10 +44,12 @@ def gpu_run(dev, X, W, b, lam, L1, L2, mode, rank, out_f32=False, use_lowrank=Tr
         ld = to_dev_bf16(L1.T, dev)
         lu = to_dev_bf16(L2.T, dev)
     wc, ws = S.svdq_pack_weight(d, Wd, lam_d, ld, lu)
-    xc, xs, T = S.svdq_quantize_act(d, Xd, lam_d, ld)
-    Y = S.svdq_linear_forward(d, xc, xs, T, S.svdq_prepare_weight(d, wc, ws), lu, bd)
+    T = None if ld is None else torch.empty(M, rank, dtype=torch.float32, device=dev)
+    xc, xs, T, ximg = S.svdq_quantize_act(d, Xd, lam_d, ld, T=T, codes=True)
+    wimg = S.svdq_prepare_weight(d, wc, ws, lu, bd)
+    Y = S.svdq_linear_forward(d, M, ximg, wimg)
     torch.cuda.synchronize()
-    return dict(lam=lam_d, wc=wc, ws=ws, xc=xc, xs=xs, T=T, Y=Y)
+    return dict(lam=lam_d, wc=wc, ws=ws, xc=xc, xs=xs, T=T, Y=Y, ximage=ximg, wimage=wimg)
 
 
 def np_(t):

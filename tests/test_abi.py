@@ -45,42 +45,67 @@ def test_arch_predicate_null():
     assert _lib().svdq_arch_supported(None) == 0
 
 
-def test_workspace_size_is_host_only():
+def _act_bytes(mode, M, K, rank):
+    """Activation image size from the documented blocks: rows padded to 256;
+    per (64-group, 32 rows) 2048 bytes (INT4) or 1024 + 64 bytes (FP4); per
+    (16 ranks, 32 rows) 2048 bytes of T."""
+    rt = -(-M // 256) * 8
+    per = 2048 if mode == 0 else 1024 + 64
+    return (K // 64) * rt * per + (rank // 16) * rt * 2048
+
+
+def _weight_bytes(mode, N, K, rank):
+    """Weight image size: columns padded to 192 (INT4) or 256 (FP4); code
+    blocks as above, 1024 bytes of L2 per (16 ranks, 32 columns), 64 bytes of
+    bias per 32 columns and a 1024-byte zero tail."""
+    ct = -(-N // (192 if mode == 0 else 256)) * (6 if mode == 0 else 8)
+    per = 2048 if mode == 0 else 1024 + 64
+    return (K // 64) * ct * per + (rank // 16) * ct * 1024 + ct * 64 + 1024
+
+
+@pytest.mark.parametrize("mode,M,K,rank", [(0, 300, 512, 16), (0, 256, 512, 0), (1, 256, 512, 16),
+                                           (1, 1, 128, 32), (0, 4096, 3072, 32),
+                                           (1, 4096, 3072, 32)])
+def test_act_image_size_is_host_only(mode, M, K, rank):
     n = ctypes.c_size_t(123)
-    # FP4: the activation image, 17/32 bytes per element, rows padded to 256
-    assert _lib().svdq_linear_workspace_size(_d(mode=1), 256, ctypes.byref(n)) == 0
-    assert n.value == 512 * 256 * 17 // 32
-    assert _lib().svdq_linear_workspace_size(_d(mode=0, K=512, N=256), 300, ctypes.byref(n)) == 0
-    # INT4: the activation operand image, K bytes per row, rows padded to 256
-    assert n.value == 512 * 512
-    assert _lib().svdq_linear_workspace_size(_d(), 256, None) == ARG
-    assert _lib().svdq_linear_workspace_size(_d(K=96), 256, ctypes.byref(n)) == SHAPE
+    assert _lib().svdq_act_image_size(_d(mode=mode, K=K, rank=rank), M, ctypes.byref(n)) == 0
+    assert n.value == _act_bytes(mode, M, K, rank)
 
 
-def test_weight_image_size_is_host_only():
+def test_act_image_size_validation():
     n = ctypes.c_size_t(0)
-    # INT4: K bytes per weight row, rows padded to a multiple of 192
-    assert _lib().svdq_weight_image_size(_d(mode=0, K=512, N=256), ctypes.byref(n)) == 0
-    assert n.value == 512 * 384
-    assert _lib().svdq_weight_image_size(_d(mode=0, K=3072, N=9216), ctypes.byref(n)) == 0
-    assert n.value == 3072 * 9216
-    # FP4: 1 KB of codes and 64 B of scales per (64-group, 32 rows), rows padded to 256
-    assert _lib().svdq_weight_image_size(_d(mode=1, K=512, N=256), ctypes.byref(n)) == 0
-    assert n.value == 8 * 8 * (1024 + 64)
-    assert _lib().svdq_weight_image_size(_d(mode=1, K=3072, N=21504), ctypes.byref(n)) == 0
-    assert n.value == 48 * 672 * (1024 + 64)
+    assert _lib().svdq_act_image_size(_d(), 256, None) == ARG
+    assert _lib().svdq_act_image_size(_d(K=96), 256, ctypes.byref(n)) == SHAPE
+    assert _lib().svdq_act_image_size(_d(), 0, ctypes.byref(n)) == SHAPE
+    assert _lib().svdq_act_image_size(None, 256, ctypes.byref(n)) == ARG
+
+
+@pytest.mark.parametrize("mode,N,K,rank", [(0, 256, 512, 16), (0, 9216, 3072, 32),
+                                           (1, 256, 512, 16), (1, 21504, 3072, 32),
+                                           (1, 128, 128, 0), (0, 128, 128, 256)])
+def test_weight_image_size_is_host_only(mode, N, K, rank):
+    n = ctypes.c_size_t(0)
+    assert _lib().svdq_weight_image_size(_d(mode=mode, K=K, N=N, rank=rank), ctypes.byref(n)) == 0
+    assert n.value == _weight_bytes(mode, N, K, rank)
+
+
+def test_weight_image_size_validation():
+    n = ctypes.c_size_t(0)
     assert _lib().svdq_weight_image_size(_d(), None) == ARG
     assert _lib().svdq_weight_image_size(_d(N=200), ctypes.byref(n)) == SHAPE
 
 
 def test_prepare_weight_validation():
     p = _lib().svdq_prepare_weight
-    assert p(None, A, A, A, None) == ARG
-    assert p(_d(mode=3), A, A, A, None) == ARG
-    assert p(_d(K=96), A, A, A, None) == SHAPE
-    assert p(_d(), None, A, A, None) == ARG
-    assert p(_d(), A, MIS, A, None) == ARG
-    assert p(_d(), A, A, None, None) == ARG
+    assert p(None, A, A, A, A, A, None) == ARG
+    assert p(_d(mode=3), A, A, A, A, A, None) == ARG
+    assert p(_d(K=96), A, A, A, A, A, None) == SHAPE
+    assert p(_d(), None, A, A, A, A, None) == ARG               # codes null
+    assert p(_d(), A, MIS, A, A, A, None) == ARG                # scales misaligned
+    assert p(_d(), A, A, None, A, A, None) == ARG               # rank > 0 needs lora_up
+    assert p(_d(rank=0), A, A, A, A, A, None) == ARG            # rank 0 forbids it
+    assert p(_d(), A, A, A, MIS, A, None) == ARG                # bias misaligned
+    assert p(_d(), A, A, A, A, None, None) == ARG               # image null
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -92,39 +117,45 @@ def test_prepare_weight_validation():
 def test_desc_validation(kw, status):
     lib = _lib()
     d = _d(**kw)
-    assert lib.svdq_quantize_act(d, 256, A, A, A, A, A, A, None) == status
+    assert lib.svdq_quantize_act(d, 256, A, A, A, A, A, A, A, None) == status
     assert lib.svdq_pack_weight(d, A, A, A, A, A, A, None) == status
-    assert lib.svdq_linear_forward(d, 256, A, A, A, A, A, A, A, None, 0, None) == status
+    assert lib.svdq_prepare_weight(d, A, A, A, A, A, None) == status
+    assert lib.svdq_linear_forward(d, 256, A, A, A, None) == status
     assert lib.svdq_lowrank_down(d, 256, A, A, A, A, None) == status
     assert lib.svdq_lowrank_up(d, 256, A, A, A, None) == status
 
 
 def test_null_desc():
     lib = _lib()
-    assert lib.svdq_quantize_act(None, 256, A, A, A, A, A, A, None) == ARG
-    assert lib.svdq_linear_forward(None, 256, A, A, A, A, A, A, A, None, 0, None) == ARG
+    assert lib.svdq_quantize_act(None, 256, A, A, A, A, A, A, A, None) == ARG
+    assert lib.svdq_linear_forward(None, 256, A, A, A, None) == ARG
 
 
 @pytest.mark.parametrize("M", [0, -1, 1 << 40])
 def test_rows_validation(M):
     lib = _lib()
-    assert lib.svdq_quantize_act(_d(), M, A, A, A, A, A, A, None) == SHAPE
-    assert lib.svdq_linear_forward(_d(), M, A, A, A, A, A, A, A, None, 0, None) == SHAPE
+    assert lib.svdq_quantize_act(_d(), M, A, A, A, A, A, A, A, None) == SHAPE
+    assert lib.svdq_linear_forward(_d(), M, A, A, A, None) == SHAPE
     assert lib.svdq_calibrate_lambda(M, 512, 512, A, A, A, None) == SHAPE
 
 
 def test_quantize_act_pointer_validation():
     lib = _lib()
     q = lib.svdq_quantize_act
-    assert q(_d(), 256, None, A, A, A, A, A, None) == ARG        # X null
-    assert q(_d(), 256, MIS, A, A, A, A, A, None) == ARG         # X misaligned
-    assert q(_d(), 256, A, None, A, A, A, A, None) == ARG        # lambda null
-    assert q(_d(), 256, A, A, A, None, A, A, None) == ARG        # codes null
-    assert q(_d(), 256, A, A, A, A, None, A, None) == ARG        # scales null
-    assert q(_d(), 256, A, A, A, A, A, None, None) == ARG        # lora_down without T
-    assert q(_d(), 256, A, A, MIS, A, A, A, None) == ARG         # lora_down misaligned
-    assert q(_d(rank=0), 256, A, A, A, A, A, A, None) == ARG     # lora_down with rank 0
-    assert q(_d(), 256, A, A, None, A, A, MIS, None) == ARG      # optional T misaligned
+    assert q(_d(), 256, None, A, A, A, A, A, A, None) == ARG        # X null
+    assert q(_d(), 256, MIS, A, A, A, A, A, A, None) == ARG         # X misaligned
+    assert q(_d(), 256, A, None, A, A, A, A, A, None) == ARG        # lambda null
+    assert q(_d(), 256, A, A, A, None, A, A, A, None) == ARG        # codes without scales
+    assert q(_d(), 256, A, A, A, A, None, A, A, None) == ARG        # scales without codes
+    assert q(_d(), 256, A, A, None, A, A, A, None, None) == ARG     # T needs lora_down
+    assert q(_d(), 256, A, A, None, A, A, None, A, None) == ARG     # image needs lora_down
+    assert q(_d(), 256, A, A, A, A, A, None, None, None) == ARG     # lora_down unused
+    assert q(_d(), 256, A, A, MIS, A, A, A, A, None) == ARG         # lora_down misaligned
+    assert q(_d(rank=0), 256, A, A, A, A, A, None, A, None) == ARG  # lora_down with rank 0
+    assert q(_d(rank=0), 256, A, A, None, A, A, A, A, None) == ARG  # T with rank 0
+    assert q(_d(), 256, A, A, A, A, A, MIS, A, None) == ARG         # T misaligned
+    assert q(_d(), 256, A, A, A, A, A, A, MIS, None) == ARG         # image misaligned
+    assert q(_d(), 256, A, A, A, None, None, None, None, None) == ARG   # no output
 
 
 def test_pack_weight_pointer_validation():
@@ -141,19 +172,14 @@ def test_pack_weight_pointer_validation():
 def test_linear_forward_pointer_validation():
     lib = _lib()
     f = lib.svdq_linear_forward
-    assert f(_d(), 256, None, A, A, A, A, A, A, None, 0, None) == ARG   # codes null
-    assert f(_d(), 256, A, A, A, None, A, A, A, None, 0, None) == ARG   # weight image null
-    assert f(_d(), 256, A, A, A, MIS, A, A, A, None, 0, None) == ARG    # misaligned
-    assert f(_d(), 256, A, A, A, A, None, A, A, None, 0, None) == ARG   # T without lora_up
-    assert f(_d(), 256, A, A, None, A, A, A, A, None, 0, None) == ARG   # lora_up without T
-    assert f(_d(rank=0), 256, A, A, A, A, A, A, A, None, 0, None) == ARG
-    assert f(_d(), 256, A, A, A, A, A, MIS, A, None, 0, None) == ARG    # bias misaligned
-    assert f(_d(), 256, A, A, A, A, A, A, None, None, 0, None) == ARG   # Y null
-    assert f(_d(), 256, A, A, A, A, A, A, A, None, 1 << 30, None) == ARG  # INT4: no workspace
-    assert f(_d(), 256, A, A, A, A, A, A, A, MIS, 1 << 30, None) == ARG   # misaligned
-    assert f(_d(), 256, A, A, A, A, A, A, A, A, 1024, None) == ARG        # too small
+    assert f(_d(), 256, None, A, A, None) == ARG    # activation image null
+    assert f(_d(), 256, MIS, A, A, None) == ARG     # misaligned
+    assert f(_d(), 256, A, None, A, None) == ARG    # weight image null
+    assert f(_d(), 256, A, MIS, A, None) == ARG
+    assert f(_d(), 256, A, A, None, None) == ARG    # Y null
+    assert f(_d(), 256, A, A, MIS, None) == ARG
     # output larger than 2^46 elements
-    assert f(_d(N=1 << 20), 1 << 27, A, A, A, A, A, A, A, A, 1 << 40, None) == SHAPE
+    assert f(_d(N=1 << 20), 1 << 27, A, A, A, None) == SHAPE
 
 
 def test_lowrank_pieces_validation():
@@ -180,7 +206,7 @@ def _has_gpu():
                     "valid-looking fake pointers would be launched on")
 def test_no_device_is_a_hip_error():
     lib = _lib()
-    assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, None) == HIP
-    assert lib.svdq_linear_forward(_d(), 256, A, A, A, A, A, A, A, A, 1 << 30, None) == HIP
-    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, A, A, A, A, A, 1 << 30, None) == HIP
-    assert lib.svdq_prepare_weight(_d(), A, A, A, None) == HIP
+    assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, A, None) == HIP
+    assert lib.svdq_linear_forward(_d(), 256, A, A, A, None) == HIP
+    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, None) == HIP
+    assert lib.svdq_prepare_weight(_d(), A, A, A, None, A, None) == HIP

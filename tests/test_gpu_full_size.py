@@ -37,8 +37,9 @@ def _run_full(spec, X, W, b, mode, weight_rows, y_rows, y_cols, rank=None):
     lamd = S.svdq_calibrate_lambda(Xd, Wd)
     ld, lu = to_dev_bf16(L1.T, DEV), to_dev_bf16(L2.T, DEV)
     wc, ws = S.svdq_pack_weight(d, Wd, lamd, ld, lu)
-    xc, xs, T = S.svdq_quantize_act(d, Xd, lamd, ld)
-    Y = S.svdq_linear_forward(d, xc, xs, T, S.svdq_prepare_weight(d, wc, ws), lu, bd)
+    T = torch.empty(M, rank, dtype=torch.float32, device=DEV)
+    xc, xs, T, ximg = S.svdq_quantize_act(d, Xd, lamd, ld, T=T, codes=True)
+    Y = S.svdq_linear_forward(d, M, ximg, S.svdq_prepare_weight(d, wc, ws, lu, bd))
     torch.cuda.synchronize()
 
     assert np.array_equal(np_(lamd), lam), "lambda"

@@ -130,8 +130,10 @@ def test_edge_values(mode):
 
 @pytest.mark.parametrize("mode", ["int4", "fp4"])
 def test_determinism_and_guard_bands(mode):
-    """Two runs give bitwise-identical outputs, and nothing is written past the
-    end of any output (canary bytes after each buffer stay intact)."""
+    """Two runs give bitwise-identical outputs, every byte of both operand
+    images is written (the two runs pre-fill the buffers with different
+    bytes), and nothing is written past the end of any output (canary bytes
+    after each buffer stay intact)."""
     from bit_diffusion_transformer_quantize_amd import svdq as S
     spec = WL.TINY
     M = 131
@@ -148,40 +150,40 @@ def test_determinism_and_guard_bands(mode):
     sc = S.scale_cols(mode, K)
     PAD = 4096
 
-    def guarded(n, dtype):
-        buf = torch.full((n + PAD,), 0x5A if dtype == torch.uint8 else 0, dtype=dtype, device=DEV)
-        if dtype != torch.uint8:
-            buf.view(torch.uint8)[:] = 0x5A
+    def guarded(n, dtype, fill):
+        buf = torch.empty((n * torch.tensor([], dtype=dtype).element_size() + PAD * 4,),
+                          dtype=torch.uint8, device=DEV)
+        buf.fill_(fill)
         return buf
 
     outs = []
-    for _ in range(2):
-        wc_b, ws_b = guarded(N * K // 2, torch.uint8), guarded(N * sc, sdt)
-        xc_b, xs_b = guarded(M * K // 2, torch.uint8), guarded(M * sc, sdt)
-        T_b, Y_b = guarded(M * r, torch.float32), guarded(M * N, torch.bfloat16)
-        wc, ws = S.svdq_pack_weight(d, Wd, lamd, ld, lu, wc_b[:N * K // 2].view(N, K // 2),
-                                    ws_b[:N * sc].view(N, sc))
-        xc, xs, T = S.svdq_quantize_act(d, Xd, lamd, ld, xc_b[:M * K // 2].view(M, K // 2),
-                                        xs_b[:M * sc].view(M, sc), T_b[:M * r].view(M, r))
-        nimg, nws = S.svdq_weight_image_size(d), S.svdq_linear_workspace_size(d, M)
-        wi_b, wk_b = guarded(nimg, torch.uint8), guarded(max(nws, 16), torch.uint8)
-        wimg = S.svdq_prepare_weight(d, wc, ws, wi_b[:nimg])
-        Y = S.svdq_linear_forward(d, xc, xs, T, wimg, lu, bd, Y_b[:M * N].view(M, N),
-                                  wk_b[:nws] if nws else None)
+    for fill in (0x5A, 0xA5):
+        nimx, nimw = S.svdq_act_image_size(d, M), S.svdq_weight_image_size(d)
+        sizes = dict(wc=N * K // 2, ws=N * sc * (4 if mode == "int4" else 1), xc=M * K // 2,
+                     xs=M * sc * (4 if mode == "int4" else 1), T=M * r * 4, Y=M * N * 2,
+                     xi=nimx, wi=nimw)
+        bufs = {k: guarded(n, torch.uint8, fill) for k, n in sizes.items()}
+        v = {k: bufs[k][:n] for k, n in sizes.items()}
+        wc, ws = S.svdq_pack_weight(d, Wd, lamd, ld, lu, v["wc"].view(N, K // 2),
+                                    v["ws"].view(sdt).view(N, sc))
+        xc, xs, T, ximg = S.svdq_quantize_act(d, Xd, lamd, ld, v["xc"].view(M, K // 2),
+                                              v["xs"].view(sdt).view(M, sc),
+                                              v["T"].view(torch.float32).view(M, r), v["xi"])
+        wimg = S.svdq_prepare_weight(d, wc, ws, lu, bd, v["wi"])
+        Y = S.svdq_linear_forward(d, M, ximg, wimg, v["Y"].view(torch.bfloat16).view(M, N))
         torch.cuda.synchronize()
-        for buf, n in ((wc_b, N * K // 2), (ws_b, N * sc), (xc_b, M * K // 2), (xs_b, M * sc),
-                       (T_b, M * r), (Y_b, M * N), (wi_b, nimg), (wk_b, max(nws, 16))):
-            tail = buf[n:].view(torch.uint8).cpu().numpy()
-            assert np.all(tail == 0x5A), "write past the end of an output"
-        outs.append([np_(t.view(torch.uint8)) for t in (wc, ws, xc, xs, T, Y, wimg)])
-    for a, bb in zip(*outs):
-        assert np.array_equal(a, bb), "non-deterministic output"
+        for k, n in sizes.items():
+            tail = bufs[k][n:].cpu().numpy()
+            assert np.all(tail == fill), f"write past the end of {k}"
+        outs.append([np_(t.view(torch.uint8)) for t in (wc, ws, xc, xs, T, Y, ximg, wimg)])
+    for name, a, bb in zip(("wc", "ws", "xc", "xs", "T", "Y", "ximage", "wimage"), *outs):
+        assert np.array_equal(a, bb), f"{name}: non-deterministic or partly unwritten"
 
 
 @pytest.mark.parametrize("mode", ["int4", "fp4"])
 def test_unfused_schedule(mode):
-    """quantize (no T) + stand-alone down-projection + GEMM (no low-rank) +
-    stand-alone up-projection gives the same layer output."""
+    """quantize (no T) + stand-alone down-projection + GEMM (rank 0: no
+    low-rank term) + stand-alone up-projection gives the same layer output."""
     from bit_diffusion_transformer_quantize_amd import svdq as S
     spec = WL.TINY
     X, W, b = WL.draw(spec, seed=9, M=200)
@@ -192,15 +194,38 @@ def test_unfused_schedule(mode):
     K, N, r = spec.K, spec.N, spec.rank
     _say("unfused schedule", mode)
     d = S.desc(mode, K, N, r, out_f32=True)
+    d0 = S.desc(mode, K, N, 0, out_f32=True)
     Xd, Wd, bd = X.to(DEV), W.to(DEV), b.to(DEV)
     lamd = torch.from_numpy(lam).to(DEV)
     ld, lu = to_dev_bf16(L1.T, DEV), to_dev_bf16(L2.T, DEV)
     wc, ws = S.svdq_pack_weight(d, Wd, lamd, ld, lu)
-    xc, xs, _ = S.svdq_quantize_act(d, Xd, lamd, None)
+    xc, xs, _, ximg = S.svdq_quantize_act(d0, Xd, lamd, None, codes=True)
     T = S.svdq_lowrank_down(d, Xd, lamd, ld)
-    Y = S.svdq_linear_forward(d, xc, xs, None, S.svdq_prepare_weight(d, wc, ws), None, bd)
+    Y = S.svdq_linear_forward(d0, 200, ximg, S.svdq_prepare_weight(d0, wc, ws, None, bd))
     S.svdq_lowrank_up(d, T, lu, Y)
     torch.cuda.synchronize()
     assert np.array_equal(np_(xc), xc_o) and np.array_equal(np_(xs), xs_o)
     assert_T(np_(T), T_o, Xh, L1, "T (stand-alone)")
     assert_y(np_(Y), Y_o, True, "unfused")
+
+
+@pytest.mark.parametrize("mode", ["int4", "fp4"])
+def test_image_only_quantize(mode):
+    """The activation image written without the row-major codes and T (the
+    production call) gives the same layer output as the one written with
+    them."""
+    from bit_diffusion_transformer_quantize_amd import svdq as S
+    spec = WL.TINY
+    M = 77
+    X, W, b = WL.draw(spec, seed=13, M=M)
+    xb, wb = WL.bits(X), WL.bits(W)
+    lam, L1, L2, _, _ = oracle_offline(xb, wb, spec.rank, mode)
+    _say("image-only quantize", mode)
+    g = gpu_run(DEV, X, W, b, lam, L1, L2, mode, spec.rank)
+    d = S.desc(mode, spec.K, spec.N, spec.rank)
+    lamd = torch.from_numpy(lam).to(DEV)
+    _, _, _, ximg = S.svdq_quantize_act(d, X.to(DEV), lamd, to_dev_bf16(L1.T, DEV))
+    Y = S.svdq_linear_forward(d, M, ximg, g["wimage"])
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(ximg), np_(g["ximage"]))
+    assert np.array_equal(np_(Y.view(torch.int16)), np_(g["Y"].view(torch.int16)))
