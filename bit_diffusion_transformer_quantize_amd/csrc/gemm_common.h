@@ -139,6 +139,24 @@ static_assert(vmcnt_imm(4) == 0x0F74 && vmcnt_imm(24) == 0x4F78, "vmcnt encoding
 // is entirely inside or outside).  bf16: the quads of the two lane halves
 // are exchanged with v_permlane32_swap so that every lane holds and stores 8
 // consecutive columns (16 bytes); fp32: every quad is one 16-byte store.
+// The two 16-byte bf16 quads a lane stores for one transposed 32x32 tile:
+// o[qp] holds columns 16 qp + 8 (lane/32) .. +7 of row lane%32 (RNE).
+__device__ __forceinline__ void tile_quads_bf16(const v16f& a, v4u (&o)[2]) {
+  uint32_t pk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const v2f x = {a[2 * j], a[2 * j + 1]};
+    pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
+  }
+#pragma unroll
+  for (int qp = 0; qp < 2; ++qp) {
+    // quads 2 qp (dwords 4 qp, +1) and 2 qp + 1 (dwords 4 qp + 2, +3)
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * qp], pk[4 * qp + 2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * qp + 1], pk[4 * qp + 3], false, false);
+    o[qp] = v4u{s0[0], s1[0], s0[1], s1[1]};
+  }
+}
+
 template <int TR, int TC, bool FULL>
 __device__ __forceinline__ void store_tiles_t_as(const v16f (&acc)[TR][TC], int64_t M, int N,
                                                  int64_t mbase, int nbase, int lane, bool out_f32,
@@ -164,20 +182,12 @@ __device__ __forceinline__ void store_tiles_t_as(const v16f (&acc)[TR][TC], int6
         }
       } else {
         uint16_t* yr = reinterpret_cast<uint16_t*>(Y) + m * N + n0;
-        uint32_t pk[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const v2f x = {acc[tr][tc][2 * j], acc[tr][tc][2 * j + 1]};
-          pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
-        }
+        v4u o[2];
+        tile_quads_bf16(acc[tr][tc], o);
 #pragma unroll
         for (int qp = 0; qp < 2; ++qp) {
-          // quads 2 qp (dwords 4 qp, +1) and 2 qp + 1 (dwords 4 qp + 2, +3)
-          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * qp], pk[4 * qp + 2], false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * qp + 1], pk[4 * qp + 3], false, false);
           const int c = 16 * qp + 8 * h;
-          if (FULL || (mok && n0 + c < N))
-            *reinterpret_cast<v4u*>(yr + c) = v4u{s0[0], s1[0], s0[1], s1[1]};
+          if (FULL || (mok && n0 + c < N)) *reinterpret_cast<v4u*>(yr + c) = o[qp];
         }
       }
     }

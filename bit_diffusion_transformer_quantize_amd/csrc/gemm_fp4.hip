@@ -127,10 +127,10 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   const int S = K >> 7;       // code stages per tile (G/2; K % 128 == 0)
   const int R16 = rank >> 4;
   // pre-stages per tile: the bias rides in the first, one 16-rank slice of
-  // the low-rank branch in each of the first R16; at least four, so that
-  // the first four positions of every tile (whose waits differ) are all
-  // pre-stages and every code stage waits the same way
-  const int P = R16 > 4 ? R16 : 4;
+  // the low-rank branch in each of the first R16; at least two, so that the
+  // first two code stages of a tile are among the positions issued ahead
+  // of the previous tile's stores
+  const int P = R16 > 2 ? R16 : 2;
   const int SPT = P + S;
   const int total = my_tiles * SPT;
 
@@ -214,12 +214,15 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   // first four stages (j = 0..3) up to three younger stages plus the
   // F4_NST output stores of the previous tile behind them (before the first
   // tile, F4_NST dummy DMAs into the pad stand in for them).
+  // With P == 2 the first code stage (j = 2) waits until only the stores
+  // may be outstanding, which covers position 3 too: the next stage's read
+  // point then needs no wait.
   auto wait_stage = [] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); };
-  auto wait_head2 = [] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 + F4_NST)); };  // j = 2, 3
   auto wait_at = [&](int j) {
     if (j == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15 + F4_NST));
     else if (j == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10 + F4_NST));
-    else if (j < 4) wait_head2();
+    else if (j == 2 && P == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(F4_NST));
+    else if (j < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 + F4_NST));
     else wait_stage();
   };
   auto barrier = [] { asm volatile("s_barrier" ::: "memory"); };
@@ -281,14 +284,14 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   // slot, group 2s+1 (f1) the second; with NEXT the next stage's wait,
   // barrier and DMA issue sit between them (GEN: the DMA issued, position
   // q + 3, is not a code stage of this tile and takes the generic form)
-  auto code_stage = [&](int q, auto next_tag, auto gen_tag) {
+  auto code_stage = [&](int q, int s, auto next_tag, auto gen_tag) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr bool GEN = decltype(gen_tag)::value;
     load_frags(f1, q, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(f0);
     if constexpr (NEXT) {
-      wait_stage();
+      if (P + s + 1 >= 4) wait_stage();  // else covered by the first code stage's wait
       barrier();
       if constexpr (GEN) dma_stage(q + 3);
       else dma_code(q + 3);
@@ -344,12 +347,12 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
     using T_ = std::true_type;
     using F_ = std::false_type;
 #pragma nounroll
-    for (int s = 0; s + 3 < S; ++s, ++q) code_stage(q, T_{}, F_{});
+    for (int s = 0; s + 3 < S; ++s, ++q) code_stage(q, s, T_{}, F_{});
     // the last two stages with a successor issue beyond the tile's code
     // stages (S == 2: one, S == 1: none)
-    if (S > 2) code_stage(q++, T_{}, T_{});
-    if (S > 1) code_stage(q++, T_{}, T_{});
-    code_stage(q, F_{}, F_{});
+    if (S > 2) code_stage(q++, S - 3, T_{}, T_{});
+    if (S > 1) code_stage(q++, S - 2, T_{}, T_{});
+    code_stage(q, S - 1, F_{}, F_{});
     ++q;
 
     const int64_t mbase = (int64_t)cur_t.tm * F4_BM + wm * 64;
