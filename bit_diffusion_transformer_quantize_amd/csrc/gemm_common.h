@@ -12,8 +12,6 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // Eight fp32 values -> their bf16 high parts and bf16 low parts (of the
 // fp32 remainder), both RNE (v_cvt_pk_bf16_f32): hi + lo is within 2^-16

@@ -16,6 +16,9 @@
 //   both  low-rank blocks (rank r > 0) [r/16][RT][2048]: per 16-rank slice,
 //         64 lanes x 8 bf16 of hi(T) at 16 l, then 64 lanes x 8 bf16 of
 //         lo(T) at 1024 + 16 l (lane l: row l%32, ranks 8 (l/32) .. +7).
+//         partial sums (r > 0 and S > 1) [S][RT*32][r] fp32: the writing
+//         pass splits K into S ranges of whole 64-groups (act_splits) and
+//         a second pass adds the S partial T rows in order.
 //
 // Weight image (columns padded to the GEMM's tile width, padding zero):
 //   INT4  code blocks [G][CT][2048] as above with the W scale pattern
@@ -46,11 +49,25 @@ constexpr int BIAS_TAIL = 1024;          // zero padding after the bias blocks
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// K ranges of the pass that writes the activation image: enough (16 rows,
+// K range) work items to fill the GPU (about 1024), each range at least 48
+// whole 64-groups (so that every wave of a workgroup has several), at most
+// 16 ranges.
+__host__ __device__ inline int act_splits(int64_t M, int K) {
+  const int64_t blocks = round_up(M, IMG_ROWS_PAD) / 16;
+  int64_t s = (1024 + blocks - 1) / blocks;
+  const int64_t by_k = (K / 64) / 48;
+  s = s > by_k ? by_k : s;
+  return (int)(s < 1 ? 1 : (s > 16 ? 16 : s));
+}
+
 struct ActImage {
   int64_t RT;              // 32-row tiles (padded rows / 32)
+  int S;                   // K ranges of the writing pass
   size_t code;             // offset of the code blocks (0)
   size_t scale;            // FP4: offset of the scale blocks
   size_t lr;               // offset of the low-rank blocks
+  size_t tpart;            // offset of the partial T sums (r > 0 and S > 1)
   size_t bytes;            // total size
 };
 
@@ -58,6 +75,7 @@ __host__ __device__ inline ActImage act_image(int mode, int64_t M, int K, int ra
   ActImage a;
   const int64_t G = K / 64;
   a.RT = round_up(M, IMG_ROWS_PAD) / 32;
+  a.S = act_splits(M, K);
   a.code = 0;
   if (mode == 0) {
     a.scale = 0;
@@ -66,7 +84,8 @@ __host__ __device__ inline ActImage act_image(int mode, int64_t M, int K, int ra
     a.scale = (size_t)(G * a.RT * F4_CBLOCK);
     a.lr = a.scale + (size_t)(G * a.RT * F4_SBLOCK);
   }
-  a.bytes = a.lr + (size_t)(rank / 16) * (size_t)a.RT * LR_XBLOCK;
+  a.tpart = a.lr + (size_t)(rank / 16) * (size_t)a.RT * LR_XBLOCK;
+  a.bytes = a.tpart + (rank > 0 && a.S > 1 ? (size_t)a.S * (size_t)a.RT * 32 * rank * 4 : 0);
   return a;
 }
 

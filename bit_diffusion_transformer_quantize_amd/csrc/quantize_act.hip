@@ -38,15 +38,22 @@
 namespace svdq {
 
 constexpr int QA_ROWS = 16;
-constexpr int QA_WAVES = 8;
-constexpr int QA_THREADS = 64 * QA_WAVES;
 constexpr int QA_KCHUNK = 4096;  // columns whose reciprocals of lambda sit in LDS at once
 
+// Waves per 16-row workgroup: INT4 16 (four per SIMD, to keep more of X in
+// flight) unless the T partials of a large rank would not fit in LDS; FP4 8
+// (measured faster).
+template <int MODE, int RB>
+struct QaShape {
+  static constexpr int kWaves = (MODE == 0 && RB <= 8) ? 16 : 8;
+  static constexpr int kThreads = 64 * kWaves;
+};
+
 // LDS: the reciprocal table during the main loop, the T partials afterwards.
-template <int RB>
+template <int MODE, int RB>
 struct QaLds {
   static constexpr int kRcp = QA_KCHUNK * 8;
-  static constexpr int kRed = QA_WAVES * (RB > 0 ? RB : 1) * 4 * 64 * 4;
+  static constexpr int kRed = QaShape<MODE, RB>::kWaves * (RB > 0 ? RB : 1) * 4 * 64 * 4;
   static constexpr int kBytes = kRcp > kRed ? kRcp : kRed;
 };
 
@@ -71,21 +78,26 @@ __device__ __forceinline__ void fp6_fields16(const uint32_t (&c)[16], uint32_t& 
   d2 = (uint32_t)hi;
 }
 
-// Where a lane writes the activation image: null img = no image.
+// Where a lane writes the activation image: null img = no image.  With
+// S > 1 the workgroup at blockIdx.y = s covers K range s and writes its T
+// partial sums (tpart != 0) instead of T, for split_t_kernel to add.
 struct QaImage {
   uint8_t* img;
   int64_t RT;
-  size_t scale, lr;
+  size_t scale, lr, tpart;
+  int S;
 };
 
 // MODE 0 = INT4, 1 = FP4.  RB = rank / 16 (0 = no down-projection).
 // CODES = false skips the quantizer (stand-alone down-projection).
 template <int MODE, int RB, bool CODES>
-__global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
+__global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_kernel(
     int64_t M, int K, const uint16_t* __restrict__ X, const float* __restrict__ lambda,
     const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ xcodes,
     void* __restrict__ xscales, float* __restrict__ T, QaImage qi) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<RB>::kBytes];
+  constexpr int QA_WAVES = QaShape<MODE, RB>::kWaves;
+  constexpr int QA_THREADS = QaShape<MODE, RB>::kThreads;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<MODE, RB>::kBytes];
   double* rlam = reinterpret_cast<double*>(smem);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -96,13 +108,17 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
   const int64_t irt = row >> 5;     // image row tile and lane slot of this row
   const int irr = (int)(row & 31);
   const uint16_t* xrow = X + (row_ok ? row : 0) * (int64_t)K;
+  // this workgroup's K range: groups [G s / S, G (s + 1) / S)
+  const int S = qi.S > 1 ? qi.S : 1;
+  const int kbeg = (int)((int64_t)(K >> 6) * blockIdx.y / S) * 64;
+  const int kend = (int)((int64_t)(K >> 6) * (blockIdx.y + 1) / S) * 64;
 
   v4f tacc[RB > 0 ? RB : 1];
 #pragma unroll
   for (int b = 0; b < (RB > 0 ? RB : 1); ++b) tacc[b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = 0; kc < K; kc += QA_KCHUNK) {
-    const int kn = min(QA_KCHUNK, K - kc);
+  for (int kc = kbeg; kc < kend; kc += QA_KCHUNK) {
+    const int kn = min(QA_KCHUNK, kend - kc);
     __syncthreads();  // the previous chunk is done with the table
     for (int c = threadIdx.x; c < kn; c += QA_THREADS) rlam[c] = 1.0 / (double)lambda[kc + c];
     __syncthreads();
@@ -130,12 +146,22 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
       float xh[16];
       float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t xbits = (xw[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        const float q = (float)((double)bf16_to_f32(xbits) * rlam[kl + i]);
-        hb[i] = f32_to_bf16(q);
-        xh[i] = bf16_to_f32(hb[i]);
-        amax = fmaxf(amax, fabsf(xh[i]));
+      for (int i = 0; i < 16; i += 2) {
+        float q[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t xbits = (xw[i >> 1] >> (e * 16)) & 0xFFFFu;
+          q[e] = (float)((double)bf16_to_f32(xbits) * rlam[kl + i + e]);
+        }
+        // RNE to bf16 (v_cvt_pk_bf16_f32: the same rounding as the
+        // bit-level definition for every finite value)
+        const v2f qv = {q[0], q[1]};
+        const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(qv, v2bf));
+        hb[i] = pk & 0xFFFFu;
+        hb[i + 1] = pk >> 16;
+        xh[i] = __uint_as_float(pk << 16);
+        xh[i + 1] = __uint_as_float(pk & 0xFFFF0000u);
+        amax = fmaxf(amax, fmaxf(fabsf(xh[i]), fabsf(xh[i + 1])));
       }
 
       if constexpr (CODES) {
@@ -261,6 +287,14 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] += red[w][b][q][l0 + i];
       const int64_t m = (int64_t)blockIdx.x * QA_ROWS + mr;
+      if (S > 1) {
+        // partial sums of K range blockIdx.y, added by split_t_kernel
+        float* tp = reinterpret_cast<float*>(qi.img + qi.tpart) +
+                    ((int64_t)blockIdx.y * qi.RT * 32 + m) * rank + 8 * c8;
+        *reinterpret_cast<v4f*>(tp) = v4f{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<v4f*>(tp + 4) = v4f{v[4], v[5], v[6], v[7]};
+        continue;
+      }
       if (T != nullptr && m < M) {
         float* tp = T + m * rank + 8 * c8;
         *reinterpret_cast<v4f*>(tp) = v4f{v[0], v[1], v[2], v[3]};
@@ -285,13 +319,55 @@ __global__ __launch_bounds__(QA_THREADS) void quantize_act_kernel(
   }
 }
 
+// T of the image (and of the row-major output when T != null) from the S
+// partial sums, added in the order of the K ranges; one thread per (row,
+// 8 consecutive ranks).
+__global__ __launch_bounds__(256) void split_t_kernel(int64_t M, int rank, float* __restrict__ T,
+                                                      QaImage qi) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c8n = rank / 8;
+  const int64_t rows = qi.RT * 32;
+  if (idx >= rows * c8n) return;
+  const int64_t m = idx / c8n;
+  const int c8 = (int)(idx - m * c8n);
+  const float* tp = reinterpret_cast<const float*>(qi.img + qi.tpart) + m * rank + 8 * c8;
+  v4f a = *reinterpret_cast<const v4f*>(tp), bq = *reinterpret_cast<const v4f*>(tp + 4);
+  for (int sp = 1; sp < qi.S; ++sp) {
+    const float* q = tp + (int64_t)sp * rows * rank;
+    const v4f x = *reinterpret_cast<const v4f*>(q), y = *reinterpret_cast<const v4f*>(q + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] += x[i];
+      bq[i] += y[i];
+    }
+  }
+  const float v[8] = {a[0], a[1], a[2], a[3], bq[0], bq[1], bq[2], bq[3]};
+  if (T != nullptr && m < M) {
+    *reinterpret_cast<v4f*>(T + m * rank + 8 * c8) = a;
+    *reinterpret_cast<v4f*>(T + m * rank + 8 * c8 + 4) = bq;
+  }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+    hi[i] = h0 | (h1 << 16);
+    lo[i] = f32_to_bf16(v[2 * i] - bf16_to_f32(h0)) |
+            (f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1)) << 16);
+  }
+  const int b = c8 >> 1;
+  uint8_t* blk = qi.img + qi.lr + ((int64_t)b * qi.RT + (m >> 5)) * LR_XBLOCK;
+  const int slot = 32 * (c8 & 1) + (int)(m & 31);
+  *reinterpret_cast<v4u*>(blk + 16 * slot) = v4u{hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<v4u*>(blk + 1024 + 16 * slot) = v4u{lo[0], lo[1], lo[2], lo[3]};
+}
+
 template <int MODE, bool CODES>
 static hipError_t launch_qa_rank(int rb, dim3 grid, hipStream_t s, int64_t M, int K,
                                  const uint16_t* X, const float* lam, const uint16_t* ld,
                                  uint8_t* xc, void* xs, float* T, QaImage qi) {
 #define SVDQ_QA_CASE(R)                                                                   \
   case R:                                                                                 \
-    hipLaunchKernelGGL((quantize_act_kernel<MODE, R, CODES>), grid, dim3(QA_THREADS), 0, \
+    hipLaunchKernelGGL((quantize_act_kernel<MODE, R, CODES>), grid, dim3(QaShape<MODE, R>::kThreads), 0, \
                        s, M, K, X, lam, ld, xc, xs, T, qi);                               \
     break;
   switch (rb) {
@@ -314,20 +390,24 @@ hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint1
                                const float* lambda, const uint16_t* lora_down,
                                uint8_t* xcodes, void* xscales, float* T, void* ximage,
                                hipStream_t s) {
-  QaImage qi{nullptr, 0, 0, 0};
+  QaImage qi{nullptr, 0, 0, 0, 0, 1};
   int64_t rows = M;
   if (ximage != nullptr) {
     const ActImage a = act_image(mode, M, K, rank);
-    qi = QaImage{reinterpret_cast<uint8_t*>(ximage), a.RT, a.scale, a.lr};
+    qi = QaImage{reinterpret_cast<uint8_t*>(ximage), a.RT, a.scale, a.lr, a.tpart, a.S};
     rows = a.RT * 32;  // cover the padding rows too
   }
-  const dim3 grid((unsigned)((rows + QA_ROWS - 1) / QA_ROWS));
   const int rb = lora_down ? rank / 16 : 0;
-  if (mode == 0)
-    return launch_qa_rank<0, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes, xscales, T,
-                                   qi);
-  return launch_qa_rank<1, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes, xscales, T,
-                                 qi);
+  const dim3 grid((unsigned)((rows + QA_ROWS - 1) / QA_ROWS), (unsigned)qi.S);
+  hipError_t e = mode == 0 ? launch_qa_rank<0, true>(rb, grid, s, M, K, X, lambda, lora_down,
+                                                     xcodes, xscales, T, qi)
+                           : launch_qa_rank<1, true>(rb, grid, s, M, K, X, lambda, lora_down,
+                                                     xcodes, xscales, T, qi);
+  if (e != hipSuccess || rb == 0 || qi.S <= 1) return e;
+  const int64_t n = qi.RT * 32 * (rank / 8);
+  hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M, rank,
+                     T, qi);
+  return hipGetLastError();
 }
 
 hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
@@ -335,7 +415,7 @@ hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                hipStream_t s) {
   const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
   return launch_qa_rank<0, false>(rank / 16, grid, s, M, K, X, lambda, lora_down, nullptr,
-                                  nullptr, T, QaImage{nullptr, 0, 0, 0});
+                                  nullptr, T, QaImage{nullptr, 0, 0, 0, 0, 1});
 }
 
 }  // namespace svdq

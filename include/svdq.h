@@ -132,6 +132,11 @@ svdq_status svdq_pack_weight(const svdq_desc* desc, const uint16_t* W, const flo
  *        64 bytes of E8M0 scales.
  *   Low-rank blocks: per (16 ranks, 32 rows) T as bf16 hi + lo (2048 bytes);
  *        per (16 ranks, 32 columns) L2 as bf16 (1024 bytes).
+ *   Partial sums (activation side, rank > 0): the pass that writes the image
+ *        splits K into S ranges of whole 64-groups, S = max(1, min(16,
+ *        (K/64)/48, ceil(1024 / (padded rows / 16)))); when S > 1 the image
+ *        ends with S fp32 partial sums of T per padded row, which a second
+ *        kernel adds in order.
  *   Bias: 64 bytes per 32 columns, then 1024 bytes of zero padding.
  * Rows of the activation image are padded to a multiple of 256 and columns
  * of the weight image to 192 (INT4) or 256 (FP4); padding is zero. */

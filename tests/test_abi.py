@@ -48,10 +48,14 @@ def test_arch_predicate_null():
 def _act_bytes(mode, M, K, rank):
     """Activation image size from the documented blocks: rows padded to 256;
     per (64-group, 32 rows) 2048 bytes (INT4) or 1024 + 64 bytes (FP4); per
-    (16 ranks, 32 rows) 2048 bytes of T."""
+    (16 ranks, 32 rows) 2048 bytes of T; with rank > 0 and S > 1 K ranges
+    (S = ceil(1024 / 16-row blocks), at most 16 and at most (K/64)/48) S
+    fp32 partial sums of T per padded row."""
     rt = -(-M // 256) * 8
     per = 2048 if mode == 0 else 1024 + 64
-    return (K // 64) * rt * per + (rank // 16) * rt * 2048
+    S = max(1, min(16, -(-1024 // (rt * 2)), (K // 64) // 48))
+    part = S * rt * 32 * rank * 4 if rank > 0 and S > 1 else 0
+    return (K // 64) * rt * per + (rank // 16) * rt * 2048 + part
 
 
 def _weight_bytes(mode, N, K, rank):
@@ -65,7 +69,9 @@ def _weight_bytes(mode, N, K, rank):
 
 @pytest.mark.parametrize("mode,M,K,rank", [(0, 300, 512, 16), (0, 256, 512, 0), (1, 256, 512, 16),
                                            (1, 1, 128, 32), (0, 4096, 3072, 32),
-                                           (1, 4096, 3072, 32)])
+                                           (1, 4096, 3072, 32), (0, 300, 6144, 32),
+                                           (0, 4608, 12288, 32), (1, 1024, 12288, 128),
+                                           (0, 8192, 12288, 0)])
 def test_act_image_size_is_host_only(mode, M, K, rank):
     n = ctypes.c_size_t(123)
     assert _lib().svdq_act_image_size(_d(mode=mode, K=K, rank=rank), M, ctypes.byref(n)) == 0

@@ -229,3 +229,13 @@ def test_image_only_quantize(mode):
     torch.cuda.synchronize()
     assert np.array_equal(np_(ximg), np_(g["ximage"]))
     assert np.array_equal(np_(Y.view(torch.int16)), np_(g["Y"].view(torch.int16)))
+
+
+@pytest.mark.parametrize("mode", ["int4", "fp4"])
+def test_split_k_quantize(mode):
+    """K = 6144 with 300 rows: the activation pass splits K into two ranges
+    and a second kernel adds the partial sums of T.  Codes, scales and T
+    against the oracle, and the layer output."""
+    spec = WL.LinearSpec("split_300x6144x256_r32", 300, 6144, 256, 32, mode,
+                         x_outliers=6, x_factor=50.0)
+    _full_check(spec, mode, seed=3)
