@@ -42,6 +42,13 @@ hipError_t launch_fp4_forward(bool out_f32, int64_t M, int N, int K, int rank,
 hipError_t launch_lowrank_up(int rank, bool out_f32, int64_t M, int N, const float* T,
                              const uint16_t* lora_up, void* Y, hipStream_t s);
 
+// AWQ W4A16 (awq.hip).
+hipError_t launch_awq_pack(int N, int K, const uint16_t* W, uint8_t* codes, float* scales,
+                           uint8_t* zeros, hipStream_t s);
+hipError_t launch_awq_linear(bool out_f32, int64_t M, int N, int K, const uint16_t* X,
+                             const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                             const uint16_t* bias, void* Y, hipStream_t s);
+
 // Compute units of the current device (cached per device).
 int device_cus();
 

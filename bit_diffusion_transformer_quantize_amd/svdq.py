@@ -57,6 +57,9 @@ _SIGNATURES = {
     "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
     "svdq_lowrank_down": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp]),
     "svdq_lowrank_up": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
+    "svdq_awq_pack_weight": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_awq_linear": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint32,
+                                       _vp, _vp]),
 }
 
 _lib = None
@@ -265,4 +268,46 @@ def svdq_lowrank_up(d: SvdqDesc, T, lora_up, Y):
     _need(Y, "Y", out_dtype, (M, d.N))
     _check("svdq_lowrank_up",
            load().svdq_lowrank_up(ctypes.byref(d), M, _p(T), _p(lora_up), _p(Y), _stream()))
+    return Y
+
+
+AWQ_GROUP = 64
+
+
+def svdq_awq_pack_weight(W, codes=None, scales=None, zeros=None):
+    """AWQ W4A16 packing of a bf16 weight [N][K]; returns (codes, scales, zeros)."""
+    N, K = W.shape
+    G = K // AWQ_GROUP
+    _need(W, "W", torch.bfloat16, (N, K))
+    if codes is None:
+        codes = torch.empty(N, K // 2, dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty(N, G, dtype=torch.float32, device=W.device)
+    if zeros is None:
+        zeros = torch.empty(N, G, dtype=torch.uint8, device=W.device)
+    _need(codes, "codes", torch.uint8, (N, K // 2))
+    _need(scales, "scales", torch.float32, (N, G))
+    _need(zeros, "zeros", torch.uint8, (N, G))
+    _check("svdq_awq_pack_weight",
+           load().svdq_awq_pack_weight(N, K, _p(W), _p(codes), _p(scales), _p(zeros), _stream()))
+    return codes, scales, zeros
+
+
+def svdq_awq_linear(X, codes, scales, zeros, bias=None, Y=None, out_f32: bool = False):
+    """Y = X deq(W)^T + bias for the AWQ W4A16 layer (small M)."""
+    M, K = X.shape
+    N = codes.shape[0]
+    G = K // AWQ_GROUP
+    out_dtype = torch.float32 if out_f32 else torch.bfloat16
+    _need(X, "X", torch.bfloat16, (M, K))
+    _need(codes, "codes", torch.uint8, (N, K // 2))
+    _need(scales, "scales", torch.float32, (N, G))
+    _need(zeros, "zeros", torch.uint8, (N, G))
+    _need(bias, "bias", torch.bfloat16, (N,), optional=True)
+    if Y is None:
+        Y = torch.empty(M, N, dtype=out_dtype, device=X.device)
+    _need(Y, "Y", out_dtype, (M, N))
+    _check("svdq_awq_linear",
+           load().svdq_awq_linear(M, N, K, _p(X), _p(codes), _p(scales), _p(zeros), _p(bias),
+                                  SVDQ_FLAG_OUT_F32 if out_f32 else 0, _p(Y), _stream()))
     return Y

@@ -203,6 +203,39 @@ svdq_status svdq_lowrank_down(const svdq_desc* desc, int64_t M, const uint16_t* 
 svdq_status svdq_lowrank_up(const svdq_desc* desc, int64_t M, const float* T,
                             const uint16_t* lora_up, void* Y, void* stream);
 
+/* AWQ W4A16 linear layer: 4-bit weights, 16-bit activations (axbrief.com
+ * page, section "The Mechanics of 4-Bit Efficiency and SVDQuant": the
+ * layer type that keeps activations in 16 bits; section "The Trade-off
+ * Between Fused Kernels and Generality": it is assigned to the modulation
+ * linear layers, whose input is one vector per image).  The pages leave the
+ * format open; this library fixes it as
+ *   codes  : uint8 [N][K/2], nibbles 0..15, element 2j in the low nibble;
+ *   scales : float32 [N][K/64], one per (row, group of 64 along K);
+ *   zeros  : uint8 [N][K/64], zero points 0..15;
+ *   deq(W)[n][k] = scales[n][g] * (q[n][k] - zeros[n][g]),  g = k / 64.
+ * Shape limits: 1 <= N <= 2^20, 128 <= K <= 2^20 with K % 128 == 0, and for
+ * svdq_awq_linear 1 <= M <= 64 (a small-batch kernel: it streams the packed
+ * weight once per 4 rows of X).  Pointers follow the conventions above. */
+
+/* Offline: asymmetric min-max quantization of a bf16 weight W [N][K] per
+ * (row, group):
+ *   d = max(fp32(max - min), 1e-5), s = fp32(d / 15),
+ *   z = clamp(rint(fp32(-min / s)), 0, 15),
+ *   q = clamp(rint(fp32(w / s)) + z, 0, 15)       (rint: ties to even).
+ * Every step is one IEEE fp32 operation; codes, scales and zeros are
+ * bit-identical to this definition.  W must be finite. */
+svdq_status svdq_awq_pack_weight(int32_t N, int32_t K, const uint16_t* W, uint8_t* codes,
+                                 float* scales, uint8_t* zeros, void* stream);
+
+/* Y[m][n] = sum_k X[m][k] deq(W)[n][k] + bias[n] for X bf16 [M][K], written
+ * [M][N] as bf16 (RNE) or float32 (flags = SVDQ_FLAG_OUT_F32; other bits are
+ * SVDQ_ERR_ARG).  bias: bf16 [N] or NULL.  fp32 arithmetic: per 16 weights
+ * the kernel forms sum (128 + q) x and sum x from exact bf16 products and
+ * combines them with the group's scale and zero point. */
+svdq_status svdq_awq_linear(int64_t M, int32_t N, int32_t K, const uint16_t* X,
+                            const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                            const uint16_t* bias, uint32_t flags, void* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

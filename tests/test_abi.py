@@ -203,6 +203,28 @@ def test_calibrate_validation():
     assert lib.svdq_calibrate_lambda(16, 512, 0, A, A, A, None) == SHAPE
 
 
+def test_awq_validation():
+    lib = _lib()
+    p = lib.svdq_awq_pack_weight
+    assert p(64, 3072, None, A, A, A, None) == ARG
+    assert p(64, 3072, A, MIS, A, A, None) == ARG
+    assert p(64, 3072, A, A, None, A, None) == ARG
+    assert p(64, 3072, A, A, A, MIS, None) == ARG
+    assert p(0, 3072, A, A, A, A, None) == SHAPE
+    assert p(64, 3000, A, A, A, A, None) == SHAPE      # K % 128
+    assert p(64, 64, A, A, A, A, None) == SHAPE
+    assert p((1 << 20) + 1, 128, A, A, A, A, None) == SHAPE
+    f = lib.svdq_awq_linear
+    assert f(1, 64, 3072, A, A, A, A, None, 2, A, None) == ARG    # unknown flag
+    assert f(1, 64, 3072, None, A, A, A, None, 0, A, None) == ARG
+    assert f(1, 64, 3072, A, A, A, A, MIS, 0, A, None) == ARG     # bias misaligned
+    assert f(1, 64, 3072, A, A, A, A, None, 0, None, None) == ARG
+    assert f(0, 64, 3072, A, A, A, A, None, 0, A, None) == SHAPE
+    assert f(65, 64, 3072, A, A, A, A, None, 0, A, None) == SHAPE
+    assert f(1, 0, 3072, A, A, A, A, None, 0, A, None) == SHAPE
+    assert f(1, 64, 3008, A, A, A, A, None, 0, A, None) == SHAPE
+
+
 def _has_gpu():
     import torch
     return torch.cuda.device_count() > 0
@@ -216,3 +238,5 @@ def test_no_device_is_a_hip_error():
     assert lib.svdq_linear_forward(_d(), 256, A, A, A, None) == HIP
     assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, None) == HIP
     assert lib.svdq_prepare_weight(_d(), A, A, A, None, A, None) == HIP
+    assert lib.svdq_awq_pack_weight(64, 3072, A, A, A, A, None) == HIP
+    assert lib.svdq_awq_linear(1, 64, 3072, A, A, A, A, None, 0, A, None) == HIP

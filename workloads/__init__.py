@@ -38,7 +38,7 @@ class LinearSpec:
     K: int
     N: int
     rank: int
-    mode: str                      # "int4" or "fp4"
+    mode: str                      # "int4", "fp4", or "awq" (W4A16, rank 0)
     x_outliers: int
     x_factor: Factor
     w_outliers: int = 0
@@ -84,6 +84,19 @@ def block_chain_specs(rank: int = 128):
                                   x_factor=1.0 if down else (20.0, 100.0),
                                   w_outliers=_round_count(0.005, K), w_factor=10.0))
     return out
+
+
+def modulation_specs(M: int = 1):
+    """The AWQ W4A16 modulation linears of one FLUX.1 forward: their input is
+    one conditioning vector per image (M = batch).  Hidden size 3072; each of
+    the 19 double-stream blocks has an image and a text modulation map
+    3072 -> 6*3072, each of the 38 single-stream blocks 3072 -> 3*3072, and
+    the output norm 3072 -> 2*3072.  Returns [(spec, count)]."""
+    kw = dict(rank=0, mode="awq", x_outliers=0, x_factor=1.0,
+              w_outliers=_round_count(0.005, 3072), w_factor=10.0)
+    return [(LinearSpec(f"mod_double_{M}x3072x18432", M, 3072, 18432, **kw), 38),
+            (LinearSpec(f"mod_single_{M}x3072x9216", M, 3072, 9216, **kw), 38),
+            (LinearSpec(f"mod_norm_out_{M}x3072x6144", M, 3072, 6144, **kw), 1)]
 
 
 def draw(spec: LinearSpec, seed: int = 0, M: Optional[int] = None):
