@@ -21,6 +21,9 @@
 // of values at each exchange step.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -136,12 +139,160 @@ __device__ __forceinline__ void wave_reduce_set(float (&v)[V], int lane) {
   for (; bit >= 0; --bit) v[0] += __shfl_xor(v[0], 1 << bit, 64);
 }
 
+// The weight side of RB rows for this lane's U units: codes, scales and
+// zero points, issued row by row so that a row's arithmetic can start while
+// later rows are still arriving (loads retire in issue order).
+template <int RB>
+struct AwqBlock {
+  v2u w[RB][kAwqUnits];
+  float s[RB][kAwqUnits];
+  // zero points and bias stay in their memory widths: a loop-carried value
+  // widened at the load would make the loop wait for the prefetched block
+  uint8_t z[RB][kAwqUnits];
+  uint16_t b[RB];   // bf16 bias of the rows (raw; ignored without bias)
+};
+
+template <int RB, bool WITH_BIAS>
+__device__ __forceinline__ void awq_load_block(AwqBlock<RB>& bk, int row0, int N, int K, int G,
+                                               const int (&gu)[kAwqUnits],
+                                               const uint8_t* __restrict__ codes,
+                                               const float* __restrict__ scales,
+                                               const uint8_t* __restrict__ zeros,
+                                               const uint16_t* __restrict__ bias) {
+  // without a bias the (ignored) value is read from the zero points, which
+  // hold at least 2N bytes, so that the load needs no branch
+  const uint16_t* bsrc = bias != nullptr ? bias : reinterpret_cast<const uint16_t*>(zeros);
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int64_t row = min(row0 + r, N - 1);
+    if constexpr (WITH_BIAS) bk.b[r] = bsrc[row];
+#pragma unroll
+    for (int u = 0; u < kAwqUnits; ++u)
+      bk.w[r][u] = __builtin_nontemporal_load(
+          reinterpret_cast<const v2u*>(codes + row * (K / 2) + (int64_t)gu[u] * 8));
+#pragma unroll
+    for (int u = 0; u < kAwqUnits; ++u) {
+      bk.s[r][u] = scales[row * G + (gu[u] >> 2)];
+      bk.z[r][u] = zeros[row * G + (gu[u] >> 2)];
+    }
+  }
+}
+
+// Activations of this lane's units for MC batch rows: raw loads, then the
+// reordered bf16 pairs and their sums (zero for units past K and rows past M).
+template <int MC>
+struct AwqAct {
+  v4u raw[kAwqUnits][MC][2];
+  v4u xp[kAwqUnits][MC][2];
+  float xs[kAwqUnits][MC];
+};
+
+template <int MC>
+__device__ __forceinline__ void awq_load_act(AwqAct<MC>& ac, int m0, int M, int K,
+                                             const int (&gu)[kAwqUnits],
+                                             const uint16_t* __restrict__ X) {
+#pragma unroll
+  for (int u = 0; u < kAwqUnits; ++u)
+#pragma unroll
+    for (int mi = 0; mi < MC; ++mi) {
+      const int m = min(m0 + mi, M - 1);
+      const v4u* src = reinterpret_cast<const v4u*>(X + (int64_t)m * K + (int64_t)gu[u] * 16);
+      ac.raw[u][mi][0] = src[0];
+      ac.raw[u][mi][1] = src[1];
+    }
+}
+
+template <int MC>
+__device__ __forceinline__ void awq_prep_act(AwqAct<MC>& ac, int m0, int M,
+                                             const bool (&valid)[kAwqUnits]) {
+#pragma unroll
+  for (int u = 0; u < kAwqUnits; ++u)
+#pragma unroll
+    for (int mi = 0; mi < MC; ++mi) {
+      const bool live = valid[u] && m0 + mi < M;
+      v4u a = ac.raw[u][mi][0], b = ac.raw[u][mi][1];
+      if (!live) a = b = v4u{0u, 0u, 0u, 0u};
+      ac.xp[u][mi][0] = awq_reorder_x(a);
+      ac.xp[u][mi][1] = awq_reorder_x(b);
+      float t = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        t = dot2(a[j], 0x3F803F80u, t);
+        t = dot2(b[j], 0x3F803F80u, t);
+      }
+      ac.xs[u][mi] = t;
+    }
+}
+
+// acc[r][mi] += sum over this lane's units of s * (A - (128 + z) B).
+template <int RB, int MC>
+__device__ __forceinline__ void awq_block_dot(const AwqBlock<RB>& bk, const AwqAct<MC>& ac,
+                                              float (&acc)[RB * MC]) {
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int u = 0; u < kAwqUnits; ++u) {
+      const v4u c0 = awq_codes_bf16(bk.w[r][u][0]);
+      const v4u c1 = awq_codes_bf16(bk.w[r][u][1]);
+      // 128 + z as fp32: z in the mantissa bits 16..19 of 128.0f
+      const float off = __uint_as_float(0x43000000u | ((uint32_t)bk.z[r][u] << 16));
+#pragma unroll
+      for (int mi = 0; mi < MC; ++mi) {
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a = dot2(c0[j], ac.xp[u][mi][0][j], a);
+          a = dot2(c1[j], ac.xp[u][mi][1][j], a);
+        }
+        acc[r * MC + mi] = fmaf(bk.s[r][u], fmaf(-off, ac.xs[u][mi], a), acc[r * MC + mi]);
+      }
+    }
+}
+
+// Wave-wide sums of acc, plus the bias, stored by one lane per output.
+// The bias comes either from the block's loads (brow, streaming kernel) or,
+// with brow == nullptr, is read here after all other loads have landed.
+template <int RB, int MC, bool F32>
+__device__ __forceinline__ void awq_store(float (&acc)[RB * MC], const uint16_t* brow,
+                                          const uint16_t* __restrict__ bias, int lane, int row0,
+                                          int m0, int M, int N, void* __restrict__ Y) {
+  wave_reduce_set<RB * MC>(acc, lane);
+  constexpr int kShift = 6 - __builtin_ctz(RB * MC);
+  const int idx = lane >> kShift;
+  float bv = 0.0f;
+  if (brow != nullptr) {
+    uint32_t bsel = brow[0];
+#pragma unroll
+    for (int r = 1; r < RB; ++r) bsel = idx / MC == r ? (uint32_t)brow[r] : bsel;
+    bv = bias != nullptr ? bf16_to_f32(bsel) : 0.0f;
+  }
+  const int row = row0 + idx / MC, m = m0 + idx % MC;
+  if ((lane & ((1 << kShift) - 1)) != 0 || row >= N || m >= M) return;
+  if (brow == nullptr && bias != nullptr) bv = bf16_to_f32(bias[row]);
+  const float y = acc[0] + bv;
+  if constexpr (F32)
+    reinterpret_cast<float*>(Y)[(int64_t)m * N + row] = y;
+  else
+    reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + row] = (uint16_t)f32_to_bf16(y);
+}
+
+__device__ __forceinline__ void awq_units(int slab, int lane, int KU, int (&gu)[kAwqUnits],
+                                          bool (&valid)[kAwqUnits]) {
+#pragma unroll
+  for (int u = 0; u < kAwqUnits; ++u) {
+    const int unit = slab * kAwqSlabUnits + u * 64 + lane;
+    valid[u] = unit < KU;
+    gu[u] = valid[u] ? unit : KU - 1;   // clamped; its activations are zero
+  }
+}
+
+// General K: one block of kAwqRows rows per wave, K in slabs of 3072 codes.
 template <int MC, bool F32>
 __global__ __launch_bounds__(kAwqWaves * 64) void awq_gemv_kernel(
     int M, int N, int K, const uint16_t* __restrict__ X, const uint8_t* __restrict__ codes,
     const float* __restrict__ scales, const uint8_t* __restrict__ zeros,
     const uint16_t* __restrict__ bias, void* __restrict__ Y) {
-  constexpr int R = kAwqRows, U = kAwqUnits;
+  constexpr int R = kAwqRows;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * kAwqWaves + wave) * R;
@@ -154,122 +305,131 @@ __global__ __launch_bounds__(kAwqWaves * 64) void awq_gemv_kernel(
   float acc[R * MC];
 #pragma unroll
   for (int i = 0; i < R * MC; ++i) acc[i] = 0.0f;
-
   for (int slab = 0; slab < nslab; ++slab) {
-    // units of this lane; past K they are clamped to the last unit and get
-    // zero activations
-    int gu[U];
-    bool valid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int unit = slab * kAwqSlabUnits + u * 64 + lane;
-      valid[u] = unit < KU;
-      gu[u] = valid[u] ? unit : KU - 1;
-    }
-    // Every load of the slab is issued before any arithmetic: the
-    // activations (cache hits) first, then the weight side (HBM), so that
-    // waiting for the activations (loads retire in issue order) leaves all
-    // weight loads in flight.  The scheduling barrier keeps the compiler from
-    // sinking loads to their first use.
-    v4u xr[U][MC][2];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mi = 0; mi < MC; ++mi) {
-        const int m = min(m0 + mi, M - 1);
-        const v4u* src = reinterpret_cast<const v4u*>(X + (int64_t)m * K + (int64_t)gu[u] * 16);
-        xr[u][mi][0] = src[0];
-        xr[u][mi][1] = src[1];
-      }
-    v2u wv[R][U];
-    float sv[R][U];
-    uint32_t zv[R][U];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = min(row0 + r, N - 1);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        wv[r][u] = __builtin_nontemporal_load(
-            reinterpret_cast<const v2u*>(codes + row * (K / 2) + (int64_t)gu[u] * 8));
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = min(row0 + r, N - 1);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        sv[r][u] = scales[row * G + (gu[u] >> 2)];
-        zv[r][u] = zeros[row * G + (gu[u] >> 2)];
-      }
-    }
+    int gu[kAwqUnits];
+    bool valid[kAwqUnits];
+    awq_units(slab, lane, KU, gu, valid);
+    // every load of the slab before any arithmetic: activations (cache hits)
+    // first, then the weight side; the scheduling barrier keeps the compiler
+    // from sinking loads to their first use
+    AwqAct<MC> ac;
+    AwqBlock<R> bk;
+    awq_load_act<MC>(ac, m0, M, K, gu, X);
+    awq_load_block<R, false>(bk, row0, N, K, G, gu, codes, scales, zeros, bias);
     __builtin_amdgcn_sched_barrier(0);
-    // activations as reordered bf16 pairs, and their sums; zero for units
-    // past K and batch rows past M
-    v4u xp[U][MC][2];
-    float xs[U][MC];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mi = 0; mi < MC; ++mi) {
-        const bool live = valid[u] && m0 + mi < M;
-        v4u a = xr[u][mi][0], b = xr[u][mi][1];
-        if (!live) a = b = v4u{0u, 0u, 0u, 0u};
-        xp[u][mi][0] = awq_reorder_x(a);
-        xp[u][mi][1] = awq_reorder_x(b);
-        float t = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          t = dot2(a[j], 0x3F803F80u, t);
-          t = dot2(b[j], 0x3F803F80u, t);
-        }
-        xs[u][mi] = t;
-      }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const v4u c0 = awq_codes_bf16(wv[r][u][0]);
-        const v4u c1 = awq_codes_bf16(wv[r][u][1]);
-        const float off = (float)(128u + zv[r][u]);
-#pragma unroll
-        for (int mi = 0; mi < MC; ++mi) {
-          float a = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a = dot2(c0[j], xp[u][mi][0][j], a);
-            a = dot2(c1[j], xp[u][mi][1][j], a);
-          }
-          acc[r * MC + mi] = fmaf(sv[r][u], fmaf(-off, xs[u][mi], a), acc[r * MC + mi]);
-        }
-      }
+    awq_prep_act<MC>(ac, m0, M, valid);
+    awq_block_dot<R, MC>(bk, ac, acc);
   }
+  awq_store<R, MC, F32>(acc, nullptr, bias, lane, row0, m0, M, N, Y);
+}
 
-  wave_reduce_set<R * MC>(acc, lane);
-  constexpr int kShift = 6 - __builtin_ctz(R * MC);
-  if ((lane & ((1 << kShift) - 1)) != 0) return;
-  const int idx = lane >> kShift;
-  const int r = idx / MC, mi = idx % MC;
-  const int row = row0 + r, m = m0 + mi;
-  if (row >= N || m >= M) return;
-  float y = acc[0];
-  if (bias != nullptr) y += bf16_to_f32(bias[row]);
-  if constexpr (F32)
-    reinterpret_cast<float*>(Y)[(int64_t)m * N + row] = y;
-  else
-    reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + row] = (uint16_t)f32_to_bf16(y);
+// K <= 3072 (one slab): each wave streams row blocks of RB rows, block
+// w, w + W, w + 2W, ... (W = waves in the grid), with the activations held in
+// registers throughout and the next block's loads in flight while the current
+// block is computed.  Two register sets alternate; the loop is unrolled by two
+// so that no set is copied while its loads are outstanding.
+template <int MC, bool F32, int RB>
+__global__ __launch_bounds__(kAwqWaves * 64) void awq_gemv_stream_kernel(
+    int M, int N, int K, const uint16_t* __restrict__ X, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint8_t* __restrict__ zeros,
+    const uint16_t* __restrict__ bias, void* __restrict__ Y) {
+  const int lane = threadIdx.x & 63;
+  const int nblk = (N + RB - 1) / RB;
+  const int stride = gridDim.x * kAwqWaves;
+  int blk = blockIdx.x * kAwqWaves + (threadIdx.x >> 6);
+  if (blk >= nblk) return;
+  const int m0 = blockIdx.y * MC;
+  const int KU = K / 16;
+  const int G = K / kAwqGroup;
+  int gu[kAwqUnits];
+  bool valid[kAwqUnits];
+  awq_units(0, lane, KU, gu, valid);
+
+  AwqAct<MC> ac;
+  AwqBlock<RB> b0, b1;
+  awq_load_act<MC>(ac, m0, M, K, gu, X);
+  awq_load_block<RB, true>(b0, blk * RB, N, K, G, gu, codes, scales, zeros, bias);
+  __builtin_amdgcn_sched_barrier(0);
+  awq_prep_act<MC>(ac, m0, M, valid);
+
+  auto finish = [&](const AwqBlock<RB>& bk, int b) {
+    float acc[RB * MC];
+#pragma unroll
+    for (int i = 0; i < RB * MC; ++i) acc[i] = 0.0f;
+    awq_block_dot<RB, MC>(bk, ac, acc);
+    awq_store<RB, MC, F32>(acc, bk.b, bias, lane, b * RB, m0, M, N, Y);
+  };
+  // The prefetch is unconditional so that the wait counts are exact on every
+  // path: past the last block it re-reads the block being computed (a cache
+  // hit); each block's arithmetic appears once per loop body, so the
+  // compiler cannot hoist it above the prefetch.
+#pragma nounroll
+  for (;;) {
+    const int n1 = blk + stride;
+    awq_load_block<RB, true>(b1, (n1 < nblk ? n1 : blk) * RB, N, K, G, gu, codes, scales, zeros, bias);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(b0, blk);
+    if (n1 >= nblk) break;
+    blk = n1;
+    const int n2 = blk + stride;
+    awq_load_block<RB, true>(b0, (n2 < nblk ? n2 : blk) * RB, N, K, G, gu, codes, scales, zeros, bias);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(b1, blk);
+    if (n2 >= nblk) break;
+    blk = n2;
+  }
+}
+
+constexpr int kAwqStreamRows = 2;   // rows per block of the streaming kernel
+
+// Resident workgroups per CU of the streaming kernel (from its register
+// use), so that the grid is exactly one wave of workgroups.
+template <int MC, bool F32>
+int stream_wg_per_cu() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, awq_gemv_stream_kernel<MC, F32, kAwqStreamRows>, kAwqWaves * 64, 0) != hipSuccess)
+      n = 1;
+    v = std::max(1, n);
+    cached.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int MC, bool F32>
+void launch_gemv_t(int64_t M, int N, int K, const uint16_t* X, const uint8_t* codes,
+                   const float* scales, const uint8_t* zeros, const uint16_t* bias, void* Y,
+                   hipStream_t s) {
+  const unsigned gy = (unsigned)((M + MC - 1) / MC);
+  // The streaming kernel wins once its waves have several blocks each, or
+  // with a batch (more arithmetic per byte); a single-row GEMV of moderate
+  // N is latency-bound and runs fastest with every block's loads issued at
+  // once by the one-shot kernel.
+  const int64_t nblk = (N + kAwqStreamRows - 1) / kAwqStreamRows;
+  const int64_t resident = (int64_t)device_cus() * stream_wg_per_cu<MC, F32>();
+  if (K <= kAwqSlabUnits * 16 && (MC > 1 || nblk > 8 * resident * kAwqWaves)) {
+    const int64_t wgs = (nblk + kAwqWaves - 1) / kAwqWaves;
+    const dim3 grid((unsigned)std::min(wgs, resident), gy);
+    awq_gemv_stream_kernel<MC, F32, kAwqStreamRows><<<grid, kAwqWaves * 64, 0, s>>>(
+        (int)M, N, K, X, codes, scales, zeros, bias, Y);
+  } else {
+    const dim3 grid((unsigned)((N + kAwqWaves * kAwqRows - 1) / (kAwqWaves * kAwqRows)), gy);
+    awq_gemv_kernel<MC, F32><<<grid, kAwqWaves * 64, 0, s>>>((int)M, N, K, X, codes, scales,
+                                                             zeros, bias, Y);
+  }
 }
 
 template <int MC>
 hipError_t launch_gemv(bool f32, int64_t M, int N, int K, const uint16_t* X,
                        const uint8_t* codes, const float* scales, const uint8_t* zeros,
                        const uint16_t* bias, void* Y, hipStream_t s) {
-  const dim3 grid((unsigned)((N + kAwqWaves * kAwqRows - 1) / (kAwqWaves * kAwqRows)),
-                  (unsigned)((M + MC - 1) / MC));
   if (f32)
-    awq_gemv_kernel<MC, true><<<grid, kAwqWaves * 64, 0, s>>>((int)M, N, K, X, codes, scales,
-                                                              zeros, bias, Y);
+    launch_gemv_t<MC, true>(M, N, K, X, codes, scales, zeros, bias, Y, s);
   else
-    awq_gemv_kernel<MC, false><<<grid, kAwqWaves * 64, 0, s>>>((int)M, N, K, X, codes, scales,
-                                                               zeros, bias, Y);
+    launch_gemv_t<MC, false>(M, N, K, X, codes, scales, zeros, bias, Y, s);
   return hipGetLastError();
 }
 

@@ -211,7 +211,8 @@ svdq_status svdq_lowrank_up(const svdq_desc* d, int64_t M, const float* T,
 svdq_status svdq_awq_pack_weight(int32_t N, int32_t K, const uint16_t* W, uint8_t* codes,
                                  float* scales, uint8_t* zeros, void* stream) {
   if (!ptr_ok(W) || !ptr_ok(codes) || !ptr_ok(scales) || !ptr_ok(zeros)) return SVDQ_ERR_ARG;
-  if (N < 1 || N > (1 << 20) || K < 128 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (N < 1 || N > (1 << 24) || K < 128 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if ((int64_t)N * K > (int64_t(1) << 36)) return SVDQ_ERR_SHAPE;
   SVDQ_TRY(check_device());
   return from_hip(svdq::launch_awq_pack(N, K, W, codes, scales, zeros, (hipStream_t)stream));
 }
@@ -224,7 +225,8 @@ svdq_status svdq_awq_linear(int64_t M, int32_t N, int32_t K, const uint16_t* X,
       !opt_ok(bias))
     return SVDQ_ERR_ARG;
   if (M < 1 || M > 64) return SVDQ_ERR_SHAPE;
-  if (N < 1 || N > (1 << 20) || K < 128 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (N < 1 || N > (1 << 24) || K < 128 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if ((int64_t)N * K > (int64_t(1) << 36)) return SVDQ_ERR_SHAPE;
   SVDQ_TRY(check_device());
   return from_hip(svdq::launch_awq_linear((flags & SVDQ_FLAG_OUT_F32) != 0u, M, N, K, X, codes,
                                           scales, zeros, bias, Y, (hipStream_t)stream));

@@ -213,9 +213,12 @@ svdq_status svdq_lowrank_up(const svdq_desc* desc, int64_t M, const float* T,
  *   scales : float32 [N][K/64], one per (row, group of 64 along K);
  *   zeros  : uint8 [N][K/64], zero points 0..15;
  *   deq(W)[n][k] = scales[n][g] * (q[n][k] - zeros[n][g]),  g = k / 64.
- * Shape limits: 1 <= N <= 2^20, 128 <= K <= 2^20 with K % 128 == 0, and for
- * svdq_awq_linear 1 <= M <= 64 (a small-batch kernel: it streams the packed
- * weight once per 4 rows of X).  Pointers follow the conventions above. */
+ * Shape limits: 1 <= N <= 2^24, 128 <= K <= 2^20 with K % 128 == 0,
+ * N*K <= 2^36, and for svdq_awq_linear 1 <= M <= 64 (a small-batch kernel:
+ * it streams the packed weight once per 4 rows of X).  Layers that share
+ * their input (the modulation maps of all blocks read the same conditioning
+ * vector) can be packed as one weight with their rows concatenated and run
+ * as one call.  Pointers follow the conventions above. */
 
 /* Offline: asymmetric min-max quantization of a bf16 weight W [N][K] per
  * (row, group):

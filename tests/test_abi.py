@@ -213,7 +213,8 @@ def test_awq_validation():
     assert p(0, 3072, A, A, A, A, None) == SHAPE
     assert p(64, 3000, A, A, A, A, None) == SHAPE      # K % 128
     assert p(64, 64, A, A, A, A, None) == SHAPE
-    assert p((1 << 20) + 1, 128, A, A, A, A, None) == SHAPE
+    assert p((1 << 24) + 1, 128, A, A, A, A, None) == SHAPE
+    assert p(1 << 24, 8192, A, A, A, A, None) == SHAPE          # N*K > 2^36
     f = lib.svdq_awq_linear
     assert f(1, 64, 3072, A, A, A, A, None, 2, A, None) == ARG    # unknown flag
     assert f(1, 64, 3072, None, A, A, A, None, 0, A, None) == ARG

@@ -181,3 +181,71 @@ def test_w4a4_graph_replay_matches_eager(mode):
         S.svdq_quantize_act(d, Xd, lam, ld, ximage=xi)
         S.svdq_linear_forward(d, M, xi, wi, Y)
     _graph_replays_match(run, Y)
+
+
+@pytest.mark.parametrize("K", [128, 256])
+def test_awq_linear_streaming_single_row(K):
+    """M = 1 with N large enough for the streaming kernel (several blocks
+    per resident wave); K = 128 leaves most lanes without a unit."""
+    M, N = 1, 140000
+    _say("awq linear streaming", M, K, N)
+    X, W, b = WL.draw(_spec(M, K, N), seed=13)
+    c, s, z = O.awq_quantize(WL.bits(W))
+    _y_check(WL.bits(X), c, s, z, WL.bits(b), out_f32=False)
+
+
+def test_awq_fused_modulation_sampled():
+    """All 77 modulation maps of a FLUX.1 forward as one call: the packed
+    weights of the three layer shapes concatenated along N (38 + 38 + 1
+    copies, 1,056,768 rows), M = 1; 1024 sampled outputs against the oracle
+    of their source layer."""
+    S = _S()
+    plan = WL.modulation_specs(1)
+    _say("awq fused modulation", sum(sp.N * n for sp, n in plan), "rows")
+    X = None
+    parts, oracle_parts = [], []
+    for spec, count in plan:
+        Xs, W, b = WL.draw(spec, seed=0)
+        X = Xs if X is None else X        # the shared conditioning vector
+        c, s, z = _pack_check(WL.bits(W))
+        cd, sd, zd = (torch.from_numpy(a).to(DEV) for a in (c, s, z))
+        bd = b.to(DEV)
+        parts.append((cd, sd, zd, bd, count))
+        oracle_parts.append((spec.N, count, c, s, z, WL.bits(b)))
+    C = torch.cat([p[0] for p in parts for _ in range(p[4])])
+    Sc = torch.cat([p[1] for p in parts for _ in range(p[4])])
+    Z = torch.cat([p[2] for p in parts for _ in range(p[4])])
+    B = torch.cat([p[3] for p in parts for _ in range(p[4])])
+    N = C.shape[0]
+    xb = WL.bits(X)
+    Y = torch.full((1, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    S.svdq_awq_linear(X.to(DEV), C, Sc, Z, B, Y=Y)
+    y = Y.float().cpu().numpy()[0].astype(np.float64)
+    del C, Sc, Z, B
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(N, 1024, replace=False))
+    # map each sampled row to (layer shape, row within the layer)
+    starts, off = [], 0
+    for n, count, *_ in oracle_parts:
+        starts.append(off)
+        off += n * count
+    got, want, ref_rows = [], [], []
+    for r in rows:
+        k = max(i for i, st in enumerate(starts) if st <= r)
+        n, count, c, s, z, bb = oracle_parts[k]
+        ref_rows.append((k, (r - starts[k]) % n))
+    for k in range(len(oracle_parts)):
+        sel = [i for i, (kk, _) in enumerate(ref_rows) if kk == k]
+        if not sel:
+            continue
+        lr = np.array([ref_rows[i][1] for i in sel])
+        n, count, c, s, z, bb = oracle_parts[k]
+        Yo = O.awq_forward(xb, c[lr], s[lr], z[lr], bb[lr])[0]
+        x = O.bf16_to_f32(xb).astype(np.float64)
+        sg = np.repeat(s[lr].astype(np.float64), 64, axis=1)
+        E = (np.abs(x) @ sg.T)[0]
+        A = (np.abs(x) @ np.abs(O.awq_dequant(c[lr], s[lr], z[lr])).T)[0]
+        tol = 2.0 ** -12 * E + 2.0 ** -16 * A + 2.0 ** -8 * np.abs(Yo)
+        err = np.abs(y[rows[sel]] - Yo)
+        assert np.all(err <= tol), f"layer shape {k}: max excess {(err - tol).max()}"
