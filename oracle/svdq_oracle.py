@@ -254,10 +254,15 @@ def smooth_act(X_bf16: np.ndarray, lam: np.ndarray) -> np.ndarray:
     return f32_to_bf16(q)
 
 
-def quantize_act(X_bf16, lam, L1_bf16, mode: str):
+def quantize_act(X_bf16, lam, L1_bf16, mode: str, gelu_in: bool = False):
     """Run-time activation side: smoothing, 4-bit quantization of X_hat and
-    the low-rank down-projection T = X_hat L1 from the same X_hat.
+    the low-rank down-projection T = X_hat L1 from the same X_hat.  With
+    gelu_in the layer's input is bf16_RNE(GELU_tanh(X)) (the MLP-down layer
+    reading the up-projection's output; the fp32 steps are in gelu_oracle).
     Returns (packed codes, scales, T fp64 [M, r] or None, X_hat bf16 bits)."""
+    if gelu_in:
+        from .gelu_oracle import gelu_bf16
+        X_bf16 = gelu_bf16(X_bf16)
     Xh = smooth_act(X_bf16, lam)
     Xf = bf16_to_f32(Xh)
     if mode == "int4":
