@@ -24,11 +24,11 @@ size_t weight_image_bytes(int mode, int N, int K, int rank);
 hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down,
                                uint8_t* xcodes, void* xscales, float* T, void* ximage,
-                               hipStream_t s);
+                               bool gelu, hipStream_t s);
 
 hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down, float* T,
-                               hipStream_t s);
+                               bool gelu, hipStream_t s);
 
 hipError_t launch_prepare_weight(int mode, int N, int K, int rank, const uint8_t* wcodes,
                                  const void* wscales, const uint16_t* lora_up,

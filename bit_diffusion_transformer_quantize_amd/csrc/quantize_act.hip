@@ -86,7 +86,48 @@ struct QaImage {
   int64_t RT;
   size_t scale, lr, tpart;
   int S;
+  int gelu;  // the layer's input is bf16_RNE(GELU_tanh(X))
 };
+
+// GELU with the tanh approximation in the cancellation-free form
+//   GELU(x) = x / (1 + e^z),  z = -2 sqrt(2/pi) (x + 0.044715 x^3)
+// (0.5 (1 + tanh y) = 1 / (1 + e^-2y)), every step one IEEE fp32 operation
+// (the library is built without contraction), so that the bf16 rounding of
+// the result, which decides the 4-bit codes, is reproducible.  e^z uses Cody
+// and Waite's reduction z = k ln2 + r with ln 2 split as 0.693359375 (10
+// significant bits, so k * 0.693359375 is exact) plus the fp32 remainder, a
+// degree-7 Taylor polynomial of e^r in Horner form and exact scaling by 2^k;
+// z is clamped to [-104, 104], where e^z is already 0 or inf in fp32.
+__device__ __forceinline__ float gelu_tanh_rn(float x) {
+  constexpr double kLn2 = 0.69314718055994530942;
+  constexpr float kA = (float)0.044715;
+  const float kB = (float)(-2.0 * __builtin_sqrt(2.0 / 3.14159265358979323846));
+  constexpr float kL = (float)(1.0 / kLn2);
+  constexpr float kC1 = 0.693359375f;
+  constexpr float kC2 = (float)(kLn2 - 0.693359375);
+  const float x3 = (x * x) * x;
+  const float u = x + kA * x3;
+  const float z = fminf(fmaxf(kB * u, -104.0f), 104.0f);
+  const float k = __builtin_rintf(z * kL);
+  const float r = (z - k * kC1) - k * kC2;
+  float p = (float)(1.0 / 5040.0);
+  p = p * r + (float)(1.0 / 720.0);
+  p = p * r + (float)(1.0 / 120.0);
+  p = p * r + (float)(1.0 / 24.0);
+  p = p * r + (float)(1.0 / 6.0);
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  const float e = __builtin_ldexpf(p, (int)k);
+  return x / (1.0f + e);
+}
+
+// Two packed bf16 inputs -> two packed bf16_RNE(GELU(x)).
+__device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w) {
+  const float a = gelu_tanh_rn(bf16_to_f32(w & 0xFFFFu));
+  const float b = gelu_tanh_rn(bf16_to_f32(w >> 16));
+  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
 
 // MODE 0 = INT4, 1 = FP4.  RB = rank / 16 (0 = no down-projection).
 // CODES = false skips the quantizer (stand-alone down-projection).
@@ -139,7 +180,11 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       load_x(t + QA_WAVES, na, nb);  // next tile of this wave
       const int kl = t * 64 + j * 16;  // column within the chunk
       const int k0 = kc + kl;          // column within the row
-      const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+      uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+      if (qi.gelu) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xw[i] = gelu_bf16x2(xw[i]);
+      }
 
       // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
       uint32_t hb[16];
@@ -389,12 +434,12 @@ size_t act_image_bytes(int mode, int64_t M, int K, int rank) {
 hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down,
                                uint8_t* xcodes, void* xscales, float* T, void* ximage,
-                               hipStream_t s) {
-  QaImage qi{nullptr, 0, 0, 0, 0, 1};
+                               bool gelu, hipStream_t s) {
+  QaImage qi{nullptr, 0, 0, 0, 0, 1, gelu ? 1 : 0};
   int64_t rows = M;
   if (ximage != nullptr) {
     const ActImage a = act_image(mode, M, K, rank);
-    qi = QaImage{reinterpret_cast<uint8_t*>(ximage), a.RT, a.scale, a.lr, a.tpart, a.S};
+    qi = QaImage{reinterpret_cast<uint8_t*>(ximage), a.RT, a.scale, a.lr, a.tpart, a.S, gelu ? 1 : 0};
     rows = a.RT * 32;  // cover the padding rows too
   }
   const int rb = lora_down ? rank / 16 : 0;
@@ -412,10 +457,10 @@ hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint1
 
 hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down, float* T,
-                               hipStream_t s) {
+                               bool gelu, hipStream_t s) {
   const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
   return launch_qa_rank<0, false>(rank / 16, grid, s, M, K, X, lambda, lora_down, nullptr,
-                                  nullptr, T, QaImage{nullptr, 0, 0, 0, 0, 1});
+                                  nullptr, T, QaImage{nullptr, 0, 0, 0, 0, 1, gelu ? 1 : 0});
 }
 
 }  // namespace svdq

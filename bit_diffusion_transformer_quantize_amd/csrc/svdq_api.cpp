@@ -19,7 +19,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 svdq_status check_desc(const svdq_desc* d) {
   if (d == nullptr) return SVDQ_ERR_ARG;
   if (d->mode != SVDQ_MODE_INT4 && d->mode != SVDQ_MODE_FP4) return SVDQ_ERR_ARG;
-  if ((d->flags & ~SVDQ_FLAG_OUT_F32) != 0u) return SVDQ_ERR_ARG;
+  if ((d->flags & ~(SVDQ_FLAG_OUT_F32 | SVDQ_FLAG_GELU_IN)) != 0u) return SVDQ_ERR_ARG;
   if (d->K <= 0 || d->K % 128 != 0 || d->K > (1 << 20)) return SVDQ_ERR_SHAPE;
   if (d->N <= 0 || d->N % 128 != 0 || d->N > (1 << 20)) return SVDQ_ERR_SHAPE;
   if (d->rank < 0 || d->rank > 256 || d->rank % 16 != 0) return SVDQ_ERR_SHAPE;
@@ -148,7 +148,9 @@ svdq_status svdq_quantize_act(const svdq_desc* d, int64_t M, const uint16_t* X,
   }
   SVDQ_TRY(check_device());
   return from_hip(svdq::launch_quantize_act(d->mode, d->rank, M, d->K, X, lambda, lora_down,
-                                            xcodes, xscales, T, ximage, (hipStream_t)stream));
+                                            xcodes, xscales, T, ximage,
+                                            (d->flags & SVDQ_FLAG_GELU_IN) != 0u,
+                                            (hipStream_t)stream));
 }
 
 svdq_status svdq_weight_image_size(const svdq_desc* d, size_t* bytes) {
@@ -194,6 +196,7 @@ svdq_status svdq_lowrank_down(const svdq_desc* d, int64_t M, const uint16_t* X,
   if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(lora_down) || !ptr_ok(T)) return SVDQ_ERR_ARG;
   SVDQ_TRY(check_device());
   return from_hip(svdq::launch_lowrank_down(d->rank, M, d->K, X, lambda, lora_down, T,
+                                            (d->flags & SVDQ_FLAG_GELU_IN) != 0u,
                                             (hipStream_t)stream));
 }
 

@@ -23,6 +23,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "svdq.h")
 SVDQ_MODE_INT4 = 0
 SVDQ_MODE_FP4 = 1
 SVDQ_FLAG_OUT_F32 = 0x1
+SVDQ_FLAG_GELU_IN = 0x2
 MODES = {"int4": SVDQ_MODE_INT4, "fp4": SVDQ_MODE_FP4}
 STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_ARG", 2: "SVDQ_ERR_SHAPE", 3: "SVDQ_ERR_ARCH",
           4: "SVDQ_ERR_HIP"}
@@ -87,9 +88,10 @@ def header_symbols() -> list:
     return sorted(set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", text)))
 
 
-def desc(mode, K: int, N: int, rank: int, out_f32: bool = False) -> SvdqDesc:
+def desc(mode, K: int, N: int, rank: int, out_f32: bool = False, gelu_in: bool = False) -> SvdqDesc:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
-    return SvdqDesc(m, K, N, rank, SVDQ_FLAG_OUT_F32 if out_f32 else 0)
+    flags = (SVDQ_FLAG_OUT_F32 if out_f32 else 0) | (SVDQ_FLAG_GELU_IN if gelu_in else 0)
+    return SvdqDesc(m, K, N, rank, flags)
 
 
 def _p(t: Optional[torch.Tensor]):

@@ -77,6 +77,21 @@ typedef enum {
 /* Y is written as float32 instead of bf16. */
 #define SVDQ_FLAG_OUT_F32 0x1u
 
+/* The layer's input is GELU(X) with the tanh approximation, applied to the
+ * bf16 X that svdq_quantize_act and svdq_lowrank_down read: the down
+ * projection of a transformer MLP reading the up projection's output (the
+ * FLUX MLP: up-projection, GELU(tanh), down-projection), with the GELU fused
+ * into the activation pass instead of a pass of its own.  Per element, in
+ * IEEE fp32 without fused multiply-add:
+ *   z = clamp(B * (x + A * ((x * x) * x)), -104, 104),
+ *       A = fp32(0.044715), B = fp32(-2 sqrt(2/pi));
+ *   e^z: k = rint(z * fp32(1/ln 2)), r = (z - k * 0.693359375) - k * fp32(ln 2 - 0.693359375),
+ *        p = Horner form of sum_{n=0..7} r^n / n! (each 1/n! rounded to fp32,
+ *        innermost first), e^z = p * 2^k;
+ *   GELU(x) = x / (1 + e^z), rounded to bf16 (RNE) before smoothing.
+ * svdq_linear_forward ignores the flag. */
+#define SVDQ_FLAG_GELU_IN 0x2u
+
 /* Static description of one quantized linear layer. */
 typedef struct {
   int32_t mode;   /* svdq_mode                                   */

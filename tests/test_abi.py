@@ -115,7 +115,7 @@ def test_prepare_weight_validation():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(mode=2), ARG), (dict(mode=-1), ARG), (dict(flags=2), ARG),
+    (dict(mode=2), ARG), (dict(mode=-1), ARG), (dict(flags=4), ARG),
     (dict(K=0), SHAPE), (dict(K=64), SHAPE), (dict(K=100), SHAPE), (dict(K=1 << 21), SHAPE),
     (dict(N=0), SHAPE), (dict(N=64), SHAPE), (dict(N=200), SHAPE),
     (dict(rank=8), SHAPE), (dict(rank=-16), SHAPE), (dict(rank=272), SHAPE),
