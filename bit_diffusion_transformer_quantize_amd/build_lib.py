@@ -26,6 +26,7 @@ SOURCES = ["svdq_api.cpp", "quantize_act.hip", "pack_weight.hip", "images.hip", 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     "-ffp-contract=off",
+    "-fconstexpr-steps=50000000",  # the GELU table is evaluated at compile time
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",

@@ -86,29 +86,73 @@ struct QaImage {
   int64_t RT;
   size_t scale, lr, tpart;
   int S;
-  int gelu;  // the layer's input is bf16_RNE(GELU_tanh(X))
 };
 
 // GELU with the tanh approximation in the cancellation-free form
 //   GELU(x) = x / (1 + e^z),  z = -2 sqrt(2/pi) (x + 0.044715 x^3)
 // (0.5 (1 + tanh y) = 1 / (1 + e^-2y)), every step one IEEE fp32 operation
-// (the library is built without contraction), so that the bf16 rounding of
-// the result, which decides the 4-bit codes, is reproducible.  e^z uses Cody
-// and Waite's reduction z = k ln2 + r with ln 2 split as 0.693359375 (10
-// significant bits, so k * 0.693359375 is exact) plus the fp32 remainder, a
-// degree-7 Taylor polynomial of e^r in Horner form and exact scaling by 2^k;
-// z is clamped to [-104, 104], where e^z is already 0 or inf in fp32.
-__device__ __forceinline__ float gelu_tanh_rn(float x) {
-  constexpr double kLn2 = 0.69314718055994530942;
-  constexpr float kA = (float)0.044715;
-  const float kB = (float)(-2.0 * __builtin_sqrt(2.0 / 3.14159265358979323846));
-  constexpr float kL = (float)(1.0 / kLn2);
-  constexpr float kC1 = 0.693359375f;
-  constexpr float kC2 = (float)(kLn2 - 0.693359375);
+// with round-to-nearest-even and no fused multiply-add, so that the bf16
+// rounding of the result, which decides the 4-bit codes, is reproducible.
+// e^z uses Cody and Waite's reduction z = k ln2 + r with ln 2 split as
+// 0.693359375 (10 significant bits, so k * 0.693359375 is exact) plus the
+// fp32 remainder, a degree-7 Taylor polynomial of e^r in Horner form and
+// exact scaling by 2^k; z is clamped to [-104, 104].
+//
+// The input is bf16, so the function has 65536 arguments: the table below
+// holds bf16_RNE(GELU(x)) for every bf16 bit pattern, evaluated by the
+// compiler's constant evaluator, whose float arithmetic is IEEE with
+// round-to-nearest-even, one rounding per operation.  Constant evaluation
+// admits no infinities, so the two places where the fp32 sequence overflows
+// take their results directly: x^3 overflows only when |x| > 2^42, where
+// z is clamped to -104 (x > 0: e^z = 0 in fp32, GELU = x) or to +104
+// (x < 0: e^z = inf, GELU = -0); and p 2^k rounds to inf in fp32 exactly
+// when it reaches 2^128 - 2^103, where GELU = x / inf = -0 (z > 0 there, so
+// x < 0).  Inf and NaN inputs map to themselves.
+namespace gelu_table {
+
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr float kA = (float)0.044715;
+constexpr float kC1 = 0.693359375f;
+constexpr float kC2 = (float)(kLn2 - 0.693359375);
+constexpr float kL = (float)(1.0 / kLn2);
+
+constexpr double csqrt(double v) {  // Newton's iteration to the correctly rounded root
+  double r = v > 1.0 ? v : 1.0;
+  for (int i = 0; i < 200; ++i) r = 0.5 * (r + v / r);
+  // the iteration settles within one ulp; step to the root whose square is closest
+  for (int i = 0; i < 4; ++i) {
+    const double lo = r - r * 0x1p-53, hi = r + r * 0x1p-52;
+    const double e0 = r * r - v, el = lo * lo - v, eh = hi * hi - v;
+    const double a0 = e0 < 0 ? -e0 : e0, al = el < 0 ? -el : el, ah = eh < 0 ? -eh : eh;
+    r = al < a0 ? lo : (ah < a0 ? hi : r);
+  }
+  return r;
+}
+constexpr float kB = (float)(-2.0 * csqrt(2.0 / 3.14159265358979323846));
+
+constexpr float rint_even(float v) {  // round to an integer, ties to even (|v| < 2^23)
+  const float a = v < 0 ? -v : v;
+  const float t = (a + 8388608.0f) - 8388608.0f;
+  return v < 0 ? -t : t;
+}
+constexpr double pow2(int k) {  // 2^k for -1022 <= k <= 1023, from its exponent field
+  return __builtin_bit_cast(double, (uint64_t)(k + 1023) << 52);
+}
+constexpr uint16_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+constexpr uint16_t entry(uint32_t xb) {
+  if ((xb & 0x7F80u) == 0x7F80u) return (uint16_t)xb;           // inf, NaN
+  const float x = __builtin_bit_cast(float, xb << 16);
+  const float ax = x < 0 ? -x : x;
+  if (ax > 0x1p42f) return x > 0 ? (uint16_t)xb : (uint16_t)0x8000u;
   const float x3 = (x * x) * x;
   const float u = x + kA * x3;
-  const float z = fminf(fmaxf(kB * u, -104.0f), 104.0f);
-  const float k = __builtin_rintf(z * kL);
+  float z = kB * u;
+  z = z < -104.0f ? -104.0f : (z > 104.0f ? 104.0f : z);
+  const float k = rint_even(z * kL);
   const float r = (z - k * kC1) - k * kC2;
   float p = (float)(1.0 / 5040.0);
   p = p * r + (float)(1.0 / 720.0);
@@ -118,20 +162,82 @@ __device__ __forceinline__ float gelu_tanh_rn(float x) {
   p = p * r + 0.5f;
   p = p * r + 1.0f;
   p = p * r + 1.0f;
-  const float e = __builtin_ldexpf(p, (int)k);
-  return x / (1.0f + e);
+  const double v = (double)p * pow2((int)k);                  // exact
+  if (v >= 0x1p128 - 0x1p103) return (uint16_t)0x8000u;       // e^z = inf, x < 0
+  const float e = (float)v;                                   // one rounding
+  return bf16_rne(x / (1.0f + e));
+}
+// Outside a band of exponents the bf16 GELU follows two rules, checked
+// against the full definition for all 65536 inputs below: |x| < 2^-10 gives
+// bf16_RNE(x / 2) (there e^z = 1 - 1.6 x + ..., so x / (1 + e^z) is within
+// 2^-10 of x / 2, inside half a bf16 ulp), and |x| >= 32 gives x for
+// positive x and -0 for negative x (inf and NaN map to themselves).  Only the
+// 15 binades in between (biased exponents 117..131, both signs: 3840
+// entries) are tabulated.
+constexpr int kLoExp = 117, kHiExp = 131;
+constexpr int kBand = kHiExp - kLoExp + 1;
+constexpr int kEntries = 2 * kBand * 128;
+
+constexpr uint16_t half_rule(uint32_t xb) {
+  return bf16_rne(__builtin_bit_cast(float, xb << 16) * 0.5f);
+}
+constexpr uint16_t rule(uint32_t xb) {  // inputs outside the band
+  const uint32_t e = (xb >> 7) & 0xFFu;
+  if (e < (uint32_t)kLoExp) return half_rule(xb);
+  if (e == 0xFFu || (xb & 0x8000u) == 0) return (uint16_t)xb;
+  return (uint16_t)0x8000u;
+}
+constexpr int band_index(uint32_t xb) {
+  return (int)((xb >> 15) * kBand + (((xb >> 7) & 0xFFu) - kLoExp)) * 128 + (int)(xb & 0x7Fu);
+}
+constexpr bool rules_hold() {
+  for (uint32_t i = 0; i < 65536; ++i) {
+    const uint32_t e = (i >> 7) & 0xFFu;
+    if ((e < (uint32_t)kLoExp || e > (uint32_t)kHiExp) && rule(i) != entry(i)) return false;
+  }
+  return true;
+}
+static_assert(rules_hold(), "the GELU rules outside the tabulated band");
+
+struct Table {
+  uint16_t v[kEntries];
+};
+constexpr Table make() {
+  Table t{};
+  for (uint32_t s = 0; s < 2; ++s)
+    for (uint32_t e = kLoExp; e <= (uint32_t)kHiExp; ++e)
+      for (uint32_t m = 0; m < 128; ++m) {
+        const uint32_t xb = (s << 15) | (e << 7) | m;
+        t.v[band_index(xb)] = entry(xb);
+      }
+  return t;
 }
 
-// Two packed bf16 inputs -> two packed bf16_RNE(GELU(x)).
-__device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w) {
-  const float a = gelu_tanh_rn(bf16_to_f32(w & 0xFFFFu));
-  const float b = gelu_tanh_rn(bf16_to_f32(w >> 16));
-  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}  // namespace gelu_table
+
+__device__ constexpr gelu_table::Table kGeluBand = gelu_table::make();
+
+// bf16 GELU of one input (low 16 bits of b) from the band table in LDS and
+// the two rules.  Branch-free: the table index is clamped into range.
+__device__ __forceinline__ uint32_t gelu_one(uint32_t b, const uint16_t* tab) {
+  using namespace gelu_table;
+  const uint32_t e = (b >> 7) & 0xFFu;
+  const bool in_band = e >= (uint32_t)kLoExp && e <= (uint32_t)kHiExp;
+  const uint32_t ec = in_band ? e : (uint32_t)kLoExp;
+  const uint32_t idx = ((b >> 15) * kBand + (ec - kLoExp)) * 128 + (b & 0x7Fu);
+  const uint32_t t = tab[idx];
+  const uint32_t half = f32_to_bf16(__uint_as_float(b << 16) * 0.5f);
+  const uint32_t big = (e == 0xFFu || (b & 0x8000u) == 0) ? b : 0x8000u;
+  return in_band ? t : (e < (uint32_t)kLoExp ? half : big);
+}
+
+__device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w, const uint16_t* tab) {
+  return gelu_one(w & 0xFFFFu, tab) | (gelu_one(w >> 16, tab) << 16);
 }
 
 // MODE 0 = INT4, 1 = FP4.  RB = rank / 16 (0 = no down-projection).
 // CODES = false skips the quantizer (stand-alone down-projection).
-template <int MODE, int RB, bool CODES>
+template <int MODE, int RB, bool CODES, bool GELU>
 __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_kernel(
     int64_t M, int K, const uint16_t* __restrict__ X, const float* __restrict__ lambda,
     const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ xcodes,
@@ -140,6 +246,13 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   constexpr int QA_THREADS = QaShape<MODE, RB>::kThreads;
   __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<MODE, RB>::kBytes];
   double* rlam = reinterpret_cast<double*>(smem);
+  // the GELU band table (7.5 KB), copied once; the first chunk's barrier
+  // orders the copy before any lookup
+  __shared__ uint16_t gtab[GELU ? gelu_table::kEntries : 2];
+  if constexpr (GELU) {
+    for (int i = threadIdx.x; i < gelu_table::kEntries / 2; i += QA_THREADS)
+      reinterpret_cast<uint32_t*>(gtab)[i] = reinterpret_cast<const uint32_t*>(kGeluBand.v)[i];
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -164,27 +277,30 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
     for (int c = threadIdx.x; c < kn; c += QA_THREADS) rlam[c] = 1.0 / (double)lambda[kc + c];
     __syncthreads();
     const int ntiles = kn >> 6;
-    auto load_x = [&](int t, v4u& xa, v4u& xb) {
-      xa = v4u{0u, 0u, 0u, 0u};
-      xb = v4u{0u, 0u, 0u, 0u};
-      if (row_ok && t < ntiles) {
-        const uint16_t* p = xrow + kc + t * 64 + j * 16;
-        xa = *reinterpret_cast<const v4u*>(p);
-        xb = *reinterpret_cast<const v4u*>(p + 8);
-      }
+    // Loads of a tile without a branch (rows past M and tiles past the chunk
+    // read a valid place; the flag zeroes them when the tile is used), so
+    // that the compiler's wait counts stay exact across the loop.
+    auto load_x = [&](int t, v4u& xa, v4u& xb, bool& ok) {
+      ok = row_ok && t < ntiles;
+      const int tc = t < ntiles ? t : ntiles - 1;
+      const uint16_t* p = xrow + kc + tc * 64 + j * 16;
+      xa = *reinterpret_cast<const v4u*>(p);
+      xb = *reinterpret_cast<const v4u*>(p + 8);
     };
     v4u na, nb;
-    load_x(wave, na, nb);
+    bool nok;
+    load_x(wave, na, nb, nok);
     for (int t = wave; t < ntiles; t += QA_WAVES) {
-      const v4u xa = na, xb = nb;
-      load_x(t + QA_WAVES, na, nb);  // next tile of this wave
+      const v4u zero4 = v4u{0u, 0u, 0u, 0u};
+      const v4u xa = nok ? na : zero4, xb = nok ? nb : zero4;
+      uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+      load_x(t + QA_WAVES, na, nb, nok);  // next tile of this wave
+      if constexpr (GELU) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xw[i] = gelu_bf16x2(xw[i], gtab);
+      }
       const int kl = t * 64 + j * 16;  // column within the chunk
       const int k0 = kc + kl;          // column within the row
-      uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
-      if (qi.gelu) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xw[i] = gelu_bf16x2(xw[i]);
-      }
 
       // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
       uint32_t hb[16];
@@ -406,13 +522,13 @@ __global__ __launch_bounds__(256) void split_t_kernel(int64_t M, int rank, float
   *reinterpret_cast<v4u*>(blk + 1024 + 16 * slot) = v4u{lo[0], lo[1], lo[2], lo[3]};
 }
 
-template <int MODE, bool CODES>
+template <int MODE, bool CODES, bool GELU>
 static hipError_t launch_qa_rank(int rb, dim3 grid, hipStream_t s, int64_t M, int K,
                                  const uint16_t* X, const float* lam, const uint16_t* ld,
                                  uint8_t* xc, void* xs, float* T, QaImage qi) {
 #define SVDQ_QA_CASE(R)                                                                   \
   case R:                                                                                 \
-    hipLaunchKernelGGL((quantize_act_kernel<MODE, R, CODES>), grid, dim3(QaShape<MODE, R>::kThreads), 0, \
+    hipLaunchKernelGGL((quantize_act_kernel<MODE, R, CODES, GELU>), grid, dim3(QaShape<MODE, R>::kThreads), 0, \
                        s, M, K, X, lam, ld, xc, xs, T, qi);                               \
     break;
   switch (rb) {
@@ -435,19 +551,26 @@ hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint1
                                const float* lambda, const uint16_t* lora_down,
                                uint8_t* xcodes, void* xscales, float* T, void* ximage,
                                bool gelu, hipStream_t s) {
-  QaImage qi{nullptr, 0, 0, 0, 0, 1, gelu ? 1 : 0};
+  QaImage qi{nullptr, 0, 0, 0, 0, 1};
   int64_t rows = M;
   if (ximage != nullptr) {
     const ActImage a = act_image(mode, M, K, rank);
-    qi = QaImage{reinterpret_cast<uint8_t*>(ximage), a.RT, a.scale, a.lr, a.tpart, a.S, gelu ? 1 : 0};
+    qi = QaImage{reinterpret_cast<uint8_t*>(ximage), a.RT, a.scale, a.lr, a.tpart, a.S};
     rows = a.RT * 32;  // cover the padding rows too
   }
   const int rb = lora_down ? rank / 16 : 0;
   const dim3 grid((unsigned)((rows + QA_ROWS - 1) / QA_ROWS), (unsigned)qi.S);
-  hipError_t e = mode == 0 ? launch_qa_rank<0, true>(rb, grid, s, M, K, X, lambda, lora_down,
-                                                     xcodes, xscales, T, qi)
-                           : launch_qa_rank<1, true>(rb, grid, s, M, K, X, lambda, lora_down,
-                                                     xcodes, xscales, T, qi);
+  hipError_t e;
+  if (mode == 0)
+    e = gelu ? launch_qa_rank<0, true, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+                                             xscales, T, qi)
+             : launch_qa_rank<0, true, false>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+                                              xscales, T, qi);
+  else
+    e = gelu ? launch_qa_rank<1, true, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+                                             xscales, T, qi)
+             : launch_qa_rank<1, true, false>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+                                              xscales, T, qi);
   if (e != hipSuccess || rb == 0 || qi.S <= 1) return e;
   const int64_t n = qi.RT * 32 * (rank / 8);
   hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, M, rank,
@@ -459,8 +582,11 @@ hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down, float* T,
                                bool gelu, hipStream_t s) {
   const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
-  return launch_qa_rank<0, false>(rank / 16, grid, s, M, K, X, lambda, lora_down, nullptr,
-                                  nullptr, T, QaImage{nullptr, 0, 0, 0, 0, 1, gelu ? 1 : 0});
+  const QaImage qi{nullptr, 0, 0, 0, 0, 1};
+  return gelu ? launch_qa_rank<0, false, true>(rank / 16, grid, s, M, K, X, lambda, lora_down,
+                                               nullptr, nullptr, T, qi)
+              : launch_qa_rank<0, false, false>(rank / 16, grid, s, M, K, X, lambda, lora_down,
+                                                nullptr, nullptr, T, qi);
 }
 
 }  // namespace svdq
