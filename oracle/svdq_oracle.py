@@ -59,7 +59,8 @@ FP4_BLOCK = 32
 E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
 
 __all__ = [
-    "bf16_to_f32", "f32_to_bf16", "calibrate_lambda", "smooth_weight",
+    "bf16_to_f32", "f32_to_bf16", "calibrate_lambda", "column_absmax", "lambda_from_absmax",
+    "smooth_weight",
     "lowrank_factors", "residual", "quantize_int4", "quantize_fp4",
     "pack_nibbles", "unpack_nibbles", "decode_int4", "decode_fp4",
     "pack_weight", "smooth_act", "quantize_act", "forward", "forward_dequant",
@@ -92,6 +93,24 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
 # Offline side: smoothing factor, smoothed weight, SVD branch, residual
 # [Apatero, "O que e Nunchaku"]; [Axbrief, "Mechanics"]
 # --------------------------------------------------------------------------
+def column_absmax(A_bf16: np.ndarray, prev=None) -> np.ndarray:
+    """max_m |A[m, j]| per column (fp32, exact), combined with a previous
+    running maximum when given: the statistic calibration keeps over many
+    batches of activations."""
+    a = np.abs(bf16_to_f32(A_bf16)).max(axis=0).astype(np.float32)
+    return a if prev is None else np.maximum(a, np.asarray(prev, np.float32))
+
+
+def lambda_from_absmax(ax: np.ndarray, aw: np.ndarray) -> np.ndarray:
+    """lambda_j = fp32(sqrt(fp64(ax_j) / fp64(aw_j))), 1 where either is 0."""
+    ax = np.asarray(ax, np.float64)
+    aw = np.asarray(aw, np.float64)
+    ok = (ax > 0) & (aw > 0)
+    lam = np.ones(ax.shape, dtype=np.float32)
+    lam[ok] = np.sqrt(ax[ok] / aw[ok]).astype(np.float32)
+    return lam
+
+
 def calibrate_lambda(X_bf16: np.ndarray, W_bf16: np.ndarray) -> np.ndarray:
     """Per-input-channel smoothing factor (alpha = 1/2).
 
@@ -101,12 +120,7 @@ def calibrate_lambda(X_bf16: np.ndarray, W_bf16: np.ndarray) -> np.ndarray:
     moves magnitude from activation channels into weight columns while
     leaving X W^T unchanged.
     """
-    ax = np.abs(bf16_to_f32(X_bf16)).max(axis=0).astype(np.float64)
-    aw = np.abs(bf16_to_f32(W_bf16)).max(axis=0).astype(np.float64)
-    ok = (ax > 0) & (aw > 0)
-    lam = np.ones(ax.shape, dtype=np.float32)
-    lam[ok] = np.sqrt(ax[ok] / aw[ok]).astype(np.float32)
-    return lam
+    return lambda_from_absmax(column_absmax(X_bf16), column_absmax(W_bf16))
 
 
 def smooth_weight(W_bf16: np.ndarray, lam: np.ndarray) -> np.ndarray:
