@@ -11,6 +11,13 @@ namespace svdq {
 hipError_t launch_calibrate_lambda(int64_t M, int K, int N, const uint16_t* X,
                                    const uint16_t* W, float* lambda, hipStream_t s);
 
+// Per-column absolute maxima of a bf16 [R][K] matrix, optionally combined
+// with amax; lambda from two such maxima.
+hipError_t launch_column_absmax(int64_t R, int K, const uint16_t* A, float* amax, bool accumulate,
+                                hipStream_t s);
+hipError_t launch_lambda_from_absmax(int K, const float* xmax, const float* wmax, float* lambda,
+                                     hipStream_t s);
+
 hipError_t launch_pack_weight(int mode, int rank, int N, int K, const uint16_t* W,
                               const float* lambda, const uint16_t* lora_down,
                               const uint16_t* lora_up, uint8_t* wcodes, void* wscales,

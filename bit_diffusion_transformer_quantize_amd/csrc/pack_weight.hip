@@ -14,36 +14,104 @@
 namespace svdq {
 
 // ---------------------------------------------------------------- lambda
-// One workgroup per 64 columns: its four waves stride over the rows of X and
-// of W, lane l owning column c0 + l (128 contiguous bytes per row and wave).
-constexpr int CAL_THREADS = 256;
+// Per-column absolute maxima, one workgroup per 64 columns (so the maxima of
+// a column never leave the workgroup and no scratch memory is needed).  Its
+// 16 waves stride over the rows: lane l reads 16 bytes (8 columns) of row
+// 8 wave + l/8 (+ 128 i), so a wave-wide load covers 8 rows x 64 columns.
+// The 8 lanes of a column chunk combine by shuffles, the waves through LDS.
+// A maximum is exact in any order.
+constexpr int CAL_WAVES = 16;
+constexpr int CAL_THREADS = 64 * CAL_WAVES;
+
+// Maxima of |A[r][c0 .. c0+63]| over all rows; the result for column c0 + i
+// is returned by thread i (i < 64) of the workgroup, 0 for the others.
+__device__ float colmax64(int64_t R, int K, const uint16_t* __restrict__ A, int c0,
+                          float (*red)[64]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cl = (lane & 7) * 8;
+  float m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = 0.f;
+  const uint16_t* base = A + c0 + cl;
+#pragma unroll 4
+  for (int64_t r = wave * 8 + (lane >> 3); r < R; r += 8 * CAL_WAVES) {
+    const v4u v = *reinterpret_cast<const v4u*>(base + r * K);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[2 * e] = fmaxf(m[2 * e], fabsf(bf16_to_f32(v[e] & 0xFFFFu)));
+      m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(bf16_to_f32(v[e] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    m[e] = fmaxf(m[e], __shfl_xor(m[e], 8, 64));
+    m[e] = fmaxf(m[e], __shfl_xor(m[e], 16, 64));
+    m[e] = fmaxf(m[e], __shfl_xor(m[e], 32, 64));
+  }
+  __syncthreads();  // red may still be read by a previous call
+  if (lane < 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][cl + e] = m[e];
+  }
+  __syncthreads();
+  float out = 0.f;
+  if (threadIdx.x < 64) {
+    for (int w = 0; w < CAL_WAVES; ++w) out = fmaxf(out, red[w][threadIdx.x]);
+  }
+  return out;
+}
+
+__device__ __forceinline__ float lambda_of(float ax, float aw) {
+  return (ax > 0.f && aw > 0.f) ? (float)__builtin_sqrt((double)ax / (double)aw) : 1.0f;
+}
 
 __global__ __launch_bounds__(CAL_THREADS) void calibrate_lambda_kernel(
     int64_t M, int K, int N, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     float* __restrict__ lambda) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + lane;
-  float ax = 0.f, aw = 0.f;
-  for (int64_t m = wave; m < M; m += 4) ax = fmaxf(ax, fabsf(bf16_to_f32(X[m * K + c])));
-  for (int64_t n = wave; n < N; n += 4) aw = fmaxf(aw, fabsf(bf16_to_f32(W[n * K + c])));
-  __shared__ float sx[4][64], sw[4][64];
-  sx[wave][lane] = ax;
-  sw[wave][lane] = aw;
-  __syncthreads();
-  if (wave == 0) {
-    ax = fmaxf(fmaxf(sx[0][lane], sx[1][lane]), fmaxf(sx[2][lane], sx[3][lane]));
-    aw = fmaxf(fmaxf(sw[0][lane], sw[1][lane]), fmaxf(sw[2][lane], sw[3][lane]));
-    float lam = 1.0f;
-    if (ax > 0.f && aw > 0.f) lam = (float)__builtin_sqrt((double)ax / (double)aw);
-    lambda[c] = lam;
+  __shared__ float red[CAL_WAVES][64];
+  const int c0 = blockIdx.x * 64;
+  const float ax = colmax64(M, K, X, c0, red);
+  const float aw = colmax64(N, K, W, c0, red);
+  if (threadIdx.x < 64) lambda[c0 + threadIdx.x] = lambda_of(ax, aw);
+}
+
+__global__ __launch_bounds__(CAL_THREADS) void column_absmax_kernel(
+    int64_t R, int K, const uint16_t* __restrict__ A, float* __restrict__ amax, int accumulate) {
+  __shared__ float red[CAL_WAVES][64];
+  const int c0 = blockIdx.x * 64;
+  const float a = colmax64(R, K, A, c0, red);
+  if (threadIdx.x < 64) {
+    const int c = c0 + threadIdx.x;
+    amax[c] = accumulate ? fmaxf(amax[c], a) : a;
   }
+}
+
+__global__ __launch_bounds__(256) void lambda_from_absmax_kernel(int K, const float* __restrict__ xmax,
+                                                                 const float* __restrict__ wmax,
+                                                                 float* __restrict__ lambda) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < K) lambda[c] = lambda_of(xmax[c], wmax[c]);
 }
 
 hipError_t launch_calibrate_lambda(int64_t M, int K, int N, const uint16_t* X,
                                    const uint16_t* W, float* lambda, hipStream_t s) {
   hipLaunchKernelGGL(calibrate_lambda_kernel, dim3(K / 64), dim3(CAL_THREADS), 0, s, M, K, N,
                      X, W, lambda);
+  return hipGetLastError();
+}
+
+hipError_t launch_column_absmax(int64_t R, int K, const uint16_t* A, float* amax, bool accumulate,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(column_absmax_kernel, dim3(K / 64), dim3(CAL_THREADS), 0, s, R, K, A, amax,
+                     accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_lambda_from_absmax(int K, const float* xmax, const float* wmax, float* lambda,
+                                     hipStream_t s) {
+  hipLaunchKernelGGL(lambda_from_absmax_kernel, dim3((K + 255) / 256), dim3(256), 0, s, K, xmax,
+                     wmax, lambda);
   return hipGetLastError();
 }
 

@@ -107,6 +107,23 @@ svdq_status svdq_calibrate_lambda(int64_t M, int32_t K, int32_t N, const uint16_
   return from_hip(svdq::launch_calibrate_lambda(M, K, N, X, W, lambda, (hipStream_t)stream));
 }
 
+svdq_status svdq_calibrate_absmax(int64_t R, int32_t K, const uint16_t* A, float* amax,
+                                  int32_t accumulate, void* stream) {
+  if (!ptr_ok(A) || !ptr_ok(amax)) return SVDQ_ERR_ARG;
+  if (accumulate != 0 && accumulate != 1) return SVDQ_ERR_ARG;
+  if (R < 1 || R > (int64_t(1) << 31) || K <= 0 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_column_absmax(R, K, A, amax, accumulate != 0, (hipStream_t)stream));
+}
+
+svdq_status svdq_lambda_from_absmax(int32_t K, const float* xmax, const float* wmax, float* lambda,
+                                    void* stream) {
+  if (!ptr_ok(xmax) || !ptr_ok(wmax) || !ptr_ok(lambda)) return SVDQ_ERR_ARG;
+  if (K <= 0 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_lambda_from_absmax(K, xmax, wmax, lambda, (hipStream_t)stream));
+}
+
 svdq_status svdq_pack_weight(const svdq_desc* d, const uint16_t* W, const float* lambda,
                              const uint16_t* lora_down, const uint16_t* lora_up,
                              uint8_t* wcodes, void* wscales, void* stream) {

@@ -50,6 +50,8 @@ _SIGNATURES = {
     "svdq_arch_supported": (ctypes.c_int, [ctypes.c_char_p]),
     "svdq_version": (ctypes.c_char_p, []),
     "svdq_calibrate_lambda": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "svdq_calibrate_absmax": (ctypes.c_int, [_i64, _i32, _vp, _vp, _i32, _vp]),
+    "svdq_lambda_from_absmax": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp]),
     "svdq_pack_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "svdq_act_image_size": (ctypes.c_int, [_DESC, _i64, ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_weight_image_size": (ctypes.c_int, [_DESC, ctypes.POINTER(ctypes.c_size_t)]),
@@ -154,6 +156,33 @@ def svdq_calibrate_lambda(X: torch.Tensor, W: torch.Tensor, lam: Optional[torch.
     _need(lam, "lambda", torch.float32, (K,))
     _check("svdq_calibrate_lambda",
            load().svdq_calibrate_lambda(M, K, N, _p(X), _p(W), _p(lam), _stream()))
+    return lam
+
+
+def svdq_calibrate_absmax(A, amax=None, accumulate: bool = False):
+    """Per-column absolute maximum of a bf16 matrix, combined with amax when
+    accumulate (the running statistic over calibration batches)."""
+    R, K = A.shape
+    _need(A, "A", torch.bfloat16, (R, K))
+    if amax is None:
+        if accumulate:
+            raise ValueError("accumulate needs amax")
+        amax = torch.empty(K, dtype=torch.float32, device=A.device)
+    _need(amax, "amax", torch.float32, (K,))
+    _check("svdq_calibrate_absmax",
+           load().svdq_calibrate_absmax(R, K, _p(A), _p(amax), 1 if accumulate else 0, _stream()))
+    return amax
+
+
+def svdq_lambda_from_absmax(xmax, wmax, lam=None):
+    K = xmax.shape[0]
+    _need(xmax, "xmax", torch.float32, (K,))
+    _need(wmax, "wmax", torch.float32, (K,))
+    if lam is None:
+        lam = torch.empty(K, dtype=torch.float32, device=xmax.device)
+    _need(lam, "lambda", torch.float32, (K,))
+    _check("svdq_lambda_from_absmax",
+           load().svdq_lambda_from_absmax(K, _p(xmax), _p(wmax), _p(lam), _stream()))
     return lam
 
 

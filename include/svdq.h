@@ -123,6 +123,23 @@ const char* svdq_version(void);
 svdq_status svdq_calibrate_lambda(int64_t M, int32_t K, int32_t N, const uint16_t* X,
                                   const uint16_t* W, float* lambda, void* stream);
 
+/* Calibration over many batches (same page and section: the outlier
+ * statistics the smoothing factor comes from).  The per-column absolute
+ * maximum of a bf16 matrix A [R][K], combined with the running maximum in
+ * amax when accumulate is 1 (0: amax is overwritten):
+ *   amax[k] = max(accumulate ? amax[k] : 0, max_r |A[r][k]|)   (exact).
+ * Call it once per calibration batch of activations (and once on W), then
+ * svdq_lambda_from_absmax.  Limits: 1 <= R <= 2^31, K % 128 == 0,
+ * K <= 2^20; accumulate is 0 or 1. */
+svdq_status svdq_calibrate_absmax(int64_t R, int32_t K, const uint16_t* A, float* amax,
+                                  int32_t accumulate, void* stream);
+
+/* lambda[k] = fp32(sqrt(fp64(xmax[k]) / fp64(wmax[k]))), 1 where either
+ * maximum is 0 (the rule of svdq_calibrate_lambda, from running maxima).
+ * xmax, wmax, lambda: float32 [K]; K % 128 == 0, K <= 2^20. */
+svdq_status svdq_lambda_from_absmax(int32_t K, const float* xmax, const float* wmax,
+                                    float* lambda, void* stream);
+
 /* Offline weight packing (same two pages; the residual branch of W4A4).
  *   W_hat[n][k] = fp32(W[n][k] * lambda[k]);
  *   acc = 0; for i = 0..r-1: acc = fp32(acc + L1[k][i] * L2[i][n]);

@@ -198,6 +198,13 @@ def test_lowrank_pieces_validation():
 
 def test_calibrate_validation():
     lib = _lib()
+    assert lib.svdq_calibrate_absmax(16, 512, None, A, 0, None) == ARG
+    assert lib.svdq_calibrate_absmax(16, 512, A, MIS, 0, None) == ARG
+    assert lib.svdq_calibrate_absmax(16, 512, A, A, 2, None) == ARG
+    assert lib.svdq_calibrate_absmax(0, 512, A, A, 0, None) == SHAPE
+    assert lib.svdq_calibrate_absmax(16, 500, A, A, 1, None) == SHAPE
+    assert lib.svdq_lambda_from_absmax(512, A, None, A, None) == ARG
+    assert lib.svdq_lambda_from_absmax(500, A, A, A, None) == SHAPE
     assert lib.svdq_calibrate_lambda(16, 512, 16, None, A, A, None) == ARG
     assert lib.svdq_calibrate_lambda(16, 500, 16, A, A, A, None) == SHAPE
     assert lib.svdq_calibrate_lambda(16, 512, 0, A, A, A, None) == SHAPE
