@@ -19,22 +19,24 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _run_full(spec, X, W, b, mode, weight_rows, y_rows, y_cols, rank=None):
-    """Oracle on the sampled rows, GPU on everything; compare."""
+def _run_full(spec, X, W, b, mode, weight_rows, y_rows, y_cols, rank=None, gelu_in=False):
+    """Oracle on the sampled rows, GPU on everything; compare.  With gelu_in
+    the layer's input is GELU(X), applied in the activation pass (lambda is
+    then the oracle's, calibrated on GELU(X))."""
     from bit_diffusion_transformer_quantize_amd import svdq as S
     rank = spec.rank if rank is None else rank
     xb, wb, bb = WL.bits(X), WL.bits(W), WL.bits(b)
-    lam = O.calibrate_lambda(xb, wb)
+    lam = O.calibrate_lambda(O.gelu_bf16(xb) if gelu_in else xb, wb)
     L1, L2, _ = O.lowrank_factors(O.smooth_weight(wb, lam), rank)
     wc_o, ws_o = O.pack_weight(wb[weight_rows], lam, L1, L2[:, weight_rows], mode)
-    xc_o, xs_o, T_o, Xh = O.quantize_act(xb, lam, L1, mode)
+    xc_o, xs_o, T_o, Xh = O.quantize_act(xb, lam, L1, mode, gelu_in=gelu_in)
 
     M, K = X.shape
     N = W.shape[0]
-    _say(spec.name, mode, M, K, N, rank)
-    d = S.desc(mode, K, N, rank)
+    _say(spec.name, mode, M, K, N, rank, "gelu input" if gelu_in else "")
+    d = S.desc(mode, K, N, rank, gelu_in=gelu_in)
     Xd, Wd, bd = X.to(DEV), W.to(DEV), b.to(DEV)
-    lamd = S.svdq_calibrate_lambda(Xd, Wd)
+    lamd = torch.from_numpy(lam).to(DEV) if gelu_in else S.svdq_calibrate_lambda(Xd, Wd)
     ld, lu = to_dev_bf16(L1.T, DEV), to_dev_bf16(L2.T, DEV)
     wc, ws = S.svdq_pack_weight(d, Wd, lamd, ld, lu)
     T = torch.empty(M, rank, dtype=torch.float32, device=DEV)
@@ -81,10 +83,11 @@ def test_fused_qkv_mlp_fp4_full():
 
 
 def test_flux_mlp_pair_int4_full():
-    """MLP up 3072 -> 12288, GELU(tanh) on the host, MLP down 12288 -> 3072.
-    The down layer's input is GELU of the oracle's up output (computed with
+    """MLP up 3072 -> 12288, GELU(tanh), MLP down 12288 -> 3072, as the bench
+    runs it: the down layer reads the oracle's bf16 up output (computed with
     the oracle's dequantize-then-matmul formulation, which the oracle's pins
-    tie to the per-group formulation)."""
+    tie to the per-group formulation) and applies the GELU in its own
+    activation pass."""
     up, down = WL.FLUX_MLP_UP, WL.FLUX_MLP_DOWN
     X, Wu, bu = WL.draw(up, seed=0)
     wr, yr, yc = _samples(up.M, up.N, 3)
@@ -96,8 +99,19 @@ def test_flux_mlp_pair_int4_full():
     wc, ws = O.pack_weight(wb, lam, L1, L2, "int4")
     xc, xs, T, _ = O.quantize_act(xb, lam, L1, "int4")
     Y_up = O.forward_dequant(xc, xs, T, wc, ws, L2, bb, "int4")
-    y_bf16 = WL.from_bits(O.to_bf16_out(Y_up))
-    X_down = torch.nn.functional.gelu(y_bf16.float(), approximate="tanh").to(torch.bfloat16)
+    X_down = WL.from_bits(O.to_bf16_out(Y_up))
     _, Wd, bd = WL.draw(down, seed=0, M=1)
     wr, yr, yc = _samples(down.M, down.N, 4)
-    _run_full(down, X_down, Wd, bd, "int4", wr, yr, yc)
+    _run_full(down, X_down, Wd, bd, "int4", wr, yr, yc, gelu_in=True)
+
+
+@pytest.mark.parametrize("layer", ["block_img_qkv", "block_img_down"])
+def test_block_chain_image_layers_full(layer):
+    """The image-stream layers of the double-stream block at batch 2 (M =
+    8192, rank 128): the QKV projection, and the MLP down layer on a GELU
+    input (its input drawn by the seeded generator, standing in for the up
+    output; the GELU is applied in the activation pass)."""
+    spec = next(s for s in WL.block_chain_specs(128) if s.name == layer)
+    X, W, b = WL.draw(spec, seed=5)
+    wr, yr, yc = _samples(spec.M, spec.N, 5, n_w=512)
+    _run_full(spec, X, W, b, "int4", wr, yr, yc, gelu_in=layer.endswith("_down"))
