@@ -12,12 +12,15 @@ SVD is computed; this is the randomized range finder with power iterations of
 Halko, Martinsson and Tropp ("Finding structure with randomness", SIAM Review
 2011, algorithms 4.4 and 5.1), with l = r + p sketch columns:
 
-  Omega [N][l]: Rademacher signs, sign (n, j) = bit j of the 128-bit block
-      Philox4x32-10(counter = (n, 0, 0, 0), key = (seed_lo, seed_hi)),
-      bit set -> -1 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
-      as easy as 1, 2, 3", SC 2011);
+  Omega [N][l]: Rademacher signs, sign (n, j) = bit (j mod 128) of the
+      128-bit block Philox4x32-10(counter = (n, j div 128, 0, 0),
+      key = (seed_lo, seed_hi)) (bit b of the block = bit b mod 32 of word
+      b div 32), bit set -> -1 (Salmon, Moraes, Dror and Shaw, "Parallel
+      random numbers: as easy as 1, 2, 3", SC 2011);
   Q = orth(W_hat^T Omega);  q times: Z = orth(W_hat Q), Q = orth(W_hat^T Z);
-  B = W_hat Q [N][l];  B^T B = V diag(s^2) V^T (eigenvalues descending);
+  B = W_hat Q [N][l];  B^T B = V diag(s^2) V^T (eigenvalues descending,
+      equal ones in index order; each eigenvector's sign is chosen so that its
+      component of largest magnitude, the first one if several, is positive);
   L1 = Q V_r diag(sqrt s_r) [K][r],  L2^T = B V_r diag(1/sqrt s_r) [N][r],
 so that L1 L2 = Q Q^T-projected W_hat^T restricted to the top r directions,
 with the balanced sqrt(s) split; both factors are rounded to bf16 (RNE).
@@ -56,14 +59,14 @@ def philox4x32_10(ctr, key):
 
 
 def rademacher(N: int, l: int, seed: int) -> np.ndarray:
-    """Omega [N][l] of +-1 (fp64); l <= 128."""
-    assert l <= 128
+    """Omega [N][l] of +-1 (fp64)."""
     key = (seed & _MASK, (seed >> 32) & _MASK)
     om = np.empty((N, l), np.float64)
     for n in range(N):
-        words = philox4x32_10((n, 0, 0, 0), key)
-        bits = [(words[j >> 5] >> (j & 31)) & 1 for j in range(l)]
-        om[n] = [-1.0 if b else 1.0 for b in bits]
+        for blk in range((l + 127) // 128):
+            words = philox4x32_10((n, blk, 0, 0), key)
+            for b in range(min(128, l - 128 * blk)):
+                om[n, 128 * blk + b] = -1.0 if (words[b >> 5] >> (b & 31)) & 1 else 1.0
     return om
 
 
@@ -95,8 +98,10 @@ def rsvd_factors_f64(What: np.ndarray, r: int, seed: int, power_iters: int = 2,
         Q = orth_cholqr2(What.T @ Z)
     B = What @ Q
     ev, V = np.linalg.eigh(B.T @ B)
-    order = np.argsort(ev)[::-1]
+    order = np.argsort(-ev, kind="stable")
     ev, V = ev[order], V[:, order]
+    big = np.argmax(np.abs(V), axis=0)
+    V = V * np.where(V[big, np.arange(V.shape[1])] < 0, -1.0, 1.0)[None, :]
     s = np.sqrt(np.maximum(ev[:r], 0.0))
     rs = np.sqrt(s)
     L1 = (Q @ V[:, :r]) * rs[None, :]

@@ -27,6 +27,44 @@ def test_rademacher_signs():
     assert not np.array_equal(om, O.rademacher(2000, 48, seed=8))
 
 
+def test_rademacher_blocks_past_128_columns():
+    """Columns 128.. come from the next counter block: the first 128 columns
+    do not depend on l, and column 128 + b is not column b again."""
+    a = O.rademacher(300, 144, seed=11)
+    assert np.array_equal(a[:, :128], O.rademacher(300, 128, seed=11))
+    assert not np.array_equal(a[:, 128:], a[:, :16])
+    w = O.philox4x32_10((5, 1, 0, 0), (11, 0))
+    assert a[5, 128 + 9] == (-1.0 if (w[0] >> 9) & 1 else 1.0)
+
+
+def test_eigenvector_signs_do_not_change_the_factors(monkeypatch):
+    """The sign rule makes the factors independent of the signs the
+    eigensolver returns."""
+    A, _ = _decaying(200, 160, 2)
+    L1, up, _ = O.rsvd_factors_f64(A, 16, seed=5)
+    eigh = np.linalg.eigh
+
+    def flipped(M):
+        ev, V = eigh(M)
+        return ev, V * np.where(np.arange(V.shape[1]) % 3 == 0, -1.0, 1.0)[None, :]
+
+    monkeypatch.setattr(np.linalg, "eigh", flipped)
+    L1b, upb, _ = O.rsvd_factors_f64(A, 16, seed=5)
+    assert np.array_equal(L1, L1b) and np.array_equal(up, upb)
+    # the largest component of every column of L1 (a positive multiple of
+    # Q v) need not be positive, but each column pair keeps its product
+    assert np.allclose(up @ L1.T, upb @ L1b.T)
+
+
+def test_rank_128_sketch_wider_than_one_block():
+    A, s = _decaying(400, 300, 6)
+    r = 128
+    L1, up, sv = O.rsvd_factors_f64(A, r, seed=2, power_iters=2)
+    opt = np.sqrt(np.sum(s[r:] ** 2))
+    assert np.linalg.norm(A - up @ L1.T) <= 1.10 * opt
+    assert np.allclose(sv[:64], s[:64], rtol=1e-6)
+
+
 def test_cholqr2_orthonormal():
     rng = np.random.default_rng(0)
     Y = rng.standard_normal((500, 40)) @ np.diag(np.logspace(0, 6, 40))
