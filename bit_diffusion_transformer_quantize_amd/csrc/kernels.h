@@ -56,6 +56,13 @@ hipError_t launch_awq_linear(bool out_f32, int64_t M, int N, int K, const uint16
                              const uint8_t* codes, const float* scales, const uint8_t* zeros,
                              const uint16_t* bias, void* Y, hipStream_t s);
 
+// Randomized truncated SVD of the smoothed weight (lowrank_factors.hip).
+size_t lowrank_factors_workspace_bytes(int N, int K, int rank);
+hipError_t launch_lowrank_factors(int N, int K, int rank, const uint16_t* W, const float* lambda,
+                                  uint64_t seed, int power_iters, uint16_t* lora_down,
+                                  uint16_t* lora_up, double* sigma, void* workspace,
+                                  hipStream_t s);
+
 // Compute units of the current device (cached per device).
 int device_cus();
 

@@ -139,6 +139,39 @@ svdq_status svdq_pack_weight(const svdq_desc* d, const uint16_t* W, const float*
                                            lora_up, wcodes, wscales, (hipStream_t)stream));
 }
 
+namespace {
+svdq_status check_factor_shape(int32_t N, int32_t K, int32_t rank) {
+  if (N < 128 || N % 128 != 0 || N > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (K < 128 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if ((int64_t)N * K > (int64_t(1) << 32)) return SVDQ_ERR_SHAPE;
+  if (rank < 16 || rank > 128 || rank % 16 != 0) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+}  // namespace
+
+svdq_status svdq_lowrank_factors_workspace(int32_t N, int32_t K, int32_t rank, size_t* bytes) {
+  SVDQ_TRY(check_factor_shape(N, K, rank));
+  if (bytes == nullptr) return SVDQ_ERR_ARG;
+  *bytes = svdq::lowrank_factors_workspace_bytes(N, K, rank);
+  return SVDQ_OK;
+}
+
+svdq_status svdq_lowrank_factors(int32_t N, int32_t K, int32_t rank, const uint16_t* W,
+                                 const float* lambda, uint64_t seed, int32_t power_iters,
+                                 uint16_t* lora_down, uint16_t* lora_up, double* sigma,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  SVDQ_TRY(check_factor_shape(N, K, rank));
+  if (power_iters < 0 || power_iters > 8) return SVDQ_ERR_SHAPE;
+  if (!ptr_ok(W) || !ptr_ok(lambda) || !ptr_ok(lora_down) || !ptr_ok(lora_up) || !opt_ok(sigma))
+    return SVDQ_ERR_ARG;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SVDQ_ERR_ARG;
+  if (workspace_bytes < svdq::lowrank_factors_workspace_bytes(N, K, rank)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_lowrank_factors(N, K, rank, W, lambda, seed, power_iters, lora_down,
+                                               lora_up, sigma, workspace, (hipStream_t)stream));
+}
+
 svdq_status svdq_act_image_size(const svdq_desc* d, int64_t M, size_t* bytes) {
   SVDQ_TRY(check_desc(d));
   SVDQ_TRY(check_rows_k(M, d->K));

@@ -63,6 +63,10 @@ _SIGNATURES = {
     "svdq_awq_pack_weight": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "svdq_awq_linear": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint32,
                                        _vp, _vp]),
+    "svdq_lowrank_factors_workspace": (ctypes.c_int, [_i32, _i32, _i32,
+                                                      ctypes.POINTER(ctypes.c_size_t)]),
+    "svdq_lowrank_factors": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, ctypes.c_uint64, _i32, _vp,
+                                            _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -342,3 +346,38 @@ def svdq_awq_linear(X, codes, scales, zeros, bias=None, Y=None, out_f32: bool = 
            load().svdq_awq_linear(M, N, K, _p(X), _p(codes), _p(scales), _p(zeros), _p(bias),
                                   SVDQ_FLAG_OUT_F32 if out_f32 else 0, _p(Y), _stream()))
     return Y
+
+
+def svdq_lowrank_factors_workspace(N: int, K: int, rank: int) -> int:
+    """Bytes of device workspace svdq_lowrank_factors needs for this shape."""
+    n = ctypes.c_size_t(0)
+    _check("svdq_lowrank_factors_workspace",
+           load().svdq_lowrank_factors_workspace(N, K, rank, ctypes.byref(n)))
+    return n.value
+
+
+def svdq_lowrank_factors(W, lam, rank: int, seed: int, power_iters: int = 2, lora_down=None,
+                         lora_up=None, sigma=None, workspace=None, want_sigma: bool = True):
+    """Rank-r factors of W diag(lambda) by the library's randomized SVD; returns
+    (lora_down bf16 [r][K], lora_up bf16 [N][r], sigma fp64 [r] or None)."""
+    N, K = W.shape
+    _need(W, "W", torch.bfloat16, (N, K))
+    _need(lam, "lambda", torch.float32, (K,))
+    if lora_down is None:
+        lora_down = torch.empty(rank, K, dtype=torch.bfloat16, device=W.device)
+    if lora_up is None:
+        lora_up = torch.empty(N, rank, dtype=torch.bfloat16, device=W.device)
+    if sigma is None and want_sigma:
+        sigma = torch.empty(rank, dtype=torch.float64, device=W.device)
+    _need(lora_down, "lora_down", torch.bfloat16, (rank, K))
+    _need(lora_up, "lora_up", torch.bfloat16, (N, rank))
+    _need(sigma, "sigma", torch.float64, (rank,), optional=True)
+    need = svdq_lowrank_factors_workspace(N, K, rank)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=W.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check("svdq_lowrank_factors",
+           load().svdq_lowrank_factors(N, K, rank, _p(W), _p(lam), ctypes.c_uint64(seed),
+                                       power_iters, _p(lora_down), _p(lora_up), _p(sigma),
+                                       _p(workspace), workspace.numel(), _stream()))
+    return lora_down, lora_up, sigma

@@ -140,6 +140,44 @@ svdq_status svdq_calibrate_absmax(int64_t R, int32_t K, const uint16_t* A, float
 svdq_status svdq_lambda_from_absmax(int32_t K, const float* xmax, const float* wmax,
                                     float* lambda, void* stream);
 
+/* Offline: the rank-r factors of the smoothed weight (apatero.com page,
+ * section "O que e Nunchaku ...", and axbrief.com page, section "The
+ * Mechanics ...": the 16-bit branch is the rank-r part of W_hat =
+ * W diag(lambda) from its SVD), by a randomized truncated SVD.  The pages
+ * leave the SVD's algorithm open; this library fixes it as the randomized
+ * range finder with power iterations (Halko, Martinsson and Tropp, "Finding
+ * structure with randomness", SIAM Review 2011, algorithms 4.4 and 5.1):
+ *   W_hat[n][k] = fp32(W[n][k] * lambda[k]), then fp64 throughout;
+ *   l = min(rank + 16, N, K) sketch columns;
+ *   Omega[n][j] = -1 if bit (j mod 128) of the Philox4x32-10 block of counter
+ *     (n, j / 128, 0, 0) and key (seed mod 2^32, seed / 2^32) is set, else +1
+ *     (bit b of a block = bit b mod 32 of its word b / 32);
+ *   Q = orth(W_hat^T Omega); power_iters times: Z = orth(W_hat Q),
+ *     Q = orth(W_hat^T Z);
+ *   B = W_hat Q; B^T B = V diag(s^2) V^T, eigenvalues in descending order
+ *     (equal ones by index), each eigenvector's largest-magnitude component
+ *     (the first if several) positive;
+ *   lora_down = L1^T with L1 = Q V_r diag(sqrt s)       bf16 [rank][K],
+ *   lora_up   = L2^T = B V_r diag(1 / sqrt s)            bf16 [N][rank]
+ *     (1 in place of sqrt s when s = 0), each rounded fp64 -> fp32 -> bf16
+ *     (RNE both times); sigma[i] = s_i (fp64 [rank], optional, NULL = not
+ *     written);
+ *   orth(Y) = shifted CholeskyQR2: twice Y <- Y L^-T with
+ *     L L^T = Y^T Y + (1e-12 trace(Y^T Y) / l) I (a zero Y stays zero).
+ * lora_down and lora_up are the inputs of svdq_pack_weight and
+ * svdq_quantize_act of a layer with this rank.  The result is a deterministic
+ * function of the inputs, equal to the definition up to fp64 rounding (the
+ * bf16 factors then match it up to a rounding-boundary ulp).
+ * Limits: N, K multiples of 128, <= 2^20, N*K <= 2^32; 16 <= rank <= 128,
+ * rank % 16 == 0; 0 <= power_iters <= 8.  workspace: device memory of at
+ * least svdq_lowrank_factors_workspace() bytes, 256-byte aligned, owned by
+ * the caller, contents undefined afterwards (SVDQ_ERR_ARG if smaller). */
+svdq_status svdq_lowrank_factors_workspace(int32_t N, int32_t K, int32_t rank, size_t* bytes);
+svdq_status svdq_lowrank_factors(int32_t N, int32_t K, int32_t rank, const uint16_t* W,
+                                 const float* lambda, uint64_t seed, int32_t power_iters,
+                                 uint16_t* lora_down, uint16_t* lora_up, double* sigma,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Offline weight packing (same two pages; the residual branch of W4A4).
  *   W_hat[n][k] = fp32(W[n][k] * lambda[k]);
  *   acc = 0; for i = 0..r-1: acc = fp32(acc + L1[k][i] * L2[i][n]);

@@ -25,7 +25,8 @@ Halko, Martinsson and Tropp ("Finding structure with randomness", SIAM Review
 so that L1 L2 = Q Q^T-projected W_hat^T restricted to the top r directions,
 with the balanced sqrt(s) split; both factors are rounded to bf16 (RNE).
 orth() is shifted CholeskyQR2 (two rounds of G = Y^T Y + 1e-12 trace(G)/l I,
-R = chol(G), Y R^-1).  This oracle runs every step in fp64.
+R = chol(G), Y R^-1; a zero Y is returned unchanged).  This oracle runs every
+step in fp64.
 """
 from __future__ import annotations
 
@@ -80,7 +81,10 @@ def orth_cholqr2(Y: np.ndarray) -> np.ndarray:
     shifted CholeskyQR; with full rank its effect is of that relative size)."""
     for _ in range(2):
         G = Y.T @ Y
-        G = G + (RSVD_SHIFT * np.trace(G) / G.shape[0]) * np.eye(G.shape[0])
+        tr = np.trace(G)
+        if tr == 0.0:                               # a zero Y stays zero
+            return Y
+        G = G + (RSVD_SHIFT * tr / G.shape[0]) * np.eye(G.shape[0])
         R = np.linalg.cholesky(G).T                 # upper triangular
         Y = np.linalg.solve(R.T, Y.T).T             # Y R^-1
     return Y

@@ -233,6 +233,43 @@ def test_awq_validation():
     assert f(1, 64, 3008, A, A, A, A, None, 0, A, None) == SHAPE
 
 
+def test_lowrank_factors_validation():
+    lib = _lib()
+    n = ctypes.c_size_t(0)
+    ws = lib.svdq_lowrank_factors_workspace
+    assert ws(3072, 1024, 32, ctypes.byref(n)) == 0
+    need = n.value
+    # transposed weight + sketch buffers dominate: at least N*K*2 + (N + K)*l*8
+    assert need >= 3072 * 1024 * 2 + (3072 + 1024) * 48 * 8
+    assert ws(3072, 1024, 32, None) == ARG
+    for N, K, r in [(3000, 1024, 32), (3072, 64, 32), (3072, 1024, 0), (3072, 1024, 144),
+                    (3072, 1024, 40), (1 << 21, 128, 16), (1 << 17, 1 << 16, 16)]:
+        assert ws(N, K, r, ctypes.byref(n)) == SHAPE, (N, K, r)
+    # workspace grows with the rank
+    assert ws(3072, 1024, 128, ctypes.byref(n)) == 0 and n.value > need
+    f = lib.svdq_lowrank_factors
+    ok = (3072, 1024, 32, A, A, 7, 2, A, A, None, A, need, None)
+
+    def call(**kw):
+        names = ["N", "K", "r", "W", "lam", "seed", "q", "ld", "lu", "sig", "ws", "wsb", "st"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[k] for k in names])
+
+    assert call(W=None) == ARG
+    assert call(lam=MIS) == ARG
+    assert call(ld=None) == ARG
+    assert call(lu=MIS) == ARG
+    assert call(sig=MIS) == ARG
+    assert call(ws=None) == ARG
+    assert call(ws=A + 16) == ARG                 # workspace must be 256-byte aligned
+    assert call(wsb=need - 1) == ARG
+    assert call(q=-1) == SHAPE
+    assert call(q=9) == SHAPE
+    assert call(r=48) == ARG                      # rank 48 needs a larger workspace
+    assert call(N=3000) == SHAPE
+
+
 def _has_gpu():
     import torch
     return torch.cuda.device_count() > 0
@@ -248,3 +285,6 @@ def test_no_device_is_a_hip_error():
     assert lib.svdq_prepare_weight(_d(), A, A, A, None, A, None) == HIP
     assert lib.svdq_awq_pack_weight(64, 3072, A, A, A, A, None) == HIP
     assert lib.svdq_awq_linear(1, 64, 3072, A, A, A, A, None, 0, A, None) == HIP
+    n = ctypes.c_size_t(0)
+    assert lib.svdq_lowrank_factors_workspace(512, 512, 16, ctypes.byref(n)) == 0
+    assert lib.svdq_lowrank_factors(512, 512, 16, A, A, 1, 2, A, A, None, A, n.value, None) == HIP

@@ -101,6 +101,12 @@ def test_factors_of_an_exact_low_rank_matrix():
     assert np.linalg.norm(A - up @ L1.T) <= 1e-5 * np.linalg.norm(A)
 
 
+def test_zero_weight_gives_zero_factors():
+    W = np.zeros((256, 128), np.uint16)
+    ld, lu, s = O.rsvd_factors(W, np.ones(128, np.float32), 16, seed=1)
+    assert not ld.any() and not lu.any() and not s.any()
+
+
 def test_bf16_factors_shapes_and_product():
     rng = np.random.default_rng(5)
     W = O.f32_to_bf16((0.02 * rng.standard_normal((256, 128))).astype(np.float32))

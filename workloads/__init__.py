@@ -126,6 +126,21 @@ def draw(spec: LinearSpec, seed: int = 0, M: Optional[int] = None):
     return X.to(torch.bfloat16), W.to(torch.bfloat16), b.to(torch.bfloat16)
 
 
+def spectral_weight(N: int, K: int, seed: int = 0, terms: int = 192, decay: float = 1.0,
+                    noise: float = 0.002) -> torch.Tensor:
+    """A bf16 weight [N][K] with a decaying spectrum, like trained projection
+    weights (and unlike an i.i.d. Gaussian draw, whose singular values
+    bunch together): sum_i s_i a_i b_i^T over ``terms`` Gaussian pairs with
+    s_i = 0.02 (1 + i)^-decay, plus N(0, noise) per entry.  One generator
+    seeded with ``seed``; draws in the order a, b, noise."""
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn(N, terms, generator=g, dtype=torch.float32)
+    b = torch.randn(terms, K, generator=g, dtype=torch.float32) / float(np.sqrt(K))
+    s = 0.02 * (1.0 + torch.arange(terms, dtype=torch.float32)) ** -decay
+    W = (a * s[None, :]) @ b + noise * torch.randn(N, K, generator=g, dtype=torch.float32)
+    return W.to(torch.bfloat16)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> numpy uint16 array of its bit patterns (no arithmetic)."""
     assert t.dtype == torch.bfloat16
