@@ -53,6 +53,14 @@ __device__ __forceinline__ v4d mfma_f64(double a, double b, v4d c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier for kernels whose waves share only LDS: waits for this
+// wave's LDS operations (lgkmcnt(0); vmcnt and expcnt left at their maxima)
+// and not for its global loads and stores, which __syncthreads() would drain.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------------------ transpose
 // Wt[k][n] = W[n][k] (bf16 bit patterns), 64 x 64 tiles through LDS.
 __global__ __launch_bounds__(256) void rsvd_transpose_kernel(int N, int K,
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(256) void rsvd_omega_kernel(int N, int l, int LP, u
 }
 
 // ------------------------------------------------------------------ products
-// out[m][j] = sum_c A_hat[m][c] X[c][j] for 64 rows m per wave and 16 CB
+// out[m][j] = sum_c A_hat[m][c] X[c][j] for 16 RB rows m per wave and 16 CB
 // columns j, c over the contraction chunks of this split (blockIdx.z).
 //   AT 0: A bf16 [rows][lda], A_hat = fp32(A * scale[c])   (W_hat);
 //   AT 1: A bf16, A_hat = fp32(A * scale[m])               (W_hat^T via Wt);
@@ -131,12 +139,22 @@ __global__ __launch_bounds__(256) void rsvd_omega_kernel(int N, int l, int LP, u
 // A chunk is 32 (bf16) or 16 (fp64) contraction indices; in MFMA step t the
 // lanes of slot g = lane / 16 take contraction index c0 + (chunk / 4) g + t,
 // so each lane loads its A values with one contiguous 16-byte (bf16) or two
-// 16-byte (fp64) loads per 16-row block.  Output:
+// 16-byte (fp64) loads per 16-row block.  The next chunk's A values are
+// loaded while the current chunk runs, and each step's X values one step
+// ahead (clamped to the last chunk, so every iteration issues the same
+// loads).  Output:
 //   OUT 0: fp64 partial sums out[split * ostride + m * old + j];
 //   OUT 1: bf16 (RNE through fp32) out[m * old + j];
 //   OUT 2: bf16 (RNE through fp32) transposed out[j * old + m].
 // Column blocks at or past nblk are skipped (wave-uniform).
-template <int AT, int CB, int OUT>
+template <int AT, int RB>
+struct AChunk {
+  double ad[AT == 2 ? RB : 1][4];
+  v4u wr[AT == 2 ? 1 : RB];
+  float csc[8];
+};
+
+template <int AT, int RB, int CB, int OUT>
 __global__ __launch_bounds__(256) void rsvd_product_kernel(
     int rows, int nchunks, int cps, const void* __restrict__ Aptr, int64_t lda,
     const float* __restrict__ scale, const double* __restrict__ X, int64_t ldx, int nblk,
@@ -144,7 +162,7 @@ __global__ __launch_bounds__(256) void rsvd_product_kernel(
   constexpr int KC = AT == 2 ? 16 : 32;
   constexpr int ST = KC / 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = (blockIdx.x * 4 + wave) * 64;
+  const int m0 = (blockIdx.x * 4 + wave) * 16 * RB;
   if (m0 >= rows) return;
   const int cb0 = blockIdx.y * CB;
   const int split = blockIdx.z;
@@ -152,74 +170,89 @@ __global__ __launch_bounds__(256) void rsvd_product_kernel(
   const int ch1 = min(nchunks, ch0 + cps);
   const int r16 = lane & 15, g = lane >> 4;
 
-  v4d acc[4][CB];
+  v4d acc[RB][CB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = v4d{0.0, 0.0, 0.0, 0.0};
 
-  float rsc[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (AT == 1) {
+  float rsc[RB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) rsc[rb] = scale[m0 + 16 * rb + r16];
-  }
+  for (int rb = 0; rb < RB; ++rb) rsc[rb] = AT == 1 ? scale[m0 + 16 * rb + r16] : 1.f;
 
-  for (int ch = ch0; ch < ch1; ++ch) {
+  auto load_a = [&](int ch, AChunk<AT, RB>& a) {
     const int c0 = ch * KC;
-    // raw A values of this chunk: fp64 (4 per row block) or bf16 (8 per row
-    // block, converted to A_hat in the step that uses them)
-    double ad[4][4];
-    v4u wr[4];
-    float csc[8];
     if constexpr (AT == 2) {
       const double* A = static_cast<const double*>(Aptr);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         const double* p = A + (int64_t)(m0 + 16 * rb + r16) * lda + c0 + 4 * g;
         const v2d x0 = *reinterpret_cast<const v2d*>(p);
         const v2d x1 = *reinterpret_cast<const v2d*>(p + 2);
-        ad[rb][0] = x0[0];
-        ad[rb][1] = x0[1];
-        ad[rb][2] = x1[0];
-        ad[rb][3] = x1[1];
+        a.ad[rb][0] = x0[0];
+        a.ad[rb][1] = x0[1];
+        a.ad[rb][2] = x1[0];
+        a.ad[rb][3] = x1[1];
       }
     } else {
       const uint16_t* A = static_cast<const uint16_t*>(Aptr);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        a.wr[rb] =
+            *reinterpret_cast<const v4u*>(A + (int64_t)(m0 + 16 * rb + r16) * lda + c0 + 8 * g);
       if constexpr (AT == 0) {
         const v4f s0 = *reinterpret_cast<const v4f*>(scale + c0 + 8 * g);
         const v4f s1 = *reinterpret_cast<const v4f*>(scale + c0 + 8 * g + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          csc[e] = s0[e];
-          csc[4 + e] = s1[e];
+          a.csc[e] = s0[e];
+          a.csc[4 + e] = s1[e];
         }
       }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        wr[rb] =
-            *reinterpret_cast<const v4u*>(A + (int64_t)(m0 + 16 * rb + r16) * lda + c0 + 8 * g);
     }
+  };
+  // X values of contraction row `row` for this lane's columns
+  auto load_x = [&](int row, double (&xb)[CB]) {
+    const double* xr = X + (int64_t)row * ldx + 16 * cb0 + r16;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) xb[cb] = (cb0 + cb < nblk) ? xr[16 * cb] : 0.0;
+  };
+  double xb[2][CB];
+  auto run_chunk = [&](const AChunk<AT, RB>& a, int ch) {
 #pragma unroll
     for (int t = 0; t < ST; ++t) {
-      double a[4];
+      const int nch = t + 1 < ST ? ch : min(ch + 1, ch1 - 1);
+      load_x(nch * KC + ST * g + (t + 1 < ST ? t + 1 : 0), xb[(t + 1) & 1]);
+      double av[RB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         if constexpr (AT == 2) {
-          a[rb] = ad[rb][t];
+          av[rb] = a.ad[rb][t];
         } else {
-          const uint32_t h = (t & 1) ? (wr[rb][t >> 1] >> 16) : (wr[rb][t >> 1] & 0xFFFFu);
-          a[rb] = (double)(bf16_to_f32(h) * (AT == 0 ? csc[t] : rsc[rb]));
+          const uint32_t h = (t & 1) ? (a.wr[rb][t >> 1] >> 16) : (a.wr[rb][t >> 1] & 0xFFFFu);
+          av[rb] = (double)(bf16_to_f32(h) * (AT == 0 ? a.csc[t] : rsc[rb]));
         }
       }
-      const double* xr = X + (int64_t)(c0 + ST * g + t) * ldx + 16 * cb0 + r16;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         if (cb0 + cb < nblk) {
-          const double b = xr[16 * cb];
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma_f64(a[rb], b, acc[rb][cb]);
+          for (int rb = 0; rb < RB; ++rb) acc[rb][cb] = mfma_f64(av[rb], xb[t & 1][cb], acc[rb][cb]);
         }
       }
+    }
+  };
+
+  if (ch0 < ch1) {
+    AChunk<AT, RB> a0, a1;
+    load_a(ch0, a0);
+    load_x(ch0 * KC + ST * g, xb[0]);
+    for (int ch = ch0; ch < ch1; ch += 2) {
+      load_a(min(ch + 1, ch1 - 1), a1);
+      run_chunk(a0, ch);
+      if (ch + 1 >= ch1) break;
+      load_a(min(ch + 2, ch1 - 1), a0);
+      run_chunk(a1, ch + 1);
     }
   }
 
@@ -231,7 +264,7 @@ __global__ __launch_bounds__(256) void rsvd_product_kernel(
     if (cb0 + cb >= nblk) continue;
     const int col = 16 * (cb0 + cb) + r16;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const int row = m0 + 16 * rb + g;
       if constexpr (OUT == 0) {
         double* o = static_cast<double*>(out) + split * ostride + (int64_t)row * old + col;
@@ -318,17 +351,29 @@ __global__ __launch_bounds__(256) void rsvd_sum_gram_kernel(const double* __rest
   }
 }
 
-// G[x][y] = G[y][x] = sum_b Gp[b][x][y] (b in order) for x <= y.
+// G[x][y] = G[y][x] = sum_b Gp[b][x][y] for x <= y: 64 entries per
+// workgroup, its 4 waves summing every 4th block (b = w, w + 4, ...), then
+// the four sums added in wave order.
 __global__ __launch_bounds__(256) void rsvd_gram_reduce_kernel(const double* __restrict__ Gp, int NB,
                                                                int LP, double* __restrict__ G) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= LP * LP) return;
-  const int x = e / LP, y = e % LP;
-  if (x > y) return;
-  double s = 0.0;
-  for (int b = 0; b < NB; ++b) s += Gp[(int64_t)b * LP * LP + e];
-  G[x * LP + y] = s;
-  G[y * LP + x] = s;
+  __shared__ double part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int n = LP * LP;
+  double acc = 0.0;
+  if (e < n) {
+    for (int b = wave; b < NB; b += 4) acc += Gp[(int64_t)b * n + e];
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && e < n) {
+    const int x = e / LP, y = e % LP;
+    if (x <= y) {
+      const double v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+      G[x * LP + y] = v;
+      G[y * LP + x] = v;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ Cholesky
@@ -348,15 +393,18 @@ __device__ __forceinline__ void tri_rc(int e, int& i, int& j) {
 // L^-1 is final once the contributions of rows 0..k-1 are added; each step
 // adds row k's contribution to the rows below).  Output XT[c][j] = L^-1[j][c]
 // (c <= j < l), zero elsewhere in LP x LP: the right operand of Y <- Y L^-T.
-// A zero matrix (trace 0) gives XT = I, so a zero Y stays zero.
-__global__ __launch_bounds__(1024) void rsvd_chol_inv_kernel(const double* __restrict__ G, int l,
+// A zero matrix (trace 0) gives XT = I, so a zero Y stays zero.  One thread
+// per entry of a step (1024 threads).
+constexpr int CHOL_THREADS = 1024;
+
+__global__ __launch_bounds__(CHOL_THREADS) void rsvd_chol_inv_kernel(const double* __restrict__ G, int l,
                                                              int LP, double* __restrict__ XT) {
   __shared__ double a[RSVD_MAX_L * (RSVD_MAX_L + 1) / 2];
   __shared__ double colk[RSVD_MAX_L];
   __shared__ double s_trace;
   const int tid = threadIdx.x;
   const int nt = l * (l + 1) / 2;
-  for (int e = tid; e < nt; e += 1024) {
+  for (int e = tid; e < nt; e += CHOL_THREADS) {
     int i, j;
     tri_rc(e, i, j);
     a[e] = G[i * LP + j];
@@ -366,26 +414,26 @@ __global__ __launch_bounds__(1024) void rsvd_chol_inv_kernel(const double* __res
     for (int i = 0; i < l; ++i) tr += G[i * LP + i];
     s_trace = tr;
   }
-  __syncthreads();
+  lds_barrier();
   const double tr = s_trace;
   if (tr == 0.0) {
-    for (int e = tid; e < LP * LP; e += 1024) {
+    for (int e = tid; e < LP * LP; e += CHOL_THREADS) {
       const int c = e / LP, j = e % LP;
       XT[e] = (c == j && j < l) ? 1.0 : 0.0;
     }
     return;
   }
   const double shift = RSVD_SHIFT * tr / (double)l;
-  for (int i = tid; i < l; i += 1024) a[tri(i, i)] += shift;
-  __syncthreads();
+  for (int i = tid; i < l; i += CHOL_THREADS) a[tri(i, i)] += shift;
+  lds_barrier();
 
   for (int j = 0; j < l; ++j) {
     const double d = __builtin_sqrt(a[tri(j, j)]);
-    for (int i = j + 1 + tid; i < l; i += 1024) a[tri(i, j)] /= d;
-    __syncthreads();
+    for (int i = j + 1 + tid; i < l; i += CHOL_THREADS) a[tri(i, j)] /= d;
+    lds_barrier();
     const int m = l - j - 1;
     const int cnt = m * (m + 1) / 2;
-    for (int e = tid; e < cnt; e += 1024) {
+    for (int e = tid; e < cnt; e += CHOL_THREADS) {
       int ii, kk;
       tri_rc(e, ii, kk);
       ii += j + 1;
@@ -393,30 +441,30 @@ __global__ __launch_bounds__(1024) void rsvd_chol_inv_kernel(const double* __res
       a[tri(ii, kk)] -= a[tri(ii, j)] * a[tri(kk, j)];
     }
     if (tid == 0) a[tri(j, j)] = d;
-    __syncthreads();
+    lds_barrier();
   }
 
   for (int k = 0; k < l; ++k) {
     const double dk = a[tri(k, k)];
-    for (int e = tid; e < l; e += 1024) {
+    for (int e = tid; e < l; e += CHOL_THREADS) {
       if (e < k) a[tri(k, e)] = -a[tri(k, e)] / dk;
       else if (e > k) colk[e] = a[tri(e, k)];
     }
-    __syncthreads();
+    lds_barrier();
     const double inv = 1.0 / dk;
     if (tid == 0) a[tri(k, k)] = inv;
     const int rows_below = l - k - 1;
     const int cnt = rows_below * (k + 1);
-    for (int e = tid; e < cnt; e += 1024) {
+    for (int e = tid; e < cnt; e += CHOL_THREADS) {
       const int i = k + 1 + e / (k + 1), j = e % (k + 1);
       const double xk = j < k ? a[tri(k, j)] : inv;
       const double prev = j < k ? a[tri(i, j)] : 0.0;
       a[tri(i, j)] = prev + colk[i] * xk;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
-  for (int e = tid; e < LP * LP; e += 1024) {
+  for (int e = tid; e < LP * LP; e += CHOL_THREADS) {
     const int c = e / LP, j = e % LP;
     XT[e] = (c <= j && j < l) ? a[tri(j, c)] : 0.0;
   }
@@ -426,7 +474,9 @@ __global__ __launch_bounds__(1024) void rsvd_chol_inv_kernel(const double* __res
 // Index at position p of step k of the round-robin ordering of le (even)
 // indices: position 0 stays, the others rotate.
 __device__ __forceinline__ int rr_index(int p, int k, int le) {
-  return p == 0 ? 0 : 1 + (p - 1 + k) % (le - 1);
+  int v = p - 1 + k;            // 0 <= p - 1 + k < 2 (le - 1): one conditional subtraction
+  v = v >= le - 1 ? v - (le - 1) : v;
+  return p == 0 ? 0 : 1 + v;
 }
 
 __device__ __forceinline__ int sym(int x, int y) { return x >= y ? tri(x, y) : tri(y, x); }
@@ -439,8 +489,11 @@ __device__ __forceinline__ int sym(int x, int y) { return x >= y ? tri(x, y) : t
 // rotated by one thread.  A pair rotates when |c_pq| > 2^-52 sqrt|c_pp c_qq|;
 // the sweeps stop after one with no rotation (at most 40).  Every step's
 // (c, s) per pair goes to the log rot[sweep][step][pair]; ev[i] is the final
-// diagonal, nsweeps the number of sweeps logged.
-__global__ __launch_bounds__(1024) void rsvd_jacobi_kernel(const double* __restrict__ Cm, int l,
+// diagonal, nsweeps the number of sweeps logged.  One thread per pair block
+// (1024 threads, at most 3 blocks each).
+constexpr int JAC_THREADS = 1024;
+
+__global__ __launch_bounds__(JAC_THREADS) void rsvd_jacobi_kernel(const double* __restrict__ Cm, int l,
                                                            int LP, double* __restrict__ rot,
                                                            double* __restrict__ ev,
                                                            int* __restrict__ nsweeps) {
@@ -450,7 +503,7 @@ __global__ __launch_bounds__(1024) void rsvd_jacobi_kernel(const double* __restr
   __shared__ int s_count;
   const int tid = threadIdx.x;
   const int nt = l * (l + 1) / 2;
-  for (int e = tid; e < nt; e += 1024) {
+  for (int e = tid; e < nt; e += JAC_THREADS) {
     int i, j;
     tri_rc(e, i, j);
     a[e] = Cm[i * LP + j];
@@ -461,7 +514,7 @@ __global__ __launch_bounds__(1024) void rsvd_jacobi_kernel(const double* __restr
   int ba[3], bb[3];
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
-    int id = tid + 1024 * q, x = 0;
+    int id = tid + JAC_THREADS * q, x = 0;
     if (id < nblocks) {
       while (id >= h - x) {
         id -= h - x;
@@ -477,7 +530,7 @@ __global__ __launch_bounds__(1024) void rsvd_jacobi_kernel(const double* __restr
   int sweep = 0;
   while (sweep < RSVD_MAX_SWEEPS) {
     if (tid == 0) s_count = 0;
-    __syncthreads();
+    lds_barrier();
     for (int k = 0; k < nsteps; ++k) {
       if (tid < h) {
         const int u = rr_index(tid, k, le), w = rr_index(le - 1 - tid, k, le);
@@ -505,7 +558,7 @@ __global__ __launch_bounds__(1024) void rsvd_jacobi_kernel(const double* __restr
         lg[0] = c;
         lg[1] = s;
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int q3 = 0; q3 < 3; ++q3) {
         const int x = ba[q3], y = bb[q3];
@@ -535,52 +588,88 @@ __global__ __launch_bounds__(1024) void rsvd_jacobi_kernel(const double* __restr
         if (va) a[sym(qa, pb)] = cb * r10 - sb * r11;
         if (va && vb) a[sym(qa, qb)] = sb * r10 + cb * r11;
       }
-      __syncthreads();
+      lds_barrier();
     }
     ++sweep;
     const int cnt = s_count;
-    __syncthreads();
+    lds_barrier();
     if (cnt == 0) break;
   }
-  for (int i = tid; i < l; i += 1024) ev[i] = a[tri(i, i)];
+  for (int i = tid; i < l; i += JAC_THREADS) ev[i] = a[tri(i, i)];
   if (tid == 0) *nsweeps = sweep;
 }
 
 // V = J_1 J_2 ... (the logged rotations in order): rows 16 blockIdx.x ..
 // +15 of V, each row vector rotated in LDS.  V[i][c] is component i of
 // eigenvector c.  Columns l..LP-1 are zero.
-__global__ __launch_bounds__(256) void rsvd_vbuild_kernel(const double* __restrict__ rot,
-                                                          const int* __restrict__ nsweeps, int l,
-                                                          int LP, double* __restrict__ V) {
+constexpr int VB_THREADS = 1024;
+constexpr int VB_ITEMS = 2;   // ceil(16 * 72 / 1024)
+
+__global__ __launch_bounds__(VB_THREADS) void rsvd_vbuild_kernel(const double* __restrict__ rot,
+                                                                 const int* __restrict__ nsweeps,
+                                                                 int l, int LP,
+                                                                 double* __restrict__ V) {
   __shared__ double vr[16][RSVD_MAX_LP];
   const int i0 = blockIdx.x * 16;
-  for (int e = threadIdx.x; e < 16 * LP; e += 256) {
+  for (int e = threadIdx.x; e < 16 * LP; e += VB_THREADS) {
     const int rho = e / LP, c = e % LP;
     vr[rho][c] = (i0 + rho == c) ? 1.0 : 0.0;
   }
   const int le = l + (l & 1), h = le / 2, nsteps = le - 1;
-  const int ns = *nsweeps;
-  for (int sw = 0; sw < ns; ++sw) {
-    for (int k = 0; k < nsteps; ++k) {
-      __syncthreads();
-      const double* lg = rot + (int64_t)(sw * nsteps + k) * h * 2;
-      for (int e = threadIdx.x; e < 16 * h; e += 256) {
-        const int rho = e / h, x = e % h;
-        const double s = lg[2 * x + 1];
-        if (s == 0.0) continue;
-        const double c = lg[2 * x];
-        const int u = rr_index(x, k, le), w = rr_index(le - 1 - x, k, le);
-        const int p = min(u, w), q = max(u, w);
-        const double vp = vr[rho][p], vq = vr[rho][q];
-        vr[rho][p] = c * vp - s * vq;
-        vr[rho][q] = s * vp + c * vq;
+  const int total = *nsweeps * nsteps;   // logged steps, in order
+  // this thread's (row, pair) items are fixed; each step's (c, s) are loaded
+  // one step ahead
+  int rho[VB_ITEMS], xi[VB_ITEMS];
+#pragma unroll
+  for (int z = 0; z < VB_ITEMS; ++z) {
+    const int e = threadIdx.x + z * VB_THREADS;
+    rho[z] = e < 16 * h ? e / h : -1;
+    xi[z] = e % h;
+  }
+  double cn[VB_ITEMS], sn[VB_ITEMS];
+#pragma unroll
+  for (int z = 0; z < VB_ITEMS; ++z) {
+    cn[z] = total > 0 && rho[z] >= 0 ? rot[2 * xi[z]] : 1.0;
+    sn[z] = total > 0 && rho[z] >= 0 ? rot[2 * xi[z] + 1] : 0.0;
+  }
+  for (int st = 0; st < total; ++st) {
+    const int k = st % nsteps;
+    const int nxt = min(st + 1, total - 1);
+    double c[VB_ITEMS], s[VB_ITEMS];
+#pragma unroll
+    for (int z = 0; z < VB_ITEMS; ++z) {
+      c[z] = cn[z];
+      s[z] = sn[z];
+      if (rho[z] >= 0) {
+        const double* lg = rot + ((int64_t)nxt * h + xi[z]) * 2;
+        cn[z] = lg[0];
+        sn[z] = lg[1];
       }
     }
+    lds_barrier();
+    double vp[VB_ITEMS], vq[VB_ITEMS];
+    int p[VB_ITEMS], q[VB_ITEMS];
+#pragma unroll
+    for (int z = 0; z < VB_ITEMS; ++z) {
+      const int u = rr_index(xi[z], k, le), w = rr_index(le - 1 - xi[z], k, le);
+      p[z] = min(u, w);
+      q[z] = max(u, w);
+      if (rho[z] >= 0 && s[z] != 0.0 && q[z] < l) {
+        vp[z] = vr[rho[z]][p[z]];
+        vq[z] = vr[rho[z]][q[z]];
+      }
+    }
+#pragma unroll
+    for (int z = 0; z < VB_ITEMS; ++z) {
+      if (rho[z] < 0 || s[z] == 0.0 || q[z] >= l) continue;
+      vr[rho[z]][p[z]] = c[z] * vp[z] - s[z] * vq[z];
+      vr[rho[z]][q[z]] = s[z] * vp[z] + c[z] * vq[z];
+    }
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 16 * LP; e += 256) {
-    const int rho = e / LP, c = e % LP;
-    if (i0 + rho < l) V[(int64_t)(i0 + rho) * LP + c] = c < l ? vr[rho][c] : 0.0;
+  lds_barrier();
+  for (int e = threadIdx.x; e < 16 * LP; e += VB_THREADS) {
+    const int r = e / LP, c = e % LP;
+    if (i0 + r < l) V[(int64_t)(i0 + r) * LP + c] = c < l ? vr[r][c] : 0.0;
   }
 }
 
@@ -657,11 +746,9 @@ struct GramPlan {
   int NB, rpb;
 };
 GramPlan plan_gram(int T) {
-  int NB = std::max(1, std::min(128, T / 64));
-  int rpb = (T + NB - 1) / NB;
-  rpb = (rpb + GRAM_ROWS - 1) / GRAM_ROWS * GRAM_ROWS;
-  NB = (T + rpb - 1) / rpb;
-  return GramPlan{NB, rpb};
+  const int chunks = (T + GRAM_ROWS - 1) / GRAM_ROWS;
+  const int rpb = GRAM_ROWS * ((chunks + 511) / 512);
+  return GramPlan{(T + rpb - 1) / rpb, rpb};
 }
 
 struct RsvdPlan {
@@ -710,27 +797,28 @@ RsvdPlan make_plan(int N, int K, int r) {
   return P;
 }
 
-template <int AT, int OUT, int CB>
-hipError_t product_cb(int rows, const Split& sp, int KC, const void* A, int64_t lda,
-                      const float* scale, const double* X, int64_t ldx, int nblk, void* out,
-                      int64_t old, int64_t ostride, hipStream_t s) {
-  (void)KC;
-  const dim3 grid((rows + 255) / 256, (nblk + CB - 1) / CB, sp.S);
-  hipLaunchKernelGGL((rsvd_product_kernel<AT, CB, OUT>), grid, dim3(256), 0, s, rows, sp.nchunks,
-                     sp.cps, A, lda, scale, X, ldx, nblk, out, old, ostride);
+template <int AT, int OUT, int RB, int CB>
+hipError_t product_cb(int rows, const Split& sp, const void* A, int64_t lda, const float* scale,
+                      const double* X, int64_t ldx, int nblk, void* out, int64_t old,
+                      int64_t ostride, hipStream_t s) {
+  const dim3 grid((rows + 64 * RB - 1) / (64 * RB), (nblk + CB - 1) / CB, sp.S);
+  hipLaunchKernelGGL((rsvd_product_kernel<AT, RB, CB, OUT>), grid, dim3(256), 0, s, rows,
+                     sp.nchunks, sp.cps, A, lda, scale, X, ldx, nblk, out, old, ostride);
   return hipGetLastError();
 }
 
+// The W_hat products (bf16 A) use 64 rows per wave; the small fp64 products
+// (CholeskyQR applications, factors) 16 rows per wave, for more waves.
 template <int AT, int OUT>
 hipError_t product(int rows, const Split& sp, const void* A, int64_t lda, const float* scale,
                    const double* X, int64_t ldx, int nblk, void* out, int64_t old,
                    int64_t ostride, hipStream_t s) {
-  constexpr int KC = AT == 2 ? 16 : 32;
+  constexpr int RB = AT == 2 ? 1 : 4;
   switch (col_blocks(nblk)) {
-    case 1: return product_cb<AT, OUT, 1>(rows, sp, KC, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
-    case 2: return product_cb<AT, OUT, 2>(rows, sp, KC, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
-    case 3: return product_cb<AT, OUT, 3>(rows, sp, KC, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
-    default: return product_cb<AT, OUT, 4>(rows, sp, KC, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
+    case 1: return product_cb<AT, OUT, RB, 1>(rows, sp, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
+    case 2: return product_cb<AT, OUT, RB, 2>(rows, sp, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
+    case 3: return product_cb<AT, OUT, RB, 3>(rows, sp, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
+    default: return product_cb<AT, OUT, RB, 4>(rows, sp, A, lda, scale, X, ldx, nblk, out, old, ostride, s);
   }
 }
 
@@ -754,7 +842,7 @@ hipError_t gram(const Ws& w, const double* Psum, int S, int64_t pstride, int T, 
   hipLaunchKernelGGL(rsvd_sum_gram_kernel, dim3(gp.NB), dim3(256), 0, s, Psum, S, pstride, T, LP,
                      gp.rpb, Y, w.d(w.P.gp));
   RSVD_TRY(hipGetLastError());
-  hipLaunchKernelGGL(rsvd_gram_reduce_kernel, dim3((LP * LP + 255) / 256), dim3(256), 0, s,
+  hipLaunchKernelGGL(rsvd_gram_reduce_kernel, dim3((LP * LP + 63) / 64), dim3(256), 0, s,
                      w.d(w.P.gp), gp.NB, LP, w.d(w.P.g));
   return hipGetLastError();
 }
@@ -768,11 +856,11 @@ hipError_t orth(const Ws& w, const double* Psum, int S, int64_t pstride, int T,
   const double* Y = Psum;
   if (S > 1) Y = w.d(P.y);
   RSVD_TRY(gram(w, Psum, S, pstride, T, gp, S > 1 ? w.d(P.y) : nullptr, s));
-  hipLaunchKernelGGL(rsvd_chol_inv_kernel, dim3(1), dim3(1024), 0, s, w.d(P.g), P.l, LP, w.d(P.xt));
+  hipLaunchKernelGGL(rsvd_chol_inv_kernel, dim3(1), dim3(CHOL_THREADS), 0, s, w.d(P.g), P.l, LP, w.d(P.xt));
   RSVD_TRY(hipGetLastError());
   RSVD_TRY((product<2, 0>(T, one, Y, LP, nullptr, w.d(P.xt), LP, nblk, w.d(P.t), LP, 0, s)));
   RSVD_TRY(gram(w, w.d(P.t), 1, 0, T, gp, nullptr, s));
-  hipLaunchKernelGGL(rsvd_chol_inv_kernel, dim3(1), dim3(1024), 0, s, w.d(P.g), P.l, LP, w.d(P.xt));
+  hipLaunchKernelGGL(rsvd_chol_inv_kernel, dim3(1), dim3(CHOL_THREADS), 0, s, w.d(P.g), P.l, LP, w.d(P.xt));
   RSVD_TRY(hipGetLastError());
   return product<2, 0>(T, one, w.d(P.t), LP, nullptr, w.d(P.xt), LP, nblk, dst, LP, 0, s);
 }
@@ -816,10 +904,10 @@ hipError_t launch_lowrank_factors(int N, int K, int rank, const uint16_t* W, con
   RSVD_TRY((product<0, 0>(N, P.left, W, K, lambda, Q, LP, nblk, Pp, LP, strideN, s)));
   double* B = P.left.S > 1 ? Z : Pp;
   RSVD_TRY(gram(w, Pp, P.left.S, strideN, N, P.gN, P.left.S > 1 ? Z : nullptr, s));
-  hipLaunchKernelGGL(rsvd_jacobi_kernel, dim3(1), dim3(1024), 0, s, w.d(P.g), P.l, LP, w.d(P.rot),
-                     w.d(P.ev), reinterpret_cast<int*>(w.base + P.ns));
+  hipLaunchKernelGGL(rsvd_jacobi_kernel, dim3(1), dim3(JAC_THREADS), 0, s, w.d(P.g), P.l, LP,
+                     w.d(P.rot), w.d(P.ev), reinterpret_cast<int*>(w.base + P.ns));
   RSVD_TRY(hipGetLastError());
-  hipLaunchKernelGGL(rsvd_vbuild_kernel, dim3((P.l + 15) / 16), dim3(256), 0, s, w.d(P.rot),
+  hipLaunchKernelGGL(rsvd_vbuild_kernel, dim3((P.l + 15) / 16), dim3(VB_THREADS), 0, s, w.d(P.rot),
                      reinterpret_cast<const int*>(w.base + P.ns), P.l, LP, w.d(P.v));
   RSVD_TRY(hipGetLastError());
   hipLaunchKernelGGL(rsvd_finish_kernel, dim3(1), dim3(256), 0, s, w.d(P.ev), w.d(P.v), P.l, LP,
