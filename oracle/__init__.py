@@ -8,3 +8,4 @@ from .svdq_oracle import INT4_GROUP, FP4_BLOCK, E2M1_GRID  # noqa: F401
 from .awq_oracle import *  # noqa: F401,F403
 from .gelu_oracle import *  # noqa: F401,F403
 from .rsvd_oracle import *  # noqa: F401,F403
+from .qkv_oracle import *  # noqa: F401,F403
