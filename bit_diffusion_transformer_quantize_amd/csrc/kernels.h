@@ -56,6 +56,11 @@ hipError_t launch_awq_linear(bool out_f32, int64_t M, int N, int K, const uint16
                              const uint8_t* codes, const float* scales, const uint8_t* zeros,
                              const uint16_t* bias, void* Y, hipStream_t s);
 
+// Q/K RMSNorm + rotary embedding of the QKV output, in place (qk_norm_rope.hip).
+hipError_t launch_qk_norm_rope(int64_t M, int heads, uint16_t* Y, const uint16_t* q_scale,
+                               const uint16_t* k_scale, const float* cosv, const float* sinv,
+                               float eps, hipStream_t s);
+
 // Randomized truncated SVD of the smoothed weight (lowrank_factors.hip).
 size_t lowrank_factors_workspace_bytes(int N, int K, int rank);
 hipError_t launch_lowrank_factors(int N, int K, int rank, const uint16_t* W, const float* lambda,

@@ -261,6 +261,18 @@ svdq_status svdq_lowrank_up(const svdq_desc* d, int64_t M, const float* T,
                                           d->N, T, lora_up, Y, (hipStream_t)stream));
 }
 
+svdq_status svdq_qk_norm_rope(int64_t M, int32_t heads, uint16_t* Y, const uint16_t* q_scale,
+                              const uint16_t* k_scale, const float* cos, const float* sin,
+                              float eps, void* stream) {
+  if (!ptr_ok(Y) || !ptr_ok(q_scale) || !ptr_ok(k_scale) || !ptr_ok(cos) || !ptr_ok(sin))
+    return SVDQ_ERR_ARG;
+  if (!(eps > 0.0f) || eps > 3.4e38f) return SVDQ_ERR_ARG;
+  if (M < 1 || M > (int64_t(1) << 31) || heads < 1 || heads > 2048) return SVDQ_ERR_SHAPE;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_qk_norm_rope(M, heads, Y, q_scale, k_scale, cos, sin, eps,
+                                            (hipStream_t)stream));
+}
+
 svdq_status svdq_awq_pack_weight(int32_t N, int32_t K, const uint16_t* W, uint8_t* codes,
                                  float* scales, uint8_t* zeros, void* stream) {
   if (!ptr_ok(W) || !ptr_ok(codes) || !ptr_ok(scales) || !ptr_ok(zeros)) return SVDQ_ERR_ARG;

@@ -63,6 +63,8 @@ _SIGNATURES = {
     "svdq_awq_pack_weight": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "svdq_awq_linear": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint32,
                                        _vp, _vp]),
+    "svdq_qk_norm_rope": (ctypes.c_int, [_i64, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                         _vp]),
     "svdq_lowrank_factors_workspace": (ctypes.c_int, [_i32, _i32, _i32,
                                                       ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_lowrank_factors": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, ctypes.c_uint64, _i32, _vp,
@@ -381,3 +383,21 @@ def svdq_lowrank_factors(W, lam, rank: int, seed: int, power_iters: int = 2, lor
                                        power_iters, _p(lora_down), _p(lora_up), _p(sigma),
                                        _p(workspace), workspace.numel(), _stream()))
     return lora_down, lora_up, sigma
+
+
+HEAD_DIM = 128
+
+
+def svdq_qk_norm_rope(Y, heads: int, q_scale, k_scale, cos, sin, eps: float = 1e-6):
+    """Per-head RMSNorm + rotary embedding of the Q and K parts of the QKV
+    output Y (bf16 [M][3 heads 128]), in place; returns Y."""
+    M = Y.shape[0]
+    _need(Y, "Y", torch.bfloat16, (M, 3 * heads * HEAD_DIM))
+    _need(q_scale, "q_scale", torch.bfloat16, (HEAD_DIM,))
+    _need(k_scale, "k_scale", torch.bfloat16, (HEAD_DIM,))
+    _need(cos, "cos", torch.float32, (M, HEAD_DIM // 2))
+    _need(sin, "sin", torch.float32, (M, HEAD_DIM // 2))
+    _check("svdq_qk_norm_rope",
+           load().svdq_qk_norm_rope(M, heads, _p(Y), _p(q_scale), _p(k_scale), _p(cos), _p(sin),
+                                    float(eps), _stream()))
+    return Y

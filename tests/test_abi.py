@@ -270,6 +270,30 @@ def test_lowrank_factors_validation():
     assert call(N=3000) == SHAPE
 
 
+def test_qk_norm_rope_validation():
+    f = _lib().svdq_qk_norm_rope
+    ok = dict(M=64, H=24, Y=A, qs=A, ks=A, c=A, s=A, eps=1e-6)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["M"], a["H"], a["Y"], a["qs"], a["ks"], a["c"], a["s"], a["eps"], None)
+
+    assert call(Y=None) == ARG
+    assert call(Y=MIS) == ARG
+    assert call(qs=None) == ARG
+    assert call(ks=MIS) == ARG
+    assert call(c=None) == ARG
+    assert call(s=MIS) == ARG
+    assert call(eps=0.0) == ARG
+    assert call(eps=-1.0) == ARG
+    assert call(eps=float("nan")) == ARG
+    assert call(eps=float("inf")) == ARG
+    assert call(M=0) == SHAPE
+    assert call(H=0) == SHAPE
+    assert call(H=2049) == SHAPE
+
+
 def _has_gpu():
     import torch
     return torch.cuda.device_count() > 0
@@ -288,3 +312,4 @@ def test_no_device_is_a_hip_error():
     n = ctypes.c_size_t(0)
     assert lib.svdq_lowrank_factors_workspace(512, 512, 16, ctypes.byref(n)) == 0
     assert lib.svdq_lowrank_factors(512, 512, 16, A, A, 1, 2, A, A, None, A, n.value, None) == HIP
+    assert lib.svdq_qk_norm_rope(64, 24, A, A, A, A, A, 1e-6, None) == HIP
