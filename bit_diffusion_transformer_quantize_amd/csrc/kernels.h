@@ -57,7 +57,7 @@ hipError_t launch_awq_linear(bool out_f32, int64_t M, int N, int K, const uint16
                              const uint16_t* bias, void* Y, hipStream_t s);
 
 // Q/K RMSNorm + rotary embedding of the QKV output, in place (qk_norm_rope.hip).
-hipError_t launch_qk_norm_rope(int64_t M, int heads, uint16_t* Y, const uint16_t* q_scale,
+hipError_t launch_qk_norm_rope(int64_t M, int heads, int64_t ld, uint16_t* Y, const uint16_t* q_scale,
                                const uint16_t* k_scale, const float* cosv, const float* sinv,
                                float eps, hipStream_t s);
 

@@ -4,7 +4,8 @@
 // The fused engine of the Nunchaku Lite page (axbrief.com, section "The
 // Trade-off Between Fused Kernels and Generality") takes the QKV projection
 // through the Q/K normalisation and the rotary embedding.  For one token the
-// projection output is [Q | K | V], H heads of 128 features each; for every
+// projection output row (ld features) starts with Q and K, H heads of 128
+// features each ([Q | K | V ...]); for every
 // head of Q and of K (each with its own scale vector):
 //   x_hat[d] = x[d] * (1 / sqrt(sum_d x[d]^2 / 128 + eps)) * scale[d],
 //   out[2i] = cos_i x_hat[2i] - sin_i x_hat[2i+1],
@@ -26,7 +27,7 @@ constexpr int QKR_LANES = 8;                          // lanes per (token, head)
 constexpr int QKR_ROWS = QKR_THREADS / QKR_LANES;     // (token, head) rows per workgroup
 
 __global__ __launch_bounds__(QKR_THREADS) void qk_norm_rope_kernel(
-    int64_t rows, int heads, uint16_t* __restrict__ Y, const uint16_t* __restrict__ q_scale,
+    int64_t rows, int heads, int64_t ld, uint16_t* __restrict__ Y, const uint16_t* __restrict__ q_scale,
     const uint16_t* __restrict__ k_scale, const float* __restrict__ cosv,
     const float* __restrict__ sinv, float eps) {
   const int64_t hr = (int64_t)blockIdx.x * QKR_ROWS + (threadIdx.x / QKR_LANES);
@@ -34,7 +35,6 @@ __global__ __launch_bounds__(QKR_THREADS) void qk_norm_rope_kernel(
   const int sub = threadIdx.x % QKR_LANES;
   const int64_t m = hr / (2 * heads);
   const int hh = (int)(hr - m * 2 * heads);            // 0..H-1: Q heads, H..2H-1: K heads
-  const int64_t ld = (int64_t)3 * heads * 128;
   uint16_t* y = Y + m * ld + (int64_t)hh * 128 + 16 * sub;
   const uint16_t* sc = (hh < heads ? q_scale : k_scale) + 16 * sub;
 
@@ -78,13 +78,13 @@ __global__ __launch_bounds__(QKR_THREADS) void qk_norm_rope_kernel(
 
 }  // namespace
 
-hipError_t launch_qk_norm_rope(int64_t M, int heads, uint16_t* Y, const uint16_t* q_scale,
+hipError_t launch_qk_norm_rope(int64_t M, int heads, int64_t ld, uint16_t* Y, const uint16_t* q_scale,
                                const uint16_t* k_scale, const float* cosv, const float* sinv,
                                float eps, hipStream_t s) {
   const int64_t rows = M * 2 * heads;
   const int64_t blocks = (rows + QKR_ROWS - 1) / QKR_ROWS;
   hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)blocks), dim3(QKR_THREADS), 0, s, rows,
-                     heads, Y, q_scale, k_scale, cosv, sinv, eps);
+                     heads, ld, Y, q_scale, k_scale, cosv, sinv, eps);
   return hipGetLastError();
 }
 

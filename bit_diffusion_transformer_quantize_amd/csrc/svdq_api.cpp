@@ -261,16 +261,45 @@ svdq_status svdq_lowrank_up(const svdq_desc* d, int64_t M, const float* T,
                                           d->N, T, lora_up, Y, (hipStream_t)stream));
 }
 
-svdq_status svdq_qk_norm_rope(int64_t M, int32_t heads, uint16_t* Y, const uint16_t* q_scale,
-                              const uint16_t* k_scale, const float* cos, const float* sin,
-                              float eps, void* stream) {
+namespace {
+svdq_status check_qk(int64_t M, int32_t heads, int64_t ld, const void* Y, const void* q_scale,
+                     const void* k_scale, const void* cos, const void* sin, float eps) {
   if (!ptr_ok(Y) || !ptr_ok(q_scale) || !ptr_ok(k_scale) || !ptr_ok(cos) || !ptr_ok(sin))
     return SVDQ_ERR_ARG;
   if (!(eps > 0.0f) || eps > 3.4e38f) return SVDQ_ERR_ARG;
   if (M < 1 || M > (int64_t(1) << 31) || heads < 1 || heads > 2048) return SVDQ_ERR_SHAPE;
+  if (ld < (int64_t)2 * heads * 128 || ld > (int64_t(1) << 24) || ld % 8 != 0) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+}  // namespace
+
+svdq_status svdq_qk_norm_rope(int64_t M, int32_t heads, int64_t ld, uint16_t* Y,
+                              const uint16_t* q_scale, const uint16_t* k_scale, const float* cos,
+                              const float* sin, float eps, void* stream) {
+  SVDQ_TRY(check_qk(M, heads, ld, Y, q_scale, k_scale, cos, sin, eps));
   SVDQ_TRY(check_device());
-  return from_hip(svdq::launch_qk_norm_rope(M, heads, Y, q_scale, k_scale, cos, sin, eps,
+  return from_hip(svdq::launch_qk_norm_rope(M, heads, ld, Y, q_scale, k_scale, cos, sin, eps,
                                             (hipStream_t)stream));
+}
+
+svdq_status svdq_linear_forward_qk(const svdq_desc* d, int64_t M, const void* ximage,
+                                   const void* wimage, int32_t heads, const uint16_t* q_scale,
+                                   const uint16_t* k_scale, const float* cos, const float* sin,
+                                   float eps, void* Y, void* stream) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows_k(M, d->K));
+  if (M > (int64_t(1) << 46) / d->N) return SVDQ_ERR_SHAPE;
+  if ((d->flags & SVDQ_FLAG_OUT_F32) != 0u) return SVDQ_ERR_ARG;
+  if (!ptr_ok(ximage) || !ptr_ok(wimage)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_qk(M, heads, d->N, Y, q_scale, k_scale, cos, sin, eps));
+  SVDQ_TRY(check_device());
+  const hipStream_t st = (hipStream_t)stream;
+  if (d->mode == SVDQ_MODE_FP4)
+    SVDQ_TRY(from_hip(svdq::launch_fp4_forward(false, M, d->N, d->K, d->rank, ximage, wimage, Y, st)));
+  else
+    SVDQ_TRY(from_hip(svdq::launch_int4_forward(false, M, d->N, d->K, d->rank, ximage, wimage, Y, st)));
+  return from_hip(svdq::launch_qk_norm_rope(M, heads, d->N, static_cast<uint16_t*>(Y), q_scale,
+                                            k_scale, cos, sin, eps, st));
 }
 
 svdq_status svdq_awq_pack_weight(int32_t N, int32_t K, const uint16_t* W, uint8_t* codes,

@@ -63,8 +63,10 @@ _SIGNATURES = {
     "svdq_awq_pack_weight": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "svdq_awq_linear": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint32,
                                        _vp, _vp]),
-    "svdq_qk_norm_rope": (ctypes.c_int, [_i64, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
-                                         _vp]),
+    "svdq_qk_norm_rope": (ctypes.c_int, [_i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
+                                         ctypes.c_float, _vp]),
+    "svdq_linear_forward_qk": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                                              ctypes.c_float, _vp, _vp]),
     "svdq_lowrank_factors_workspace": (ctypes.c_int, [_i32, _i32, _i32,
                                                       ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_lowrank_factors": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, ctypes.c_uint64, _i32, _vp,
@@ -389,15 +391,35 @@ HEAD_DIM = 128
 
 
 def svdq_qk_norm_rope(Y, heads: int, q_scale, k_scale, cos, sin, eps: float = 1e-6):
-    """Per-head RMSNorm + rotary embedding of the Q and K parts of the QKV
-    output Y (bf16 [M][3 heads 128]), in place; returns Y."""
-    M = Y.shape[0]
-    _need(Y, "Y", torch.bfloat16, (M, 3 * heads * HEAD_DIM))
+    """Per-head RMSNorm + rotary embedding of the Q and K columns (the first
+    2 heads 128) of Y (bf16 [M][ld]), in place; returns Y."""
+    M, ld = Y.shape
+    _need(Y, "Y", torch.bfloat16, (M, ld))
     _need(q_scale, "q_scale", torch.bfloat16, (HEAD_DIM,))
     _need(k_scale, "k_scale", torch.bfloat16, (HEAD_DIM,))
     _need(cos, "cos", torch.float32, (M, HEAD_DIM // 2))
     _need(sin, "sin", torch.float32, (M, HEAD_DIM // 2))
     _check("svdq_qk_norm_rope",
-           load().svdq_qk_norm_rope(M, heads, _p(Y), _p(q_scale), _p(k_scale), _p(cos), _p(sin),
-                                    float(eps), _stream()))
+           load().svdq_qk_norm_rope(M, heads, ld, _p(Y), _p(q_scale), _p(k_scale), _p(cos),
+                                    _p(sin), float(eps), _stream()))
+    return Y
+
+
+def svdq_linear_forward_qk(d: SvdqDesc, M: int, ximage, wimage, heads: int, q_scale, k_scale,
+                           cos, sin, eps: float = 1e-6, Y=None):
+    """The layer's forward followed by the Q/K RMSNorm + rotary embedding of
+    its first 2 heads 128 output columns (the GEMM, then the in-place pass)."""
+    if Y is None:
+        Y = torch.empty(M, d.N, dtype=torch.bfloat16, device=ximage.device)
+    _need(Y, "Y", torch.bfloat16, (M, d.N))
+    _need(ximage, "ximage", torch.uint8)
+    _need(wimage, "wimage", torch.uint8)
+    _need(q_scale, "q_scale", torch.bfloat16, (HEAD_DIM,))
+    _need(k_scale, "k_scale", torch.bfloat16, (HEAD_DIM,))
+    _need(cos, "cos", torch.float32, (M, HEAD_DIM // 2))
+    _need(sin, "sin", torch.float32, (M, HEAD_DIM // 2))
+    _check("svdq_linear_forward_qk",
+           load().svdq_linear_forward_qk(ctypes.byref(d), M, _p(ximage), _p(wimage), heads,
+                                         _p(q_scale), _p(k_scale), _p(cos), _p(sin), float(eps),
+                                         _p(Y), _stream()))
     return Y

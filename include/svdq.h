@@ -277,21 +277,34 @@ svdq_status svdq_lowrank_up(const svdq_desc* desc, int64_t M, const float* T,
  * Trade-off Between Fused Kernels and Generality": the fused engine takes
  * the QKV projection through the Q/K normalisation and the rotary
  * embedding; the pages leave the arithmetic open, and this library follows
- * the FLUX attention input).  Y: bf16 [M][3 * heads * 128], one row per
- * token laid out [Q | K | V], heads of 128 features (the output of
- * svdq_linear_forward of the QKV layer, N = 3 * heads * 128).  In place, for
- * every token m and every head of Q (scale q_scale) and of K (k_scale):
+ * the FLUX attention input).  Y: bf16 [M][ld], one row per token whose
+ * first 2 * heads * 128 features are Q and K, heads of 128 features each
+ * ([Q | K | V] for a QKV layer, ld = 3 * heads * 128; the rest of the row,
+ * e.g. V or a fused MLP part, is not touched).  In place, for every token m
+ * and every head of Q (scale q_scale) and of K (k_scale):
  *   x_hat[d] = x[d] * (1 / sqrt(sum_d x[d]^2 / 128 + eps)) * scale[d],
  *   out[2i]   = cos[m][i] x_hat[2i] - sin[m][i] x_hat[2i+1],
  *   out[2i+1] = sin[m][i] x_hat[2i] + cos[m][i] x_hat[2i+1],   i < 64,
- * in fp32, each output rounded to bf16 (RNE); V is not touched.
+ * in fp32, each output rounded to bf16 (RNE).
  * q_scale, k_scale: bf16 [128]; cos, sin: float32 [M][64] (the positional
- * angles belong to the model).  Limits: 1 <= M <= 2^31, 1 <= heads <= 2048;
- * eps > 0 and finite (else SVDQ_ERR_ARG).  Pointers as in the conventions
- * above. */
-svdq_status svdq_qk_norm_rope(int64_t M, int32_t heads, uint16_t* Y, const uint16_t* q_scale,
-                              const uint16_t* k_scale, const float* cos, const float* sin,
-                              float eps, void* stream);
+ * angles belong to the model).  Limits: 1 <= M <= 2^31, 1 <= heads <= 2048,
+ * 2 * heads * 128 <= ld <= 2^24, ld % 8 == 0; eps > 0 and finite (else
+ * SVDQ_ERR_ARG).  Pointers as in the conventions above. */
+svdq_status svdq_qk_norm_rope(int64_t M, int32_t heads, int64_t ld, uint16_t* Y,
+                              const uint16_t* q_scale, const uint16_t* k_scale, const float* cos,
+                              const float* sin, float eps, void* stream);
+
+/* svdq_linear_forward of a layer whose output starts with Q and K (the QKV
+ * projection, or a fused QKV + MLP projection), followed by the transform
+ * of svdq_qk_norm_rope on its first 2 * heads * 128 columns (ld = N), on the
+ * bf16 output: two launches on `stream` (the GEMM, then the in-place pass),
+ * in INT4 and FP4 mode alike.  Output bf16 only (SVDQ_FLAG_OUT_F32 is
+ * SVDQ_ERR_ARG); 2 * heads * 128 <= N; other limits as for
+ * svdq_linear_forward and svdq_qk_norm_rope. */
+svdq_status svdq_linear_forward_qk(const svdq_desc* desc, int64_t M, const void* ximage,
+                                   const void* wimage, int32_t heads, const uint16_t* q_scale,
+                                   const uint16_t* k_scale, const float* cos, const float* sin,
+                                   float eps, void* Y, void* stream);
 
 /* AWQ W4A16 linear layer: 4-bit weights, 16-bit activations (axbrief.com
  * page, section "The Mechanics of 4-Bit Efficiency and SVDQuant": the

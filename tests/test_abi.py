@@ -272,12 +272,12 @@ def test_lowrank_factors_validation():
 
 def test_qk_norm_rope_validation():
     f = _lib().svdq_qk_norm_rope
-    ok = dict(M=64, H=24, Y=A, qs=A, ks=A, c=A, s=A, eps=1e-6)
+    ok = dict(M=64, H=24, ld=9216, Y=A, qs=A, ks=A, c=A, s=A, eps=1e-6)
 
     def call(**kw):
         a = dict(ok)
         a.update(kw)
-        return f(a["M"], a["H"], a["Y"], a["qs"], a["ks"], a["c"], a["s"], a["eps"], None)
+        return f(a["M"], a["H"], a["ld"], a["Y"], a["qs"], a["ks"], a["c"], a["s"], a["eps"], None)
 
     assert call(Y=None) == ARG
     assert call(Y=MIS) == ARG
@@ -292,6 +292,17 @@ def test_qk_norm_rope_validation():
     assert call(M=0) == SHAPE
     assert call(H=0) == SHAPE
     assert call(H=2049) == SHAPE
+    assert call(ld=6143) == SHAPE            # shorter than Q and K
+    assert call(ld=9220) == SHAPE            # rows not 16-byte aligned
+    g = _lib().svdq_linear_forward_qk
+    d = _d(mode=1, K=512, N=9216, rank=32)
+    assert g(d, 64, A, A, 24, A, A, A, A, 1e-6, None, None) == ARG            # Y null
+    assert g(d, 64, None, A, 24, A, A, A, A, 1e-6, A, None) == ARG
+    assert g(_d(mode=1, K=512, N=9216, rank=32, flags=1), 64, A, A, 24, A, A, A, A, 1e-6, A,
+             None) == ARG                                                      # fp32 output
+    assert g(d, 64, A, A, 37, A, A, A, A, 1e-6, A, None) == SHAPE             # 2 H 128 > N
+    assert g(d, 64, A, A, 24, A, A, A, A, 0.0, A, None) == ARG
+    assert g(_d(mode=1, K=500, N=9216), 64, A, A, 24, A, A, A, A, 1e-6, A, None) == SHAPE
 
 
 def _has_gpu():
@@ -312,4 +323,6 @@ def test_no_device_is_a_hip_error():
     n = ctypes.c_size_t(0)
     assert lib.svdq_lowrank_factors_workspace(512, 512, 16, ctypes.byref(n)) == 0
     assert lib.svdq_lowrank_factors(512, 512, 16, A, A, 1, 2, A, A, None, A, n.value, None) == HIP
-    assert lib.svdq_qk_norm_rope(64, 24, A, A, A, A, A, 1e-6, None) == HIP
+    assert lib.svdq_qk_norm_rope(64, 24, 9216, A, A, A, A, A, 1e-6, None) == HIP
+    assert lib.svdq_linear_forward_qk(_d(mode=1, N=9216), 256, A, A, 24, A, A, A, A, 1e-6, A,
+                                      None) == HIP

@@ -129,3 +129,49 @@ def test_after_the_qkv_layer(mode):
     for name, g, w in (("Q", got[:, :HD], Q_o), ("K", got[:, HD:2 * HD], K_o)):
         rms = np.sqrt(np.mean(w ** 2))
         assert np.max(np.abs(g - w)) <= 3e-2 * rms, f"{name}: {np.max(np.abs(g - w)) / rms:.3g} rms"
+
+
+@pytest.mark.parametrize("mode,H,extra,M", [("fp4", 3, 0, 200), ("fp4", 2, 512, 333),
+                                             ("int4", 3, 0, 200), ("fp4", 24, 12288, 256)])
+def test_forward_qk(mode, H, extra, M):
+    """svdq_linear_forward_qk: the QKV (or fused QKV + MLP, `extra` more
+    columns) layer with the Q/K transform.  Q and K against the oracle layer
+    followed by the oracle transform; the columns after Q and K bit-identical
+    to svdq_linear_forward, and the whole output to svdq_linear_forward
+    followed by svdq_qk_norm_rope.  The last case is the FLUX single-stream
+    shape (24 heads, N = 21504)."""
+    S = _S()
+    K = 3072 if H == 24 else 512
+    N = 3 * H * 128 + extra
+    _say("forward_qk", mode, M, K, N, H)
+    spec = WL.LinearSpec("qkv_fwd", M, K, N, 32, mode, x_outliers=4, x_factor=20.0)
+    X, W, b = WL.draw(spec, seed=H + extra)
+    xb, wb, bb = WL.bits(X), WL.bits(W), WL.bits(b)
+    lam, L1, L2, wc_o, ws_o = oracle_offline(xb, wb, 32, mode)
+    xc_o, xs_o, T_o, _ = O.quantize_act(xb, lam, L1, mode)
+    Y_o = O.forward(xc_o, xs_o, T_o, wc_o, ws_o, L2, bb, mode)
+    _, qs, ks, c, s = _inputs(M, H, seed=5)
+    HD = H * 128
+    Q_o, K_o, _ = O.qk_norm_rope(Y_o[:, :3 * HD], H, O.bf16_to_f32(qs), O.bf16_to_f32(ks),
+                                 c.astype(np.float64), s.astype(np.float64), 1e-6)
+    d = S.desc(mode, K, N, 32)
+    lamd = torch.from_numpy(lam).to(DEV)
+    ld = WL.from_bits(np.ascontiguousarray(L1.T)).to(DEV)
+    lu = WL.from_bits(np.ascontiguousarray(L2.T)).to(DEV)
+    _, _, _, ximg = S.svdq_quantize_act(d, X.to(DEV), lamd, ld)
+    wc, ws = S.svdq_pack_weight(d, W.to(DEV), lamd, ld, lu)
+    wimg = S.svdq_prepare_weight(d, wc, ws, lu, b.to(DEV))
+    args = (WL.from_bits(qs).to(DEV), WL.from_bits(ks).to(DEV), torch.from_numpy(c).to(DEV),
+            torch.from_numpy(s).to(DEV))
+    Yq = S.svdq_linear_forward_qk(d, M, ximg, wimg, H, *args)
+    Yp = S.svdq_linear_forward(d, M, ximg, wimg)
+    Yu = Yp.clone()
+    S.svdq_qk_norm_rope(Yu, H, *args)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f32(WL.bits(Yq.cpu())).astype(np.float64)
+    for name, g, w in (("Q", got[:, :HD], Q_o), ("K", got[:, HD:2 * HD], K_o)):
+        rms = np.sqrt(np.mean(w ** 2))
+        assert np.max(np.abs(g - w)) <= 3e-2 * rms, f"{name}: {np.max(np.abs(g - w)) / rms:.3g} rms"
+    assert np.array_equal(WL.bits(Yq[:, 2 * HD:].cpu()), WL.bits(Yp[:, 2 * HD:].cpu())), \
+        "columns after Q and K"
+    assert np.array_equal(WL.bits(Yq.cpu()), WL.bits(Yu.cpu())), "forward + pass"
