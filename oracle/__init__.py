@@ -9,3 +9,4 @@ from .awq_oracle import *  # noqa: F401,F403
 from .gelu_oracle import *  # noqa: F401,F403
 from .rsvd_oracle import *  # noqa: F401,F403
 from .qkv_oracle import *  # noqa: F401,F403
+from .nvfp4_oracle import *  # noqa: F401,F403
