@@ -61,6 +61,20 @@ hipError_t launch_qk_norm_rope(int64_t M, int heads, int64_t ld, uint16_t* Y, co
                                const uint16_t* k_scale, const float* cosv, const float* sinv,
                                float eps, hipStream_t s);
 
+// NVFP4 variant (nvfp4.hip).
+hipError_t launch_nvfp4_quantize_act(int64_t M, int K, const uint16_t* X, const float* lambda,
+                                     const float* g, uint8_t* codes, uint8_t* scales,
+                                     hipStream_t s);
+hipError_t launch_nvfp4_scale_from_absmax(int n, const float* amax, float* g, hipStream_t s);
+hipError_t launch_nvfp4_pack_weight(int N, int K, int rank, const uint16_t* W, const float* lambda,
+                                    const uint16_t* lora_down, const uint16_t* lora_up,
+                                    uint8_t* codes, uint8_t* scales, float* g, hipStream_t s);
+hipError_t launch_nvfp4_linear(bool out_f32, int64_t M, int N, int K, int rank,
+                               const uint8_t* xcodes, const uint8_t* xscales, const float* gx,
+                               const uint8_t* wcodes, const uint8_t* wscales, const float* gw,
+                               const float* T, const uint16_t* lora_up, const uint16_t* bias,
+                               void* Y, hipStream_t s);
+
 // Randomized truncated SVD of the smoothed weight (lowrank_factors.hip).
 size_t lowrank_factors_workspace_bytes(int N, int K, int rank);
 hipError_t launch_lowrank_factors(int N, int K, int rank, const uint16_t* W, const float* lambda,

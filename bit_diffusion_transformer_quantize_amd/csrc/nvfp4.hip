@@ -1,0 +1,363 @@
+// The NVFP4 variant of the W4A4 layer on gfx950.
+//
+// NVFP4 (the 4-bit float format the pages name for the FP4 path: Nunchaku
+// Lite page on axbrief.com, sections "The Mechanics of 4-Bit Efficiency and
+// SVDQuant" and "Hardware Specialization and the Compression Workflow"; the
+// layout is NVIDIA's published one) stores E2M1 codes in blocks of 16 along K
+// with an FP8 E4M3 scale per block and one fp32 scale g per tensor:
+//   t = fp32(6 g); per block a = max |v|, s = E4M3_RNE_sat(fp32(a / t)),
+//   d = fp32(s g), code = E2M1_RNE_sat(fp32(v / d)) (all 0 when s = 0);
+//   value = code * s * g.
+// gfx950's scaled matrix instructions take only power-of-two (E8M0) block
+// scales for 32 elements, so an E4M3 scale per 16 cannot ride in them.  A
+// code times its block scale has at most 6 significant bits, which bf16
+// holds exactly, so the GEMM dequantizes both operands to bf16 in LDS and
+// runs the bf16 matrix instruction: every product is exact in fp32 and the
+// sums are fp32, as for the other modes.  g_x g_w is applied once per output.
+#include <algorithm>
+
+#include "common.h"
+#include "gemm_common.h"
+#include "kernels.h"
+#include "weight_residual.h"
+
+namespace svdq {
+namespace {
+
+constexpr int NV_BLOCK = 16;
+
+// Byte of E4M3_RNE_sat(v) for v >= 0: nearest value of the E4M3 grid
+// (normals (1 + m/8) 2^e for e = -6..8, subnormals m 2^-9), ties to the even
+// mantissa, 448 for everything from 448 up.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  if (!(v < 448.0f)) return 0x7Eu;
+  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);  // 0..8 (8 = 2^-6)
+  const uint32_t b = __float_as_uint(v);
+  int e = (int)(b >> 23) - 127;
+  uint32_t q = (b >> 20) & 7u;
+  const uint32_t rem = b & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+  if (q == 8u) {
+    q = 0;
+    ++e;
+  }
+  const uint32_t byte = ((uint32_t)(e + 7) << 3) | q;
+  return byte > 0x7Eu ? 0x7Eu : byte;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Value of a 4-bit E2M1 code (bit 3 = sign): magnitudes 0, .5, 1, 1.5, 2, 3,
+// 4, 6 built from the exponent and mantissa bits.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const uint32_t mag = e == 0 ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
+  return __uint_as_float(mag | ((c & 8u) << 28));
+}
+
+// One block of 16 values: codes (two dwords, element 2j in the low nibble of
+// byte j) and the scale byte, for per-tensor scale g and t = fp32(6 g).
+__device__ __forceinline__ void nvfp4_block(const float (&v)[16], float g, float t, uint32_t& w0,
+                                            uint32_t& w1, uint32_t& sbyte) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+  sbyte = e4m3_encode(a / t);
+  const float sv = e4m3_value(sbyte);
+  w0 = w1 = 0u;
+  if (sv > 0.f) {
+    const float d = __fmul_rn(sv, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w0 |= e2m1_code(v[i] / d) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w1 |= e2m1_code(v[8 + i] / d) << (4 * i);
+  }
+}
+
+// ------------------------------------------------------------------ activations
+// One thread per block of 16: X_hat = bf16_RNE(fp32(X / lambda)), quantized
+// with the per-tensor scale *g.
+__global__ __launch_bounds__(256) void nvfp4_act_kernel(int64_t M, int K,
+                                                        const uint16_t* __restrict__ X,
+                                                        const float* __restrict__ lambda,
+                                                        const float* __restrict__ gptr,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  const int nbk = K / NV_BLOCK;
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= M * nbk) return;
+  const int64_t m = blk / nbk;
+  const int kb = (int)(blk - m * nbk);
+  const int k0 = kb * NV_BLOCK;
+  const v4u xa = *reinterpret_cast<const v4u*>(X + m * K + k0);
+  const v4u xb = *reinterpret_cast<const v4u*>(X + m * K + k0 + 8);
+  const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float x = bf16_to_f32((xw[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu);
+    v[i] = bf16_to_f32(f32_to_bf16(x / lambda[k0 + i]));
+  }
+  const float g = *gptr;
+  uint32_t w0, w1, sb;
+  nvfp4_block(v, g, __fmul_rn(6.0f, g), w0, w1, sb);
+  *reinterpret_cast<v2u*>(codes + m * (K / 2) + kb * 8) = v2u{w0, w1};
+  scales[m * nbk + kb] = (uint8_t)sb;
+}
+
+// g = fp32(max_k amax[k] / 2688), 1 when the maximum is 0 (one workgroup).
+__global__ __launch_bounds__(256) void nvfp4_scale_from_absmax_kernel(int n,
+                                                                      const float* __restrict__ amax,
+                                                                      float* __restrict__ g) {
+  __shared__ float red[4];
+  float a = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) a = fmaxf(a, amax[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    *g = m > 0.f ? m / 2688.0f : 1.0f;
+  }
+}
+
+// ------------------------------------------------------------------ weights
+// The residual R of the smoothed weight, 16 rows x 64 columns per wave step
+// (lane: row l % 16, columns 16 (l / 16)..), as the other modes' packer.
+constexpr int NVW_ROWS = 16;
+
+__global__ __launch_bounds__(64) void nvfp4_zero_kernel(uint32_t* __restrict__ p) {
+  if (threadIdx.x == 0) *p = 0u;
+}
+
+// max |R| over the tensor into *amax_bits (the bits of a non-negative float
+// order like the values, so an integer maximum is the float maximum).
+__global__ __launch_bounds__(256) void nvfp4_weight_amax_kernel(
+    int N, int K, int rank, const uint16_t* __restrict__ W, const float* __restrict__ lambda,
+    const uint16_t* __restrict__ lora_down, const uint16_t* __restrict__ lora_up,
+    uint32_t* __restrict__ amax_bits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * NVW_ROWS + (lane & 15);
+  float a = 0.f;
+  for (int t = wave; t < (K >> 6); t += 4) {
+    float r[16];
+    weight_residual16(n, t * 64 + (lane >> 4) * 16, K, rank, W, lambda, lora_down, lora_up, r);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(r[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+  if (lane == 0) atomicMax(amax_bits, __float_as_uint(a));
+}
+
+// In place: the maximum's bits -> g = fp32(amax / 2688), 1 when it is 0.
+__global__ __launch_bounds__(64) void nvfp4_weight_scale_kernel(float* __restrict__ g) {
+  if (threadIdx.x == 0) {
+    const float a = __uint_as_float(*reinterpret_cast<const uint32_t*>(g));
+    *g = a > 0.f ? a / 2688.0f : 1.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void nvfp4_weight_quant_kernel(
+    int N, int K, int rank, const uint16_t* __restrict__ W, const float* __restrict__ lambda,
+    const uint16_t* __restrict__ lora_down, const uint16_t* __restrict__ lora_up,
+    const float* __restrict__ gptr, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * NVW_ROWS + (lane & 15);
+  const float g = *gptr;
+  const float t6 = __fmul_rn(6.0f, g);
+  for (int t = wave; t < (K >> 6); t += 4) {
+    const int k0 = t * 64 + (lane >> 4) * 16;
+    float r[16];
+    weight_residual16(n, k0, K, rank, W, lambda, lora_down, lora_up, r);
+    uint32_t w0, w1, sb;
+    nvfp4_block(r, g, t6, w0, w1, sb);
+    *reinterpret_cast<v2u*>(codes + (int64_t)n * (K / 2) + k0 / 2) = v2u{w0, w1};
+    scales[(int64_t)n * (K / NV_BLOCK) + k0 / NV_BLOCK] = (uint8_t)sb;
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+// A 128 x 128 output tile per workgroup (4 waves of 64 x 64, 2 x 2 MFMA
+// tiles each), K in steps of 32 (two blocks): every thread dequantizes one
+// block of 16 of X and one of W into bf16 rows in LDS (the next step's codes
+// and scales are loaded while the current step runs), then each wave issues
+// 8 v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the
+// transposed accumulator layout of gemm_common.h).  Epilogue: * g_x g_w,
+// + T L2 on the same instruction (T as a bf16 hi/lo split), + bias.
+constexpr int NV_BM = 128, NV_BN = 128, NV_KS = 32;
+constexpr int NV_LDS_ROW = NV_KS + 8;  // bf16 elements per LDS row (16-byte pad)
+
+struct NvRaw {
+  v2u xc, wc;
+  uint32_t xs, ws;
+};
+
+__device__ __forceinline__ void nv_dequant16(v2u c, float s, uint16_t* dst) {
+  v4u o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t byte = (c[h] >> (8 * q)) & 0xFFu;
+      o[h][q] = pack_bf16x2(__fmul_rn(e2m1_value(byte & 0xFu), s),
+                            __fmul_rn(e2m1_value(byte >> 4), s));
+    }
+  reinterpret_cast<v4u*>(dst)[0] = o[0];
+  reinterpret_cast<v4u*>(dst)[1] = o[1];
+}
+
+__global__ __launch_bounds__(256) void nvfp4_gemm_kernel(
+    int64_t M, int N, int K, int rank, int out_f32, const uint8_t* __restrict__ xcodes,
+    const uint8_t* __restrict__ xscales, const float* __restrict__ gx,
+    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales,
+    const float* __restrict__ gw, const float* __restrict__ T,
+    const uint16_t* __restrict__ lora_up, const uint16_t* __restrict__ bias,
+    void* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs_l[NV_BM * NV_LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t ws_l[NV_BN * NV_LDS_ROW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * NV_BM;
+  const int n0 = blockIdx.y * NV_BN;
+  const int nbk = K / NV_BLOCK;
+  // this thread's block of 16 in each operand: row tid / 2, half tid % 2
+  const int lr = tid >> 1, hf = tid & 1;
+  const int64_t xrow = std::min<int64_t>(m0 + lr, M - 1);  // rows past M are read, not stored
+  const uint8_t* xcp = xcodes + xrow * (K / 2) + hf * 8;
+  const uint8_t* xsp = xscales + xrow * nbk + hf;
+  const uint8_t* wcp = wcodes + (int64_t)(n0 + lr) * (K / 2) + hf * 8;
+  const uint8_t* wsp = wscales + (int64_t)(n0 + lr) * nbk + hf;
+  auto load = [&](int ks, NvRaw& r) {
+    r.xc = *reinterpret_cast<const v2u*>(xcp + ks * (NV_KS / 2));
+    r.wc = *reinterpret_cast<const v2u*>(wcp + ks * (NV_KS / 2));
+    r.xs = xsp[ks * 2];
+    r.ws = wsp[ks * 2];
+  };
+  v16f acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  const int nks = K / NV_KS;
+  NvRaw cur, nxt;
+  load(0, cur);
+  const int l32 = lane & 31, kh = (lane >> 5) * 8;
+  for (int ks = 0; ks < nks; ++ks) {
+    load(std::min(ks + 1, nks - 1), nxt);
+    nv_dequant16(cur.xc, e4m3_value(cur.xs), xs_l + lr * NV_LDS_ROW + hf * 16);
+    nv_dequant16(cur.wc, e4m3_value(cur.ws), ws_l + lr * NV_LDS_ROW + hf * 16);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < NV_KS; kk += 16) {
+      v8bf af[2], bfr[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        af[t] = *reinterpret_cast<const v8bf*>(ws_l + (wn * 64 + 32 * t + l32) * NV_LDS_ROW + kk + kh);
+        bfr[t] = *reinterpret_cast<const v8bf*>(xs_l + (wm * 64 + 32 * t + l32) * NV_LDS_ROW + kk + kh);
+      }
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc)
+          acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tc], bfr[tr], acc[tr][tc], 0, 0, 0);
+    }
+    __syncthreads();
+    cur = nxt;
+  }
+
+  const int64_t mbase = m0 + wm * 64;
+  const int nbase = n0 + wn * 64;
+  const float gg = __fmul_rn(*gx, *gw);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = __fmul_rn(acc[a][b][i], gg);
+  // T L2: T rows (B operand, bf16 hi + lo), lora_up rows (A operand)
+  for (int q0 = 0; q0 < rank; q0 += 16) {
+    v8bf lu[2], thi[2], tlo[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      lu[t] = *reinterpret_cast<const v8bf*>(lora_up + (int64_t)(nbase + 32 * t + l32) * rank + q0 + kh);
+      const int64_t tm = std::min<int64_t>(mbase + 32 * t + l32, M - 1);
+      const v4f t0 = *reinterpret_cast<const v4f*>(T + tm * rank + q0 + kh);
+      const v4f t1 = *reinterpret_cast<const v4f*>(T + tm * rank + q0 + kh + 4);
+      const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = f32_to_bf16(tv[e]);
+        thi[t][e] = __builtin_bit_cast(__bf16, (uint16_t)h);
+        tlo[t][e] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16(tv[e] - bf16_to_f32(h)));
+      }
+    }
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[tc], thi[tr], acc[tr][tc], 0, 0, 0);
+        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[tc], tlo[tr], acc[tr][tc], 0, 0, 0);
+      }
+  }
+  if (bias != nullptr) {
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float bv = bf16_to_f32(bias[nbase + 32 * tc + acc_row(i, lane)]);
+#pragma unroll
+        for (int tr = 0; tr < 2; ++tr) acc[tr][tc][i] = __fadd_rn(acc[tr][tc][i], bv);
+      }
+  }
+  store_tiles_t<2, 2>(acc, M, N, mbase, nbase, lane, out_f32 != 0, Y);
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_quantize_act(int64_t M, int K, const uint16_t* X, const float* lambda,
+                                     const float* g, uint8_t* codes, uint8_t* scales,
+                                     hipStream_t s) {
+  const int64_t blocks = (M * (K / NV_BLOCK) + 255) / 256;
+  hipLaunchKernelGGL(nvfp4_act_kernel, dim3((unsigned)blocks), dim3(256), 0, s, M, K, X, lambda,
+                     g, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_scale_from_absmax(int n, const float* amax, float* g, hipStream_t s) {
+  hipLaunchKernelGGL(nvfp4_scale_from_absmax_kernel, dim3(1), dim3(256), 0, s, n, amax, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_pack_weight(int N, int K, int rank, const uint16_t* W, const float* lambda,
+                                    const uint16_t* lora_down, const uint16_t* lora_up,
+                                    uint8_t* codes, uint8_t* scales, float* g, hipStream_t s) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(g);
+  hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(64), 0, s, bits);
+  hipLaunchKernelGGL(nvfp4_weight_amax_kernel, dim3(N / NVW_ROWS), dim3(256), 0, s, N, K, rank, W,
+                     lambda, lora_down, lora_up, bits);
+  hipLaunchKernelGGL(nvfp4_weight_scale_kernel, dim3(1), dim3(64), 0, s, g);
+  hipLaunchKernelGGL(nvfp4_weight_quant_kernel, dim3(N / NVW_ROWS), dim3(256), 0, s, N, K, rank, W,
+                     lambda, lora_down, lora_up, g, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_linear(bool out_f32, int64_t M, int N, int K, int rank,
+                               const uint8_t* xcodes, const uint8_t* xscales, const float* gx,
+                               const uint8_t* wcodes, const uint8_t* wscales, const float* gw,
+                               const float* T, const uint16_t* lora_up, const uint16_t* bias,
+                               void* Y, hipStream_t s) {
+  const dim3 grid((unsigned)((M + NV_BM - 1) / NV_BM), N / NV_BN);
+  hipLaunchKernelGGL(nvfp4_gemm_kernel, grid, dim3(256), 0, s, M, N, K, rank, (int)out_f32, xcodes,
+                     xscales, gx, wcodes, wscales, gw, T, lora_up, bias, Y);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

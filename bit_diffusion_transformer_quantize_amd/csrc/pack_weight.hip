@@ -10,6 +10,7 @@
 // are bit-identical to the definition.
 #include "common.h"
 #include "kernels.h"
+#include "weight_residual.h"
 
 namespace svdq {
 
@@ -137,33 +138,7 @@ __global__ __launch_bounds__(PW_THREADS) void pack_weight_kernel(
   for (int t = wave; t < ntiles; t += 4) {
     const int k0 = t * 64 + j * 16;
     float r[16];
-    const v4u wa = *reinterpret_cast<const v4u*>(W + (int64_t)n * K + k0);
-    const v4u wb = *reinterpret_cast<const v4u*>(W + (int64_t)n * K + k0 + 8);
-    const uint32_t ww[8] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float w = bf16_to_f32((ww[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu);
-      r[i] = __fmul_rn(w, lambda[k0 + i]);  // W_hat
-    }
-    if (rank > 0) {
-      float acc[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      for (int q = 0; q < rank; ++q) {
-        const float u = bf16_to_f32(lora_up[(int64_t)n * rank + q]);  // L2[q][n]
-        const uint16_t* ld = lora_down + (int64_t)q * K + k0;           // L1[k][q]
-        const v4u da = *reinterpret_cast<const v4u*>(ld);
-        const v4u db = *reinterpret_cast<const v4u*>(ld + 8);
-        const uint32_t dd[8] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3]};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float d = bf16_to_f32((dd[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu);
-          acc[i] = __fadd_rn(acc[i], __fmul_rn(d, u));  // product exact in fp32
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] = __fsub_rn(r[i], acc[i]);
-    }
+    weight_residual16(n, k0, K, rank, W, lambda, lora_down, lora_up, r);
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(r[i]));

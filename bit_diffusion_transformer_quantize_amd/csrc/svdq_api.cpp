@@ -302,6 +302,68 @@ svdq_status svdq_linear_forward_qk(const svdq_desc* d, int64_t M, const void* xi
                                             k_scale, cos, sin, eps, st));
 }
 
+namespace {
+svdq_status check_nv_shape(int64_t M, int32_t N, int32_t K, int32_t rank) {
+  if (K < 128 || K % 128 != 0 || K > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (N < 128 || N % 128 != 0 || N > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (M < 1 || M > (int64_t(1) << 31) || M * (int64_t)K > (int64_t(1) << 36)) return SVDQ_ERR_SHAPE;
+  if (rank < 0 || rank > 256 || rank % 16 != 0) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+}  // namespace
+
+svdq_status svdq_nvfp4_scale_from_absmax(int32_t n, const float* amax, float* g, void* stream) {
+  if (!ptr_ok(amax) || !ptr_ok(g)) return SVDQ_ERR_ARG;
+  if (n < 1) return SVDQ_ERR_SHAPE;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_nvfp4_scale_from_absmax(n, amax, g, (hipStream_t)stream));
+}
+
+svdq_status svdq_nvfp4_quantize_act(int64_t M, int32_t K, const uint16_t* X, const float* lambda,
+                                    const float* g, uint8_t* xcodes, uint8_t* xscales,
+                                    void* stream) {
+  if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(g) || !ptr_ok(xcodes) || !ptr_ok(xscales))
+    return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_nv_shape(M, 128, K, 0));
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_nvfp4_quantize_act(M, K, X, lambda, g, xcodes, xscales,
+                                                  (hipStream_t)stream));
+}
+
+svdq_status svdq_nvfp4_pack_weight(int32_t N, int32_t K, int32_t rank, const uint16_t* W,
+                                   const float* lambda, const uint16_t* lora_down,
+                                   const uint16_t* lora_up, uint8_t* wcodes, uint8_t* wscales,
+                                   float* g, void* stream) {
+  if (!ptr_ok(W) || !ptr_ok(lambda) || !ptr_ok(wcodes) || !ptr_ok(wscales) || !ptr_ok(g))
+    return SVDQ_ERR_ARG;
+  if (rank > 0 ? (!ptr_ok(lora_down) || !ptr_ok(lora_up))
+               : (lora_down != nullptr || lora_up != nullptr))
+    return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_nv_shape(1, N, K, rank));
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_nvfp4_pack_weight(N, K, rank, W, lambda, lora_down, lora_up,
+                                                 wcodes, wscales, g, (hipStream_t)stream));
+}
+
+svdq_status svdq_nvfp4_linear(int64_t M, int32_t N, int32_t K, int32_t rank,
+                              const uint8_t* xcodes, const uint8_t* xscales, const float* g_x,
+                              const uint8_t* wcodes, const uint8_t* wscales, const float* g_w,
+                              const float* T, const uint16_t* lora_up, const uint16_t* bias,
+                              uint32_t flags, void* Y, void* stream) {
+  if ((flags & ~SVDQ_FLAG_OUT_F32) != 0u) return SVDQ_ERR_ARG;
+  if (!ptr_ok(xcodes) || !ptr_ok(xscales) || !ptr_ok(g_x) || !ptr_ok(wcodes) || !ptr_ok(wscales) ||
+      !ptr_ok(g_w) || !ptr_ok(Y) || !opt_ok(bias))
+    return SVDQ_ERR_ARG;
+  if (rank > 0 ? (!ptr_ok(T) || !ptr_ok(lora_up)) : (T != nullptr || lora_up != nullptr))
+    return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_nv_shape(M, N, K, rank));
+  if (M > (int64_t(1) << 46) / N) return SVDQ_ERR_SHAPE;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_nvfp4_linear((flags & SVDQ_FLAG_OUT_F32) != 0u, M, N, K, rank,
+                                            xcodes, xscales, g_x, wcodes, wscales, g_w, T, lora_up,
+                                            bias, Y, (hipStream_t)stream));
+}
+
 svdq_status svdq_awq_pack_weight(int32_t N, int32_t K, const uint16_t* W, uint8_t* codes,
                                  float* scales, uint8_t* zeros, void* stream) {
   if (!ptr_ok(W) || !ptr_ok(codes) || !ptr_ok(scales) || !ptr_ok(zeros)) return SVDQ_ERR_ARG;

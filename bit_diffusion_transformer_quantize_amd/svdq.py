@@ -67,6 +67,12 @@ _SIGNATURES = {
                                          ctypes.c_float, _vp]),
     "svdq_linear_forward_qk": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                               ctypes.c_float, _vp, _vp]),
+    "svdq_nvfp4_scale_from_absmax": (ctypes.c_int, [_i32, _vp, _vp, _vp]),
+    "svdq_nvfp4_quantize_act": (ctypes.c_int, [_i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_nvfp4_pack_weight": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _vp]),
+    "svdq_nvfp4_linear": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, ctypes.c_uint32, _vp, _vp]),
     "svdq_lowrank_factors_workspace": (ctypes.c_int, [_i32, _i32, _i32,
                                                       ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_lowrank_factors": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, ctypes.c_uint64, _i32, _vp,
@@ -422,4 +428,79 @@ def svdq_linear_forward_qk(d: SvdqDesc, M: int, ximage, wimage, heads: int, q_sc
            load().svdq_linear_forward_qk(ctypes.byref(d), M, _p(ximage), _p(wimage), heads,
                                          _p(q_scale), _p(k_scale), _p(cos), _p(sin), float(eps),
                                          _p(Y), _stream()))
+    return Y
+
+
+NVFP4_BLOCK = 16
+
+
+def svdq_nvfp4_scale_from_absmax(amax, g=None):
+    """g = fp32(max(amax) / 2688) (1 if the maximum is 0), as a 1-element
+    device tensor."""
+    _need(amax, "amax", torch.float32, (amax.numel(),))
+    if g is None:
+        g = torch.empty(1, dtype=torch.float32, device=amax.device)
+    _need(g, "g", torch.float32, (1,))
+    _check("svdq_nvfp4_scale_from_absmax",
+           load().svdq_nvfp4_scale_from_absmax(amax.numel(), _p(amax), _p(g), _stream()))
+    return g
+
+
+def svdq_nvfp4_quantize_act(X, lam, g, xcodes=None, xscales=None):
+    """NVFP4 codes [M][K/2] and E4M3 scales [M][K/16] of X_hat = X / lambda."""
+    M, K = X.shape
+    _need(X, "X", torch.bfloat16, (M, K))
+    _need(lam, "lambda", torch.float32, (K,))
+    _need(g, "g", torch.float32, (1,))
+    if xcodes is None:
+        xcodes = torch.empty(M, K // 2, dtype=torch.uint8, device=X.device)
+    if xscales is None:
+        xscales = torch.empty(M, K // NVFP4_BLOCK, dtype=torch.uint8, device=X.device)
+    _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
+    _need(xscales, "xscales", torch.uint8, (M, K // NVFP4_BLOCK))
+    _check("svdq_nvfp4_quantize_act",
+           load().svdq_nvfp4_quantize_act(M, K, _p(X), _p(lam), _p(g), _p(xcodes), _p(xscales),
+                                          _stream()))
+    return xcodes, xscales
+
+
+def svdq_nvfp4_pack_weight(W, lam, rank: int, lora_down=None, lora_up=None):
+    """(codes [N][K/2], E4M3 scales [N][K/16], g [1]) of the weight residual."""
+    N, K = W.shape
+    _need(W, "W", torch.bfloat16, (N, K))
+    _need(lam, "lambda", torch.float32, (K,))
+    _need(lora_down, "lora_down", torch.bfloat16, (rank, K), optional=rank == 0)
+    _need(lora_up, "lora_up", torch.bfloat16, (N, rank), optional=rank == 0)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=W.device)
+    scales = torch.empty(N, K // NVFP4_BLOCK, dtype=torch.uint8, device=W.device)
+    g = torch.empty(1, dtype=torch.float32, device=W.device)
+    _check("svdq_nvfp4_pack_weight",
+           load().svdq_nvfp4_pack_weight(N, K, rank, _p(W), _p(lam), _p(lora_down), _p(lora_up),
+                                         _p(codes), _p(scales), _p(g), _stream()))
+    return codes, scales, g
+
+
+def svdq_nvfp4_linear(xcodes, xscales, g_x, wcodes, wscales, g_w, T=None, lora_up=None,
+                      bias=None, Y=None, out_f32: bool = False):
+    """Y = deq(X) deq(W)^T + T L2 + bias for NVFP4 operands."""
+    M, K2 = xcodes.shape
+    N = wcodes.shape[0]
+    K = 2 * K2
+    rank = 0 if lora_up is None else lora_up.shape[1]
+    out_dtype = torch.float32 if out_f32 else torch.bfloat16
+    _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
+    _need(xscales, "xscales", torch.uint8, (M, K // NVFP4_BLOCK))
+    _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
+    _need(wscales, "wscales", torch.uint8, (N, K // NVFP4_BLOCK))
+    _need(g_x, "g_x", torch.float32, (1,))
+    _need(g_w, "g_w", torch.float32, (1,))
+    _need(T, "T", torch.float32, (M, rank), optional=rank == 0)
+    _need(bias, "bias", torch.bfloat16, (N,), optional=True)
+    if Y is None:
+        Y = torch.empty(M, N, dtype=out_dtype, device=xcodes.device)
+    _need(Y, "Y", out_dtype, (M, N))
+    _check("svdq_nvfp4_linear",
+           load().svdq_nvfp4_linear(M, N, K, rank, _p(xcodes), _p(xscales), _p(g_x), _p(wcodes),
+                                    _p(wscales), _p(g_w), _p(T), _p(lora_up), _p(bias),
+                                    SVDQ_FLAG_OUT_F32 if out_f32 else 0, _p(Y), _stream()))
     return Y

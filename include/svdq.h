@@ -140,6 +140,60 @@ svdq_status svdq_calibrate_absmax(int64_t R, int32_t K, const uint16_t* A, float
 svdq_status svdq_lambda_from_absmax(int32_t K, const float* xmax, const float* wmax,
                                     float* lambda, void* stream);
 
+/* NVFP4 variant (axbrief.com page, sections "The Mechanics of 4-Bit
+ * Efficiency and SVDQuant" and "Hardware Specialization and the Compression
+ * Workflow": NVFP4 is the pages' 4-bit float format; its layout is NVIDIA's
+ * published one).  The same layer (smoothing, rank-r 16-bit branch, 4-bit
+ * residual), with both operands in NVFP4:
+ *   codes  : E2M1 nibbles as in SVDQ_MODE_FP4, [rows][K/2];
+ *   scales : uint8 [rows][K/16], the E4M3 scale of each block of 16 along K
+ *            (bias 7, subnormals m 2^-9, largest finite 448 = byte 0x7E);
+ *   g      : one float32 per tensor (device memory), > 0.
+ * Quantization of a row-major tensor V: t = fp32(6 g); per block a = max |v|,
+ * s = E4M3_RNE_sat(fp32(a / t)) (nearest E4M3 value, ties to the even
+ * mantissa, 448 from 448 up), d = fp32(s * g), code = the E2M1 code of
+ * fp32(v / d) as in SVDQ_MODE_FP4 (all codes 0 when s = 0); value = code * s
+ * * g.  The per-tensor scale is g = fp32(amax / 2688) (2688 = 6 * 448), 1
+ * when amax = 0.  Codes and scales are bit-identical to this definition.
+ * gfx950's block-scaled matrix instructions take only power-of-two scales
+ * per 32 elements, so the GEMM dequantizes both operands to bf16 (exact:
+ * code * s has at most 6 significant bits) and runs the bf16 matrix
+ * instruction; it is slower than SVDQ_MODE_FP4 (MXFP4), which gfx950 runs
+ * natively.  Shape limits: K, N multiples of 128, <= 2^20; 1 <= M <= 2^31,
+ * M * K <= 2^36; rank % 16 == 0, 0 <= rank <= 256. */
+
+/* g = fp32(max_i amax[i] / 2688), or 1 if the maximum is 0: the activation
+ * scale from calibration maxima (e.g. svdq_calibrate_absmax of X_hat's
+ * columns).  amax: float32 [n] device, n >= 1; g: float32 [1] device. */
+svdq_status svdq_nvfp4_scale_from_absmax(int32_t n, const float* amax, float* g, void* stream);
+
+/* X_hat = bf16_RNE(fp32(X / lambda)) quantized with the per-tensor scale *g
+ * (device).  X: bf16 [M][K]; xcodes [M][K/2]; xscales uint8 [M][K/16]. */
+svdq_status svdq_nvfp4_quantize_act(int64_t M, int32_t K, const uint16_t* X, const float* lambda,
+                                    const float* g, uint8_t* xcodes, uint8_t* xscales,
+                                    void* stream);
+
+/* Offline: the residual R of svdq_pack_weight (same arithmetic) quantized
+ * with g = fp32(max |R| / 2688) (written to *g, device float).  W bf16
+ * [N][K]; lora_down bf16 [r][K] and lora_up bf16 [N][r] (NULL when rank is
+ * 0); wcodes [N][K/2]; wscales uint8 [N][K/16]. */
+svdq_status svdq_nvfp4_pack_weight(int32_t N, int32_t K, int32_t rank, const uint16_t* W,
+                                   const float* lambda, const uint16_t* lora_down,
+                                   const uint16_t* lora_up, uint8_t* wcodes, uint8_t* wscales,
+                                   float* g, void* stream);
+
+/* Y = g_x g_w sum_b s_x[m][b] s_w[n][b] sum_{k in b} c_x[m][k] c_w[n][k]
+ *     + T L2 + bias, written [M][N] as bf16 (RNE) or float32
+ * (flags = SVDQ_FLAG_OUT_F32; other bits are SVDQ_ERR_ARG).  T: float32
+ * [M][r] (svdq_lowrank_down), lora_up bf16 [N][r] (both NULL when rank is
+ * 0); bias bf16 [N] or NULL.  fp32 arithmetic: exact products of the
+ * dequantized values, fp32 sums, T L2 through a bf16 hi/lo split of T. */
+svdq_status svdq_nvfp4_linear(int64_t M, int32_t N, int32_t K, int32_t rank,
+                              const uint8_t* xcodes, const uint8_t* xscales, const float* g_x,
+                              const uint8_t* wcodes, const uint8_t* wscales, const float* g_w,
+                              const float* T, const uint16_t* lora_up, const uint16_t* bias,
+                              uint32_t flags, void* Y, void* stream);
+
 /* Offline: the rank-r factors of the smoothed weight (apatero.com page,
  * section "O que e Nunchaku ...", and axbrief.com page, section "The
  * Mechanics ...": the 16-bit branch is the rank-r part of W_hat =
