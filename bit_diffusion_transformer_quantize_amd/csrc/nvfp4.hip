@@ -182,14 +182,16 @@ __global__ __launch_bounds__(256) void nvfp4_weight_quant_kernel(
 }
 
 // ------------------------------------------------------------------ GEMM
-// A 128 x 128 output tile per workgroup (4 waves of 64 x 64, 2 x 2 MFMA
+// A 256 x 256 output tile per workgroup (8 waves of 64 x 128, 2 x 4 MFMA
 // tiles each), K in steps of 32 (two blocks): every thread dequantizes one
 // block of 16 of X and one of W into bf16 rows in LDS (the next step's codes
 // and scales are loaded while the current step runs), then each wave issues
-// 8 v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the
-// transposed accumulator layout of gemm_common.h).  Epilogue: * g_x g_w,
+// 16 v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the
+// transposed accumulator layout of gemm_common.h).  The dequantization is
+// VALU work per element, so the tile is as large as the registers allow:
+// 128 elements dequantized per matrix instruction.  Epilogue: * g_x g_w,
 // + T L2 on the same instruction (T as a bf16 hi/lo split), + bias.
-constexpr int NV_BM = 128, NV_BN = 128, NV_KS = 32;
+constexpr int NV_BM = 256, NV_BN = 256, NV_KS = 32, NV_THREADS = 512;
 constexpr int NV_LDS_ROW = NV_KS + 8;  // bf16 elements per LDS row (16-byte pad)
 
 struct NvRaw {
@@ -197,21 +199,43 @@ struct NvRaw {
   uint32_t xs, ws;
 };
 
+// bf16 values of 16 codes (two dwords) of a block with scale s, by byte
+// permutes: the 8 magnitudes E2M1(i) * s (exact in fp32 and in bf16, so the
+// upper half of the fp32 product is the bf16 value) are split into a table
+// of high bytes and one of low bytes (8 bytes each); v_perm_b32 looks up four
+// codes at a time in each (selector bytes 0-3 address its second source,
+// 4-7 its first), the code's sign bit goes to the top of the high byte, and
+// two more permutes interleave the bytes into bf16 pairs.
 __device__ __forceinline__ void nv_dequant16(v2u c, float s, uint16_t* dst) {
+  const uint32_t t1 = __float_as_uint(s * 0.5f) >> 16, t2 = __float_as_uint(s) >> 16;
+  const uint32_t t3 = __float_as_uint(s * 1.5f) >> 16, t4 = __float_as_uint(s * 2.0f) >> 16;
+  const uint32_t t5 = __float_as_uint(s * 3.0f) >> 16, t6 = __float_as_uint(s * 4.0f) >> 16;
+  const uint32_t t7 = __float_as_uint(s * 6.0f) >> 16;
+  const uint32_t p01 = t1 << 16, p23 = t2 | (t3 << 16), p45 = t4 | (t5 << 16), p67 = t6 | (t7 << 16);
+  const uint32_t L0 = __builtin_amdgcn_perm(p23, p01, 0x06040200u);  // low bytes of 0..3
+  const uint32_t H0 = __builtin_amdgcn_perm(p23, p01, 0x07050301u);  // high bytes of 0..3
+  const uint32_t L1 = __builtin_amdgcn_perm(p67, p45, 0x06040200u);
+  const uint32_t H1 = __builtin_amdgcn_perm(p67, p45, 0x07050301u);
   v4u o[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = c[h] & 0x0F0F0F0Fu, hi = (c[h] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t byte = (c[h] >> (8 * q)) & 0xFFu;
-      o[h][q] = pack_bf16x2(__fmul_rn(e2m1_value(byte & 0xFu), s),
-                            __fmul_rn(e2m1_value(byte >> 4), s));
+    for (int q = 0; q < 2; ++q) {
+      // codes of elements 4q .. 4q + 3 of this dword, one per byte
+      const uint32_t sel = __builtin_amdgcn_perm(hi, lo, q == 0 ? 0x05010400u : 0x07030602u);
+      const uint32_t mag = sel & 0x07070707u;
+      const uint32_t hb = __builtin_amdgcn_perm(H1, H0, mag) | ((sel & 0x08080808u) << 4);
+      const uint32_t lb = __builtin_amdgcn_perm(L1, L0, mag);
+      o[h][2 * q] = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
+      o[h][2 * q + 1] = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
     }
+  }
   reinterpret_cast<v4u*>(dst)[0] = o[0];
   reinterpret_cast<v4u*>(dst)[1] = o[1];
 }
 
-__global__ __launch_bounds__(256) void nvfp4_gemm_kernel(
+__global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
     int64_t M, int N, int K, int rank, int out_f32, const uint8_t* __restrict__ xcodes,
     const uint8_t* __restrict__ xscales, const float* __restrict__ gx,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales,
@@ -225,24 +249,26 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(
   const int64_t m0 = (int64_t)blockIdx.x * NV_BM;
   const int n0 = blockIdx.y * NV_BN;
   const int nbk = K / NV_BLOCK;
-  // this thread's block of 16 in each operand: row tid / 2, half tid % 2
+  // this thread's block of 16 in each operand: row tid / 2, half tid % 2;
+  // rows past M or N are read from the last row and not stored
   const int lr = tid >> 1, hf = tid & 1;
-  const int64_t xrow = std::min<int64_t>(m0 + lr, M - 1);  // rows past M are read, not stored
+  const int64_t xrow = std::min<int64_t>(m0 + lr, M - 1);
+  const int64_t wrow = std::min(n0 + lr, N - 1);
   const uint8_t* xcp = xcodes + xrow * (K / 2) + hf * 8;
   const uint8_t* xsp = xscales + xrow * nbk + hf;
-  const uint8_t* wcp = wcodes + (int64_t)(n0 + lr) * (K / 2) + hf * 8;
-  const uint8_t* wsp = wscales + (int64_t)(n0 + lr) * nbk + hf;
+  const uint8_t* wcp = wcodes + wrow * (K / 2) + hf * 8;
+  const uint8_t* wsp = wscales + wrow * nbk + hf;
   auto load = [&](int ks, NvRaw& r) {
     r.xc = *reinterpret_cast<const v2u*>(xcp + ks * (NV_KS / 2));
     r.wc = *reinterpret_cast<const v2u*>(wcp + ks * (NV_KS / 2));
     r.xs = xsp[ks * 2];
     r.ws = wsp[ks * 2];
   };
-  v16f acc[2][2];
+  v16f acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
@@ -257,16 +283,17 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < NV_KS; kk += 16) {
-      v8bf af[2], bfr[2];
+      v8bf af[4], bfr[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        af[t] = *reinterpret_cast<const v8bf*>(ws_l + (wn * 64 + 32 * t + l32) * NV_LDS_ROW + kk + kh);
+      for (int t = 0; t < 4; ++t)
+        af[t] = *reinterpret_cast<const v8bf*>(ws_l + (wn * 128 + 32 * t + l32) * NV_LDS_ROW + kk + kh);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
         bfr[t] = *reinterpret_cast<const v8bf*>(xs_l + (wm * 64 + 32 * t + l32) * NV_LDS_ROW + kk + kh);
-      }
 #pragma unroll
       for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-        for (int tc = 0; tc < 2; ++tc)
+        for (int tc = 0; tc < 4; ++tc)
           acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tc], bfr[tr], acc[tr][tc], 0, 0, 0);
     }
     __syncthreads();
@@ -274,20 +301,23 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(
   }
 
   const int64_t mbase = m0 + wm * 64;
-  const int nbase = n0 + wn * 64;
+  const int nbase = n0 + wn * 128;
+  if (nbase >= N) return;  // a partial last column tile: this wave's columns are all past N
   const float gg = __fmul_rn(*gx, *gw);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = __fmul_rn(acc[a][b][i], gg);
   // T L2: T rows (B operand, bf16 hi + lo), lora_up rows (A operand)
   for (int q0 = 0; q0 < rank; q0 += 16) {
-    v8bf lu[2], thi[2], tlo[2];
+    v8bf lu[4], thi[2], tlo[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      lu[t] = *reinterpret_cast<const v8bf*>(lora_up + (int64_t)(nbase + 32 * t + l32) * rank + q0 + kh);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      lu[t] = *reinterpret_cast<const v8bf*>(lora_up + (int64_t)(nbase + 32 * t + l32) * rank + q0 + kh);
       const int64_t tm = std::min<int64_t>(mbase + 32 * t + l32, M - 1);
       const v4f t0 = *reinterpret_cast<const v4f*>(T + tm * rank + q0 + kh);
       const v4f t1 = *reinterpret_cast<const v4f*>(T + tm * rank + q0 + kh + 4);
@@ -302,14 +332,14 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-      for (int tc = 0; tc < 2; ++tc) {
+      for (int tc = 0; tc < 4; ++tc) {
         acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[tc], thi[tr], acc[tr][tc], 0, 0, 0);
         acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lu[tc], tlo[tr], acc[tr][tc], 0, 0, 0);
       }
   }
   if (bias != nullptr) {
 #pragma unroll
-    for (int tc = 0; tc < 2; ++tc)
+    for (int tc = 0; tc < 4; ++tc)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float bv = bf16_to_f32(bias[nbase + 32 * tc + acc_row(i, lane)]);
@@ -317,7 +347,7 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(
         for (int tr = 0; tr < 2; ++tr) acc[tr][tc][i] = __fadd_rn(acc[tr][tc][i], bv);
       }
   }
-  store_tiles_t<2, 2>(acc, M, N, mbase, nbase, lane, out_f32 != 0, Y);
+  store_tiles_t<2, 4>(acc, M, N, mbase, nbase, lane, out_f32 != 0, Y);
 }
 
 }  // namespace
@@ -354,8 +384,8 @@ hipError_t launch_nvfp4_linear(bool out_f32, int64_t M, int N, int K, int rank,
                                const uint8_t* wcodes, const uint8_t* wscales, const float* gw,
                                const float* T, const uint16_t* lora_up, const uint16_t* bias,
                                void* Y, hipStream_t s) {
-  const dim3 grid((unsigned)((M + NV_BM - 1) / NV_BM), N / NV_BN);
-  hipLaunchKernelGGL(nvfp4_gemm_kernel, grid, dim3(256), 0, s, M, N, K, rank, (int)out_f32, xcodes,
+  const dim3 grid((unsigned)((M + NV_BM - 1) / NV_BM), (N + NV_BN - 1) / NV_BN);
+  hipLaunchKernelGGL(nvfp4_gemm_kernel, grid, dim3(NV_THREADS), 0, s, M, N, K, rank, (int)out_f32, xcodes,
                      xscales, gx, wcodes, wscales, gw, T, lora_up, bias, Y);
   return hipGetLastError();
 }
