@@ -184,55 +184,63 @@ __global__ __launch_bounds__(256) void nvfp4_weight_quant_kernel(
 // ------------------------------------------------------------------ GEMM
 // A 256 x 256 output tile per workgroup (8 waves of 64 x 128, 2 x 4 MFMA
 // tiles each), K in steps of 32 (two blocks): every thread dequantizes one
-// block of 16 of X and one of W into bf16 rows in LDS (the next step's codes
-// and scales are loaded while the current step runs), then each wave issues
+// block of 16 of X and one of W to bf16 in LDS (the next step's codes and
+// scales are loaded while the current step runs), then each wave issues
 // 16 v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the
 // transposed accumulator layout of gemm_common.h).  The dequantization is
 // VALU work per element, so the tile is as large as the registers allow:
 // 128 elements dequantized per matrix instruction.  Epilogue: * g_x g_w,
 // + T L2 on the same instruction (T as a bf16 hi/lo split), + bias.
 constexpr int NV_BM = 256, NV_BN = 256, NV_KS = 32, NV_THREADS = 512;
-constexpr int NV_LDS_ROW = NV_KS + 8;  // bf16 elements per LDS row (16-byte pad)
+// LDS holds each operand tile in the matrix instruction's fragment order:
+// 16-byte unit ((r / 32) * 2 + kb) * 64 + r % 32 + 32 * h holds row r's
+// eight values of half h of block kb, so a wave reads a fragment as 64
+// consecutive units and a thread writes its block as two units of a
+// lane-consecutive run (no bank conflicts either way).
+constexpr int NV_TILE_UNITS = NV_BM / 32 * 2 * 64;
 
 struct NvRaw {
   v2u xc, wc;
   uint32_t xs, ws;
 };
 
-// bf16 values of 16 codes (two dwords) of a block with scale s, by byte
-// permutes: the 8 magnitudes E2M1(i) * s (exact in fp32 and in bf16, so the
-// upper half of the fp32 product is the bf16 value) are split into a table
-// of high bytes and one of low bytes (8 bytes each); v_perm_b32 looks up four
-// codes at a time in each (selector bytes 0-3 address its second source,
-// 4-7 its first), the code's sign bit goes to the top of the high byte, and
-// two more permutes interleave the bytes into bf16 pairs.
-__device__ __forceinline__ void nv_dequant16(v2u c, float s, uint16_t* dst) {
-  const uint32_t t1 = __float_as_uint(s * 0.5f) >> 16, t2 = __float_as_uint(s) >> 16;
-  const uint32_t t3 = __float_as_uint(s * 1.5f) >> 16, t4 = __float_as_uint(s * 2.0f) >> 16;
-  const uint32_t t5 = __float_as_uint(s * 3.0f) >> 16, t6 = __float_as_uint(s * 4.0f) >> 16;
-  const uint32_t t7 = __float_as_uint(s * 6.0f) >> 16;
-  const uint32_t p01 = t1 << 16, p23 = t2 | (t3 << 16), p45 = t4 | (t5 << 16), p67 = t6 | (t7 << 16);
-  const uint32_t L0 = __builtin_amdgcn_perm(p23, p01, 0x06040200u);  // low bytes of 0..3
-  const uint32_t H0 = __builtin_amdgcn_perm(p23, p01, 0x07050301u);  // high bytes of 0..3
+// bf16 values of a block of 16 codes (two dwords) with scale s, by byte
+// permutes.  The 8 magnitudes E2M1(i) * s are exact in fp32 with at most 6
+// significant bits, so their fp32 bytes 0 and 1 are zero and bytes 2 and 3
+// are the bf16 value; tables H (bytes 3) and L (bytes 2) of 8 entries each
+// take two dwords.  v_perm_b32 looks up four code magnitudes at a time in
+// each (its selector bytes 0-3 address the second source, 4-7 the first),
+// and the code's sign goes to bit 7 of the high byte.  The 8 values of a
+// code dword come out in the order 0 2 4 6 1 3 5 7 (low nibbles, then high
+// nibbles): both operands use this order, and a dot product does not depend
+// on the order of its terms.
+__device__ __forceinline__ void nv_dequant16(v2u c, float s, v4u& o0, v4u& o1) {
+  const uint32_t f1 = __float_as_uint(s * 0.5f), f2 = __float_as_uint(s);
+  const uint32_t f3 = __float_as_uint(s * 1.5f), f4 = __float_as_uint(s * 2.0f);
+  const uint32_t f5 = __float_as_uint(s * 3.0f), f6 = __float_as_uint(s * 4.0f);
+  const uint32_t f7 = __float_as_uint(s * 6.0f);
+  const uint32_t p12 = __builtin_amdgcn_perm(f2, f1, 0x07060302u);  // hi16(f1) | hi16(f2) << 16
+  const uint32_t p45 = __builtin_amdgcn_perm(f5, f4, 0x07060302u);
+  const uint32_t p67 = __builtin_amdgcn_perm(f7, f6, 0x07060302u);
+  // entry 0 takes byte 0 of f3, which is zero
+  const uint32_t L0 = __builtin_amdgcn_perm(f3, p12, 0x06020004u);
+  const uint32_t H0 = __builtin_amdgcn_perm(f3, p12, 0x07030104u);
   const uint32_t L1 = __builtin_amdgcn_perm(p67, p45, 0x06040200u);
   const uint32_t H1 = __builtin_amdgcn_perm(p67, p45, 0x07050301u);
-  v4u o[2];
+  v4u* o[2] = {&o0, &o1};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t lo = c[h] & 0x0F0F0F0Fu, hi = (c[h] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      // codes of elements 4q .. 4q + 3 of this dword, one per byte
-      const uint32_t sel = __builtin_amdgcn_perm(hi, lo, q == 0 ? 0x05010400u : 0x07030602u);
-      const uint32_t mag = sel & 0x07070707u;
-      const uint32_t hb = __builtin_amdgcn_perm(H1, H0, mag) | ((sel & 0x08080808u) << 4);
-      const uint32_t lb = __builtin_amdgcn_perm(L1, L0, mag);
-      o[h][2 * q] = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
-      o[h][2 * q + 1] = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
-    }
+    const uint32_t w = c[h];
+    const uint32_t ml = w & 0x07070707u, mh = (w >> 4) & 0x07070707u;
+    const uint32_t hl = __builtin_amdgcn_perm(H1, H0, ml) | ((w << 4) & 0x80808080u);
+    const uint32_t hh = __builtin_amdgcn_perm(H1, H0, mh) | (w & 0x80808080u);
+    const uint32_t ll = __builtin_amdgcn_perm(L1, L0, ml);
+    const uint32_t lh = __builtin_amdgcn_perm(L1, L0, mh);
+    (*o[h])[0] = __builtin_amdgcn_perm(hl, ll, 0x05010400u);
+    (*o[h])[1] = __builtin_amdgcn_perm(hl, ll, 0x07030602u);
+    (*o[h])[2] = __builtin_amdgcn_perm(hh, lh, 0x05010400u);
+    (*o[h])[3] = __builtin_amdgcn_perm(hh, lh, 0x07030602u);
   }
-  reinterpret_cast<v4u*>(dst)[0] = o[0];
-  reinterpret_cast<v4u*>(dst)[1] = o[1];
 }
 
 __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
@@ -242,28 +250,30 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
     const float* __restrict__ gw, const float* __restrict__ T,
     const uint16_t* __restrict__ lora_up, const uint16_t* __restrict__ bias,
     void* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs_l[NV_BM * NV_LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t ws_l[NV_BN * NV_LDS_ROW];
+  __shared__ v4u xs_l[NV_TILE_UNITS];
+  __shared__ v4u ws_l[NV_TILE_UNITS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.x * NV_BM;
   const int n0 = blockIdx.y * NV_BN;
   const int nbk = K / NV_BLOCK;
-  // this thread's block of 16 in each operand: row tid / 2, half tid % 2;
-  // rows past M or N are read from the last row and not stored
-  const int lr = tid >> 1, hf = tid & 1;
+  // this thread's block of each operand: row 32 * wave + lane % 32, block
+  // lane / 32 of the step; rows past M or N are read from the last row (their
+  // outputs are not stored)
+  const int lr = 32 * wave + (lane & 31), kb = lane >> 5;
   const int64_t xrow = std::min<int64_t>(m0 + lr, M - 1);
   const int64_t wrow = std::min(n0 + lr, N - 1);
-  const uint8_t* xcp = xcodes + xrow * (K / 2) + hf * 8;
-  const uint8_t* xsp = xscales + xrow * nbk + hf;
-  const uint8_t* wcp = wcodes + wrow * (K / 2) + hf * 8;
-  const uint8_t* wsp = wscales + wrow * nbk + hf;
+  const uint8_t* xcp = xcodes + xrow * (K / 2) + kb * 8;
+  const uint8_t* xsp = xscales + xrow * nbk + kb;
+  const uint8_t* wcp = wcodes + wrow * (K / 2) + kb * 8;
+  const uint8_t* wsp = wscales + wrow * nbk + kb;
   auto load = [&](int ks, NvRaw& r) {
     r.xc = *reinterpret_cast<const v2u*>(xcp + ks * (NV_KS / 2));
     r.wc = *reinterpret_cast<const v2u*>(wcp + ks * (NV_KS / 2));
     r.xs = xsp[ks * 2];
     r.ws = wsp[ks * 2];
   };
+  const int dst = (wave * 2 + kb) * 64 + (lane & 31);
   v16f acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -275,21 +285,30 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
   const int nks = K / NV_KS;
   NvRaw cur, nxt;
   load(0, cur);
-  const int l32 = lane & 31, kh = (lane >> 5) * 8;
+  const int l32 = lane & 31;
   for (int ks = 0; ks < nks; ++ks) {
     load(std::min(ks + 1, nks - 1), nxt);
-    nv_dequant16(cur.xc, e4m3_value(cur.xs), xs_l + lr * NV_LDS_ROW + hf * 16);
-    nv_dequant16(cur.wc, e4m3_value(cur.ws), ws_l + lr * NV_LDS_ROW + hf * 16);
+    {
+      v4u a0, a1, b0, b1;
+      // gfx950's fp8 conversion decodes an OCP E4M3 byte exactly (subnormals
+      // included): the same value as e4m3_value in one instruction
+      nv_dequant16(cur.xc, __builtin_amdgcn_cvt_f32_fp8((int)cur.xs, 0), a0, a1);
+      nv_dequant16(cur.wc, __builtin_amdgcn_cvt_f32_fp8((int)cur.ws, 0), b0, b1);
+      xs_l[dst] = a0;
+      xs_l[dst + 32] = a1;
+      ws_l[dst] = b0;
+      ws_l[dst + 32] = b1;
+    }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < NV_KS; kk += 16) {
+    for (int k2 = 0; k2 < 2; ++k2) {
       v8bf af[4], bfr[2];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        af[t] = *reinterpret_cast<const v8bf*>(ws_l + (wn * 128 + 32 * t + l32) * NV_LDS_ROW + kk + kh);
+        af[t] = __builtin_bit_cast(v8bf, ws_l[((wn * 4 + t) * 2 + k2) * 64 + lane]);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        bfr[t] = *reinterpret_cast<const v8bf*>(xs_l + (wm * 64 + 32 * t + l32) * NV_LDS_ROW + kk + kh);
+        bfr[t] = __builtin_bit_cast(v8bf, xs_l[((wm * 2 + t) * 2 + k2) * 64 + lane]);
 #pragma unroll
       for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -300,6 +319,7 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
     cur = nxt;
   }
 
+  const int kh = (lane >> 5) * 8;
   const int64_t mbase = m0 + wm * 64;
   const int nbase = n0 + wn * 128;
   if (nbase >= N) return;  // a partial last column tile: this wave's columns are all past N

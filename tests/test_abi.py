@@ -326,3 +326,45 @@ def test_no_device_is_a_hip_error():
     assert lib.svdq_qk_norm_rope(64, 24, 9216, A, A, A, A, A, 1e-6, None) == HIP
     assert lib.svdq_linear_forward_qk(_d(mode=1, N=9216), 256, A, A, 24, A, A, A, A, 1e-6, A,
                                       None) == HIP
+
+
+def test_nvfp4_validation():
+    lib = _lib()
+    sfa = lib.svdq_nvfp4_scale_from_absmax
+    assert sfa(4, None, A, None) == ARG
+    assert sfa(4, A, MIS, None) == ARG
+    assert sfa(0, A, A, None) == SHAPE
+    qa = lib.svdq_nvfp4_quantize_act
+    assert qa(64, 512, None, A, A, A, A, None) == ARG
+    assert qa(64, 512, A, A, A, A, MIS, None) == ARG
+    for M, K in [(0, 512), (64, 96), (64, 0), (64, 1 << 21)]:
+        assert qa(M, K, A, A, A, A, A, None) == SHAPE, (M, K)
+    pw = lib.svdq_nvfp4_pack_weight
+    assert pw(256, 512, 16, A, A, None, A, A, A, A, None) == ARG       # rank > 0 needs both factors
+    assert pw(256, 512, 0, A, A, A, None, A, A, A, None) == ARG        # rank 0 takes none
+    assert pw(256, 512, 16, A, A, A, A, A, A, None, None) == ARG       # g null
+    for N, K, r in [(200, 512, 16), (256, 200, 16), (256, 512, 24), (256, 512, 272)]:
+        assert pw(N, K, r, A, A, A, A, A, A, A, None) == SHAPE, (N, K, r)
+    assert pw(256, 512, -16, A, A, None, None, A, A, A, None) == SHAPE
+    lin = lib.svdq_nvfp4_linear
+    ok = dict(M=64, N=256, K=512, r=16, xc=A, xs=A, gx=A, wc=A, ws=A, gw=A, T=A, lu=A, b=None,
+              fl=0, Y=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lin(a["M"], a["N"], a["K"], a["r"], a["xc"], a["xs"], a["gx"], a["wc"], a["ws"],
+                   a["gw"], a["T"], a["lu"], a["b"], a["fl"], a["Y"], None)
+
+    assert call(fl=2) == ARG                 # only the fp32-output flag is defined
+    assert call(xc=None) == ARG
+    assert call(ws=MIS) == ARG
+    assert call(gw=None) == ARG
+    assert call(Y=None) == ARG
+    assert call(b=MIS) == ARG
+    assert call(T=None) == ARG               # rank 16 needs T and lora_up
+    assert call(r=0) == ARG                  # rank 0 takes neither
+    assert call(r=0, T=None, lu=None, M=0) == SHAPE
+    assert call(N=200) == SHAPE
+    assert call(K=96) == SHAPE
+    assert call(r=24) == SHAPE

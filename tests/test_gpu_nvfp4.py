@@ -107,3 +107,29 @@ def test_full_size_fused_projection():
         assert np.array_equal(*res[k]), k
     assert np.float32(res["gw"][0]) == np.float32(res["gw"][1])
     assert_y(*res["Y"], False, "nvfp4 Y (C4 rows)")
+
+
+def test_every_scale_byte_in_the_gemm():
+    """The GEMM on hand-made codes whose block scales run through every E4M3
+    byte 0x00..0x7E (zero, the 7 subnormals, all normals) on both operands,
+    g_x = 0.75, g_w = 1.25, fp32 output: each output within the fp32
+    summation bound (K 2^-24 sum |x w|) of the oracle's exact sum, so a wrong
+    decode of any scale byte fails."""
+    S = _S()
+    M, N, K = 64, 128, 256
+    _say("nvfp4 gemm every scale byte", M, N, K)
+    rng = np.random.default_rng(11)
+    nb = K // 16
+    xs = ((np.arange(M)[:, None] * nb + np.arange(nb)[None, :]) % 127).astype(np.uint8)
+    ws = ((np.arange(N)[:, None] * 5 + 3 * np.arange(nb)[None, :]) % 127).astype(np.uint8)
+    xc = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    gx, gw = np.float32(0.75), np.float32(1.25)
+    Y_o = O.nvfp4_forward(xc, xs, gx, None, wc, ws, gw, None, None)
+    absum = np.abs(O.decode_nvfp4(xc, xs, gx)) @ np.abs(O.decode_nvfp4(wc, ws, gw)).T
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    Y = S.svdq_nvfp4_linear(t(xc), t(xs), _g(gx), t(wc), t(ws), _g(gw), out_f32=True)
+    torch.cuda.synchronize()
+    err = np.abs(np_(Y).astype(np.float64) - Y_o)
+    bound = K * 2.0 ** -24 * absum + 1e-300
+    assert np.all(err <= bound), f"{np.sum(err > bound)} outputs, worst {np.max(err / bound):.3g}x"
