@@ -58,11 +58,12 @@ def _layer(spec, seed, r, out_f32=False, rows=None):
 
 
 @pytest.mark.parametrize("M,K,N,r", [(77, 512, 256, 16), (256, 1024, 384, 32), (130, 256, 128, 0),
-                                     (300, 3072, 512, 128)])
+                                     (300, 3072, 512, 128), (1, 128, 128, 16), (513, 128, 640, 0)])
 @pytest.mark.parametrize("out_f32", [False, True])
 def test_layer_matches_oracle(M, K, N, r, out_f32):
-    """Ragged M (not a multiple of the 128-row tile), rank 0 to 128, both
-    output types."""
+    """Ragged M (one row; not a multiple of the 256-row tile), the smallest
+    K (128, four K-steps), a partial last 256-column tile (N = 384, 640),
+    rank 0 to 128, both output types."""
     _say("nvfp4 layer", M, K, N, r, out_f32)
     spec = WL.LinearSpec(f"nv_{M}x{K}x{N}", M, K, N, r, "fp4", x_outliers=4, x_factor=30.0,
                          w_outliers=2, w_factor=10.0)
