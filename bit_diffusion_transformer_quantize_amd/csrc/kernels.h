@@ -61,10 +61,13 @@ hipError_t launch_qk_norm_rope(int64_t M, int heads, int64_t ld, uint16_t* Y, co
                                const uint16_t* k_scale, const float* cosv, const float* sinv,
                                float eps, hipStream_t s);
 
-// NVFP4 variant (nvfp4.hip).
-hipError_t launch_nvfp4_quantize_act(int64_t M, int K, const uint16_t* X, const float* lambda,
-                                     const float* g, uint8_t* codes, uint8_t* scales,
-                                     hipStream_t s);
+// NVFP4 variant.  The activation pass is the mode-2 quantize_act_kernel
+// (quantize_act.hip: codes, scale bytes and, when rank > 0, T = X_hat L1 from
+// the same registers); the rest is nvfp4.hip.
+hipError_t launch_nvfp4_quantize_act(int64_t M, int K, int rank, const uint16_t* X,
+                                     const float* lambda, const float* g,
+                                     const uint16_t* lora_down, uint8_t* xcodes, uint8_t* xscales,
+                                     float* T, hipStream_t s);
 hipError_t launch_nvfp4_scale_from_absmax(int n, const float* amax, float* g, hipStream_t s);
 hipError_t launch_nvfp4_pack_weight(int N, int K, int rank, const uint16_t* W, const float* lambda,
                                     const uint16_t* lora_down, const uint16_t* lora_up,

@@ -19,44 +19,13 @@
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
+#include "nvfp4_codec.h"
 #include "weight_residual.h"
 
 namespace svdq {
 namespace {
 
 constexpr int NV_BLOCK = 16;
-
-// Byte of E4M3_RNE_sat(v) for v >= 0: nearest value of the E4M3 grid
-// (normals (1 + m/8) 2^e for e = -6..8, subnormals m 2^-9), ties to the even
-// mantissa, 448 for everything from 448 up.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  if (!(v < 448.0f)) return 0x7Eu;
-  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);  // 0..8 (8 = 2^-6)
-  const uint32_t b = __float_as_uint(v);
-  int e = (int)(b >> 23) - 127;
-  uint32_t q = (b >> 20) & 7u;
-  const uint32_t rem = b & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-  if (q == 8u) {
-    q = 0;
-    ++e;
-  }
-  const uint32_t byte = ((uint32_t)(e + 7) << 3) | q;
-  return byte > 0x7Eu ? 0x7Eu : byte;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  return e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
-
-// Value of a 4-bit E2M1 code (bit 3 = sign): magnitudes 0, .5, 1, 1.5, 2, 3,
-// 4, 6 built from the exponent and mantissa bits.
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const uint32_t mag = e == 0 ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
-  return __uint_as_float(mag | ((c & 8u) << 28));
-}
 
 // One block of 16 values: codes (two dwords, element 2j in the low nibble of
 // byte j) and the scale byte, for per-tensor scale g and t = fp32(6 g).
@@ -75,37 +44,6 @@ __device__ __forceinline__ void nvfp4_block(const float (&v)[16], float g, float
 #pragma unroll
     for (int i = 0; i < 8; ++i) w1 |= e2m1_code(v[8 + i] / d) << (4 * i);
   }
-}
-
-// ------------------------------------------------------------------ activations
-// One thread per block of 16: X_hat = bf16_RNE(fp32(X / lambda)), quantized
-// with the per-tensor scale *g.
-__global__ __launch_bounds__(256) void nvfp4_act_kernel(int64_t M, int K,
-                                                        const uint16_t* __restrict__ X,
-                                                        const float* __restrict__ lambda,
-                                                        const float* __restrict__ gptr,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales) {
-  const int nbk = K / NV_BLOCK;
-  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (blk >= M * nbk) return;
-  const int64_t m = blk / nbk;
-  const int kb = (int)(blk - m * nbk);
-  const int k0 = kb * NV_BLOCK;
-  const v4u xa = *reinterpret_cast<const v4u*>(X + m * K + k0);
-  const v4u xb = *reinterpret_cast<const v4u*>(X + m * K + k0 + 8);
-  const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
-  float v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float x = bf16_to_f32((xw[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu);
-    v[i] = bf16_to_f32(f32_to_bf16(x / lambda[k0 + i]));
-  }
-  const float g = *gptr;
-  uint32_t w0, w1, sb;
-  nvfp4_block(v, g, __fmul_rn(6.0f, g), w0, w1, sb);
-  *reinterpret_cast<v2u*>(codes + m * (K / 2) + kb * 8) = v2u{w0, w1};
-  scales[m * nbk + kb] = (uint8_t)sb;
 }
 
 // g = fp32(max_k amax[k] / 2688), 1 when the maximum is 0 (one workgroup).
@@ -371,15 +309,6 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_nvfp4_quantize_act(int64_t M, int K, const uint16_t* X, const float* lambda,
-                                     const float* g, uint8_t* codes, uint8_t* scales,
-                                     hipStream_t s) {
-  const int64_t blocks = (M * (K / NV_BLOCK) + 255) / 256;
-  hipLaunchKernelGGL(nvfp4_act_kernel, dim3((unsigned)blocks), dim3(256), 0, s, M, K, X, lambda,
-                     g, codes, scales);
-  return hipGetLastError();
-}
 
 hipError_t launch_nvfp4_scale_from_absmax(int n, const float* amax, float* g, hipStream_t s) {
   hipLaunchKernelGGL(nvfp4_scale_from_absmax_kernel, dim3(1), dim3(256), 0, s, n, amax, g);

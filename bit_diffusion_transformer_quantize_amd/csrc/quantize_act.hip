@@ -34,6 +34,7 @@
 #include "common.h"
 #include "image.h"
 #include "kernels.h"
+#include "nvfp4_codec.h"
 
 namespace svdq {
 
@@ -86,6 +87,7 @@ struct QaImage {
   int64_t RT;
   size_t scale, lr, tpart;
   int S;
+  const float* g = nullptr;  // NVFP4: the per-tensor scale (device)
 };
 
 // GELU with the tanh approximation in the cancellation-free form
@@ -235,7 +237,8 @@ __device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w, const uint16_t* tab)
   return gelu_one(w & 0xFFFFu, tab) | (gelu_one(w >> 16, tab) << 16);
 }
 
-// MODE 0 = INT4, 1 = FP4.  RB = rank / 16 (0 = no down-projection).
+// MODE 0 = INT4, 1 = FP4, 2 = NVFP4 (row-major codes and scales only, no
+// image).  RB = rank / 16 (0 = no down-projection).
 // CODES = false skips the quantizer (stand-alone down-projection).
 template <int MODE, int RB, bool CODES, bool GELU>
 __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_kernel(
@@ -375,7 +378,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
               *reinterpret_cast<v2u*>(blk + 1536 + 8 * (32 * j + irr)) = so;
             }
           }
-        } else {
+        } else if constexpr (MODE == 1) {
           // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
           amax = fmaxf(amax, __shfl_xor(amax, 16));
           const int e = e8m0_exponent(amax);
@@ -397,6 +400,26 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
             const int slot = 32 * (j >> 1) + irr;
             *reinterpret_cast<v2u*>(qi.img + b * F4_CBLOCK + 16 * slot + 8 * (j & 1)) = v2u{w0, w1};
             if ((j & 1) == 0) qi.img[qi.scale + b * F4_SBLOCK + slot] = (uint8_t)(e + 127);
+          }
+        } else {
+          // NVFP4: this lane's 16 elements are one block.  s =
+          // E4M3_RNE_sat(fp32(amax / fp32(6 g))), d = fp32(s g), codes of
+          // fp32(x_hat / d); the quotient comes from d's fp64 reciprocal,
+          // exact for a bf16 numerator as x / lambda above.
+          const float g = *qi.g;
+          const uint32_t sb = e4m3_encode(amax / __fmul_rn(6.0f, g));
+          const float sv = e4m3_value(sb);
+          uint32_t w0 = 0, w1 = 0;
+          if (sv > 0.f) {
+            const double rd = 1.0 / (double)__fmul_rn(sv, g);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w0 |= e2m1_code((float)((double)xh[i] * rd)) << (4 * i);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w1 |= e2m1_code((float)((double)xh[8 + i] * rd)) << (4 * i);
+          }
+          if (xcodes != nullptr && row_ok) {
+            *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
+            reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 4) + (k0 >> 4)] = (uint8_t)sb;
           }
         }
       }
@@ -541,6 +564,16 @@ static hipError_t launch_qa_rank(int rb, dim3 grid, hipStream_t s, int64_t M, in
   }
 #undef SVDQ_QA_CASE
   return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize_act(int64_t M, int K, int rank, const uint16_t* X,
+                                     const float* lambda, const float* g,
+                                     const uint16_t* lora_down, uint8_t* xcodes, uint8_t* xscales,
+                                     float* T, hipStream_t s) {
+  QaImage qi{nullptr, 0, 0, 0, 0, 1, g};
+  const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
+  return launch_qa_rank<2, true, false>(lora_down ? rank / 16 : 0, grid, s, M, K, X, lambda,
+                                        lora_down, xcodes, xscales, T, qi);
 }
 
 size_t act_image_bytes(int mode, int64_t M, int K, int rank) {

@@ -319,15 +319,18 @@ svdq_status svdq_nvfp4_scale_from_absmax(int32_t n, const float* amax, float* g,
   return from_hip(svdq::launch_nvfp4_scale_from_absmax(n, amax, g, (hipStream_t)stream));
 }
 
-svdq_status svdq_nvfp4_quantize_act(int64_t M, int32_t K, const uint16_t* X, const float* lambda,
-                                    const float* g, uint8_t* xcodes, uint8_t* xscales,
-                                    void* stream) {
+svdq_status svdq_nvfp4_quantize_act(int64_t M, int32_t K, int32_t rank, const uint16_t* X,
+                                    const float* lambda, const float* g,
+                                    const uint16_t* lora_down, uint8_t* xcodes, uint8_t* xscales,
+                                    float* T, void* stream) {
   if (!ptr_ok(X) || !ptr_ok(lambda) || !ptr_ok(g) || !ptr_ok(xcodes) || !ptr_ok(xscales))
     return SVDQ_ERR_ARG;
-  SVDQ_TRY(check_nv_shape(M, 128, K, 0));
+  if (rank > 0 ? (!ptr_ok(lora_down) || !ptr_ok(T)) : (lora_down != nullptr || T != nullptr))
+    return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_nv_shape(M, 128, K, rank));
   SVDQ_TRY(check_device());
-  return from_hip(svdq::launch_nvfp4_quantize_act(M, K, X, lambda, g, xcodes, xscales,
-                                                  (hipStream_t)stream));
+  return from_hip(svdq::launch_nvfp4_quantize_act(M, K, rank, X, lambda, g, lora_down, xcodes,
+                                                  xscales, T, (hipStream_t)stream));
 }
 
 svdq_status svdq_nvfp4_pack_weight(int32_t N, int32_t K, int32_t rank, const uint16_t* W,

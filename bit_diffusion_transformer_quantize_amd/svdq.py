@@ -68,7 +68,8 @@ _SIGNATURES = {
     "svdq_linear_forward_qk": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                               ctypes.c_float, _vp, _vp]),
     "svdq_nvfp4_scale_from_absmax": (ctypes.c_int, [_i32, _vp, _vp, _vp]),
-    "svdq_nvfp4_quantize_act": (ctypes.c_int, [_i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_nvfp4_quantize_act": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _vp]),
     "svdq_nvfp4_pack_weight": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _vp]),
     "svdq_nvfp4_linear": (ctypes.c_int, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -446,9 +447,12 @@ def svdq_nvfp4_scale_from_absmax(amax, g=None):
     return g
 
 
-def svdq_nvfp4_quantize_act(X, lam, g, xcodes=None, xscales=None):
-    """NVFP4 codes [M][K/2] and E4M3 scales [M][K/16] of X_hat = X / lambda."""
+def svdq_nvfp4_quantize_act(X, lam, g, xcodes=None, xscales=None, lora_down=None, T=None):
+    """NVFP4 codes [M][K/2] and E4M3 scales [M][K/16] of X_hat = X / lambda,
+    and T = X_hat L1 [M][r] fp32 from the same pass when lora_down ([r][K])
+    is given.  Returns (xcodes, xscales, T or None)."""
     M, K = X.shape
+    rank = 0 if lora_down is None else lora_down.shape[0]
     _need(X, "X", torch.bfloat16, (M, K))
     _need(lam, "lambda", torch.float32, (K,))
     _need(g, "g", torch.float32, (1,))
@@ -458,10 +462,16 @@ def svdq_nvfp4_quantize_act(X, lam, g, xcodes=None, xscales=None):
         xscales = torch.empty(M, K // NVFP4_BLOCK, dtype=torch.uint8, device=X.device)
     _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
     _need(xscales, "xscales", torch.uint8, (M, K // NVFP4_BLOCK))
+    if rank:
+        _need(lora_down, "lora_down", torch.bfloat16, (rank, K))
+        if T is None:
+            T = torch.empty(M, rank, dtype=torch.float32, device=X.device)
+        _need(T, "T", torch.float32, (M, rank))
     _check("svdq_nvfp4_quantize_act",
-           load().svdq_nvfp4_quantize_act(M, K, _p(X), _p(lam), _p(g), _p(xcodes), _p(xscales),
+           load().svdq_nvfp4_quantize_act(M, K, rank, _p(X), _p(lam), _p(g), _p(lora_down),
+                                          _p(xcodes), _p(xscales), _p(T if rank else None),
                                           _stream()))
-    return xcodes, xscales
+    return xcodes, xscales, (T if rank else None)
 
 
 def svdq_nvfp4_pack_weight(W, lam, rank: int, lora_down=None, lora_up=None):

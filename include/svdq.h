@@ -168,10 +168,16 @@ svdq_status svdq_lambda_from_absmax(int32_t K, const float* xmax, const float* w
 svdq_status svdq_nvfp4_scale_from_absmax(int32_t n, const float* amax, float* g, void* stream);
 
 /* X_hat = bf16_RNE(fp32(X / lambda)) quantized with the per-tensor scale *g
- * (device).  X: bf16 [M][K]; xcodes [M][K/2]; xscales uint8 [M][K/16]. */
-svdq_status svdq_nvfp4_quantize_act(int64_t M, int32_t K, const uint16_t* X, const float* lambda,
-                                    const float* g, uint8_t* xcodes, uint8_t* xscales,
-                                    void* stream);
+ * (device), and, when rank > 0, the down-projection T = X_hat L1 from the
+ * same read of X (the fusion the apatero.com page describes in section "O
+ * que e Nunchaku ...", as in svdq_quantize_act).
+ * X: bf16 [M][K]; xcodes [M][K/2]; xscales uint8 [M][K/16]; lora_down bf16
+ * [r][K] (= L1 transposed) and T float32 [M][r], both NULL when rank is 0.
+ * rank % 16 == 0, 0 <= rank <= 256. */
+svdq_status svdq_nvfp4_quantize_act(int64_t M, int32_t K, int32_t rank, const uint16_t* X,
+                                    const float* lambda, const float* g,
+                                    const uint16_t* lora_down, uint8_t* xcodes, uint8_t* xscales,
+                                    float* T, void* stream);
 
 /* Offline: the residual R of svdq_pack_weight (same arithmetic) quantized
  * with g = fp32(max |R| / 2688) (written to *g, device float).  W bf16
@@ -185,7 +191,7 @@ svdq_status svdq_nvfp4_pack_weight(int32_t N, int32_t K, int32_t rank, const uin
 /* Y = g_x g_w sum_b s_x[m][b] s_w[n][b] sum_{k in b} c_x[m][k] c_w[n][k]
  *     + T L2 + bias, written [M][N] as bf16 (RNE) or float32
  * (flags = SVDQ_FLAG_OUT_F32; other bits are SVDQ_ERR_ARG).  T: float32
- * [M][r] (svdq_lowrank_down), lora_up bf16 [N][r] (both NULL when rank is
+ * [M][r] (svdq_nvfp4_quantize_act), lora_up bf16 [N][r] (both NULL when rank is
  * 0); bias bf16 [N] or NULL.  fp32 arithmetic: exact products of the
  * dequantized values, fp32 sums, T L2 through a bf16 hi/lo split of T. */
 svdq_status svdq_nvfp4_linear(int64_t M, int32_t N, int32_t K, int32_t rank,

@@ -335,10 +335,15 @@ def test_nvfp4_validation():
     assert sfa(4, A, MIS, None) == ARG
     assert sfa(0, A, A, None) == SHAPE
     qa = lib.svdq_nvfp4_quantize_act
-    assert qa(64, 512, None, A, A, A, A, None) == ARG
-    assert qa(64, 512, A, A, A, A, MIS, None) == ARG
-    for M, K in [(0, 512), (64, 96), (64, 0), (64, 1 << 21)]:
-        assert qa(M, K, A, A, A, A, A, None) == SHAPE, (M, K)
+    assert qa(64, 512, 0, None, A, A, None, A, A, None, None) == ARG
+    assert qa(64, 512, 0, A, A, A, None, A, MIS, None, None) == ARG
+    assert qa(64, 512, 16, A, A, A, None, A, A, A, None) == ARG     # rank > 0 needs lora_down and T
+    assert qa(64, 512, 16, A, A, A, A, A, A, MIS, None) == ARG
+    assert qa(64, 512, 0, A, A, A, A, A, A, None, None) == ARG      # rank 0 takes neither
+    for M, K, r in [(0, 512, 0), (64, 96, 0), (64, 0, 0), (64, 1 << 21, 0), (64, 512, 24),
+                    (64, 512, 272)]:
+        ld, T = (A, A) if r else (None, None)
+        assert qa(M, K, r, A, A, A, ld, A, A, T, None) == SHAPE, (M, K, r)
     pw = lib.svdq_nvfp4_pack_weight
     assert pw(256, 512, 16, A, A, None, A, A, A, A, None) == ARG       # rank > 0 needs both factors
     assert pw(256, 512, 0, A, A, A, None, A, A, A, None) == ARG        # rank 0 takes none

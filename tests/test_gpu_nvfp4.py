@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import workloads as WL
-from layer_util import assert_y, np_, oracle_offline
+from layer_util import assert_T, assert_y, np_, oracle_offline
 
 pytestmark = pytest.mark.gpu
 
@@ -46,15 +46,15 @@ def _layer(spec, seed, r, out_f32=False, rows=None):
     lamd = torch.from_numpy(lam).to(DEV)
     Xd, Wd = X.to(DEV), W.to(DEV)
     gx = _g(g_x)
-    xc, xs = S.svdq_nvfp4_quantize_act(Xd, lamd, gx)
     ld = WL.from_bits(np.ascontiguousarray(L1.T)).to(DEV) if r else None
     lu = WL.from_bits(np.ascontiguousarray(L2.T)).to(DEV) if r else None
+    xc, xs, T = S.svdq_nvfp4_quantize_act(Xd, lamd, gx, lora_down=ld)
     wc, ws, gw = S.svdq_nvfp4_pack_weight(Wd, lamd, r, ld, lu)
-    T = S.svdq_lowrank_down(S.desc("fp4", spec.K, spec.N, r), Xd, lamd, ld) if r else None
     Y = S.svdq_nvfp4_linear(xc, xs, gx, wc, ws, gw, T, lu, b.to(DEV), out_f32=out_f32)
     torch.cuda.synchronize()
     return dict(xc=(np_(xc), xc_o), xs=(np_(xs), xs_o), wc=(np_(wc), wc_o), ws=(np_(ws), ws_o),
-                gw=(np_(gw)[0], gw_o), Y=(np_(Y.float())[sel], Y_o))
+                gw=(np_(gw)[0], gw_o), Y=(np_(Y.float())[sel], Y_o),
+                T=(np_(T)[sel] if r else None, T_o, Xh[sel], L1))
 
 
 @pytest.mark.parametrize("M,K,N,r", [(77, 512, 256, 16), (256, 1024, 384, 32), (130, 256, 128, 0),
@@ -71,6 +71,8 @@ def test_layer_matches_oracle(M, K, N, r, out_f32):
     for k in ("xc", "xs", "wc", "ws"):
         assert np.array_equal(*res[k]), k
     assert np.float32(res["gw"][0]) == np.float32(res["gw"][1])
+    if r:
+        assert_T(*res["T"], "nvfp4 T (fused into the activation pass)")
     assert_y(*res["Y"], out_f32, "nvfp4 Y")
 
 
@@ -89,7 +91,7 @@ def test_zero_blocks_and_scale_helper():
     xc_o, xs_o, _ = O.nvfp4_quantize_act(xb, lam, g)
     amax = torch.from_numpy(np.abs(O.bf16_to_f32(xb)).max(axis=0)).to(DEV)
     gd = S.svdq_nvfp4_scale_from_absmax(amax)
-    xc, xs = S.svdq_nvfp4_quantize_act(X.to(DEV), torch.from_numpy(lam).to(DEV), gd)
+    xc, xs, _ = S.svdq_nvfp4_quantize_act(X.to(DEV), torch.from_numpy(lam).to(DEV), gd)
     z = S.svdq_nvfp4_scale_from_absmax(torch.zeros(7, device=DEV))
     torch.cuda.synchronize()
     assert np.float32(np_(gd)[0]) == g
@@ -107,6 +109,7 @@ def test_full_size_fused_projection():
     for k in ("xc", "xs", "wc", "ws"):
         assert np.array_equal(*res[k]), k
     assert np.float32(res["gw"][0]) == np.float32(res["gw"][1])
+    assert_T(*res["T"], "nvfp4 T (C4 rows)")
     assert_y(*res["Y"], False, "nvfp4 Y (C4 rows)")
 
 
