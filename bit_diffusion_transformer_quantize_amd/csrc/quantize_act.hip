@@ -19,10 +19,12 @@
 // cannot have only 8 significant bits) and, when it is not, it lies at least
 // about 2^-48 (relative) away from every midpoint, while fp64(a * fp64(1/b))
 // is within 2^-52 of a/b.  So fp32(fp64(a * fp64(1/b))) is exactly the
-// correctly rounded fp32(a / b) (checked on the host for every bf16 a against
-// 20000 fp32 b, subnormals and all-ones significands included).  The fp64
-// reciprocals of lambda are computed once per workgroup into LDS, the one of
-// s once per lane and group.
+// correctly rounded fp32(a / b), provided fp64(1/b) is the correctly rounded
+// reciprocal (tests/test_exact_quotient.py checks this on the CPU for every
+// finite bf16 a against thousands of divisors: subnormals, all-ones
+// significands, INT4 scales, NVFP4 s g values).  The fp64 reciprocals of
+// lambda are computed once per workgroup into LDS, the one of s once per
+// lane and group.
 //
 // Outputs: the codes, scales and T in the documented row-major layouts
 // (each optional) and/or the activation operand image the GEMM reads

@@ -45,6 +45,15 @@ svdq_status check_rows_k(int64_t M, int32_t K) {
   return SVDQ_OK;
 }
 
+// The images handed to the GEMM must be exactly the sizes the descriptor and
+// M give (the kernels address them from desc and M alone, so this bounds
+// every access to the bytes the caller owns).
+svdq_status check_images(const svdq_desc* d, int64_t M, size_t ximage_bytes, size_t wimage_bytes) {
+  if (ximage_bytes != svdq::act_image_bytes(d->mode, M, d->K, d->rank)) return SVDQ_ERR_ARG;
+  if (wimage_bytes != svdq::weight_image_bytes(d->mode, d->N, d->K, d->rank)) return SVDQ_ERR_ARG;
+  return SVDQ_OK;
+}
+
 // Required pointer: non-null and 16-byte aligned.
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 // Optional pointer: null, or 16-byte aligned.
@@ -182,10 +191,13 @@ svdq_status svdq_act_image_size(const svdq_desc* d, int64_t M, size_t* bytes) {
 
 svdq_status svdq_quantize_act(const svdq_desc* d, int64_t M, const uint16_t* X,
                               const float* lambda, const uint16_t* lora_down, uint8_t* xcodes,
-                              void* xscales, float* T, void* ximage, void* stream) {
+                              void* xscales, float* T, void* ximage, size_t ximage_bytes,
+                              void* stream) {
   SVDQ_TRY(check_desc(d));
   SVDQ_TRY(check_rows_k(M, d->K));
   if (!ptr_ok(X) || !ptr_ok(lambda)) return SVDQ_ERR_ARG;
+  if (ximage_bytes != (ximage == nullptr ? 0 : svdq::act_image_bytes(d->mode, M, d->K, d->rank)))
+    return SVDQ_ERR_ARG;
   if ((xcodes == nullptr) != (xscales == nullptr)) return SVDQ_ERR_ARG;
   if (!opt_ok(xcodes) || !opt_ok(xscales) || !opt_ok(T) || !opt_ok(ximage)) return SVDQ_ERR_ARG;
   if (xcodes == nullptr && T == nullptr && ximage == nullptr) return SVDQ_ERR_ARG;
@@ -212,9 +224,10 @@ svdq_status svdq_weight_image_size(const svdq_desc* d, size_t* bytes) {
 
 svdq_status svdq_prepare_weight(const svdq_desc* d, const uint8_t* wcodes, const void* wscales,
                                 const uint16_t* lora_up, const uint16_t* bias, void* wimage,
-                                void* stream) {
+                                size_t wimage_bytes, void* stream) {
   SVDQ_TRY(check_desc(d));
   if (!ptr_ok(wcodes) || !ptr_ok(wscales) || !ptr_ok(wimage) || !opt_ok(bias)) return SVDQ_ERR_ARG;
+  if (wimage_bytes != svdq::weight_image_bytes(d->mode, d->N, d->K, d->rank)) return SVDQ_ERR_ARG;
   if (d->rank > 0 ? !ptr_ok(lora_up) : lora_up != nullptr) return SVDQ_ERR_ARG;
   SVDQ_TRY(check_device());
   return from_hip(svdq::launch_prepare_weight(d->mode, d->N, d->K, d->rank, wcodes, wscales,
@@ -222,12 +235,14 @@ svdq_status svdq_prepare_weight(const svdq_desc* d, const uint8_t* wcodes, const
 }
 
 svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const void* ximage,
-                                const void* wimage, void* Y, void* stream) {
+                                size_t ximage_bytes, const void* wimage, size_t wimage_bytes,
+                                void* Y, void* stream) {
   SVDQ_TRY(check_desc(d));
   SVDQ_TRY(check_rows_k(M, d->K));
   // outputs are limited to 2^46 elements (tile counts stay 32-bit)
   if (M > (int64_t(1) << 46) / d->N) return SVDQ_ERR_SHAPE;
   if (!ptr_ok(ximage) || !ptr_ok(wimage) || !ptr_ok(Y)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_images(d, M, ximage_bytes, wimage_bytes));
   const bool f32 = (d->flags & SVDQ_FLAG_OUT_F32) != 0u;
   SVDQ_TRY(check_device());
   if (d->mode == SVDQ_MODE_INT4)
@@ -283,7 +298,8 @@ svdq_status svdq_qk_norm_rope(int64_t M, int32_t heads, int64_t ld, uint16_t* Y,
 }
 
 svdq_status svdq_linear_forward_qk(const svdq_desc* d, int64_t M, const void* ximage,
-                                   const void* wimage, int32_t heads, const uint16_t* q_scale,
+                                   size_t ximage_bytes, const void* wimage, size_t wimage_bytes,
+                                   int32_t heads, const uint16_t* q_scale,
                                    const uint16_t* k_scale, const float* cos, const float* sin,
                                    float eps, void* Y, void* stream) {
   SVDQ_TRY(check_desc(d));
@@ -291,6 +307,7 @@ svdq_status svdq_linear_forward_qk(const svdq_desc* d, int64_t M, const void* xi
   if (M > (int64_t(1) << 46) / d->N) return SVDQ_ERR_SHAPE;
   if ((d->flags & SVDQ_FLAG_OUT_F32) != 0u) return SVDQ_ERR_ARG;
   if (!ptr_ok(ximage) || !ptr_ok(wimage)) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_images(d, M, ximage_bytes, wimage_bytes));
   SVDQ_TRY(check_qk(M, heads, d->N, Y, q_scale, k_scale, cos, sin, eps));
   SVDQ_TRY(check_device());
   const hipStream_t st = (hipStream_t)stream;

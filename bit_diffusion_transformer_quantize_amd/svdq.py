@@ -43,6 +43,7 @@ class SvdqError(RuntimeError):
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
 _DESC = ctypes.POINTER(SvdqDesc)
 
 _SIGNATURES = {
@@ -55,9 +56,10 @@ _SIGNATURES = {
     "svdq_pack_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "svdq_act_image_size": (ctypes.c_int, [_DESC, _i64, ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_weight_image_size": (ctypes.c_int, [_DESC, ctypes.POINTER(ctypes.c_size_t)]),
-    "svdq_quantize_act": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "svdq_prepare_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
+    "svdq_quantize_act": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                         _vp]),
+    "svdq_prepare_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _vp, _vp]),
     "svdq_lowrank_down": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp]),
     "svdq_lowrank_up": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
     "svdq_awq_pack_weight": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -65,8 +67,8 @@ _SIGNATURES = {
                                        _vp, _vp]),
     "svdq_qk_norm_rope": (ctypes.c_int, [_i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
                                          ctypes.c_float, _vp]),
-    "svdq_linear_forward_qk": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
-                                              ctypes.c_float, _vp, _vp]),
+    "svdq_linear_forward_qk": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _i32, _vp, _vp,
+                                              _vp, _vp, ctypes.c_float, _vp, _vp]),
     "svdq_nvfp4_scale_from_absmax": (ctypes.c_int, [_i32, _vp, _vp, _vp]),
     "svdq_nvfp4_quantize_act": (ctypes.c_int, [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                _vp]),
@@ -113,6 +115,11 @@ def desc(mode, K: int, N: int, rank: int, out_f32: bool = False, gelu_in: bool =
 
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    """Byte count of a buffer passed to the library (0 for none)."""
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream():
@@ -254,11 +261,11 @@ def svdq_quantize_act(d: SvdqDesc, X, lam, lora_down=None, xcodes=None, xscales=
     _need(xcodes, "xcodes", torch.uint8, (M, K // 2), optional=True)
     _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)), optional=True)
     _need(T, "T", torch.float32, (M, r), optional=True)
-    if ximage is not None:
-        _need(ximage, "ximage", torch.uint8, (svdq_act_image_size(d, M),))
+    _need(ximage, "ximage", torch.uint8, optional=True)
     _check("svdq_quantize_act",
            load().svdq_quantize_act(ctypes.byref(d), M, _p(X), _p(lam), _p(lora_down),
-                                    _p(xcodes), _p(xscales), _p(T), _p(ximage), _stream()))
+                                    _p(xcodes), _p(xscales), _p(T), _p(ximage), _nbytes(ximage),
+                                    _stream()))
     return xcodes, xscales, T, ximage
 
 
@@ -269,26 +276,25 @@ def svdq_prepare_weight(d: SvdqDesc, wcodes, wscales, lora_up=None, bias=None, w
     _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
     _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=True)
     _need(bias, "bias", torch.bfloat16, (N,), optional=True)
-    nbytes = svdq_weight_image_size(d)
     if wimage is None:
-        wimage = torch.empty(nbytes, dtype=torch.uint8, device=wcodes.device)
-    _need(wimage, "wimage", torch.uint8, (nbytes,))
+        wimage = torch.empty(svdq_weight_image_size(d), dtype=torch.uint8, device=wcodes.device)
+    _need(wimage, "wimage", torch.uint8)
     _check("svdq_prepare_weight",
            load().svdq_prepare_weight(ctypes.byref(d), _p(wcodes), _p(wscales), _p(lora_up),
-                                      _p(bias), _p(wimage), _stream()))
+                                      _p(bias), _p(wimage), _nbytes(wimage), _stream()))
     return wimage
 
 
 def svdq_linear_forward(d: SvdqDesc, M: int, ximage, wimage, Y=None):
     out_dtype = torch.float32 if (d.flags & SVDQ_FLAG_OUT_F32) else torch.bfloat16
-    _need(ximage, "ximage", torch.uint8, (svdq_act_image_size(d, M),))
-    _need(wimage, "wimage", torch.uint8, (svdq_weight_image_size(d),))
+    _need(ximage, "ximage", torch.uint8)
+    _need(wimage, "wimage", torch.uint8)
     if Y is None:
         Y = torch.empty(M, d.N, dtype=out_dtype, device=ximage.device)
     _need(Y, "Y", out_dtype, (M, d.N))
     _check("svdq_linear_forward",
-           load().svdq_linear_forward(ctypes.byref(d), M, _p(ximage), _p(wimage), _p(Y),
-                                      _stream()))
+           load().svdq_linear_forward(ctypes.byref(d), M, _p(ximage), _nbytes(ximage), _p(wimage),
+                                      _nbytes(wimage), _p(Y), _stream()))
     return Y
 
 
@@ -426,7 +432,8 @@ def svdq_linear_forward_qk(d: SvdqDesc, M: int, ximage, wimage, heads: int, q_sc
     _need(cos, "cos", torch.float32, (M, HEAD_DIM // 2))
     _need(sin, "sin", torch.float32, (M, HEAD_DIM // 2))
     _check("svdq_linear_forward_qk",
-           load().svdq_linear_forward_qk(ctypes.byref(d), M, _p(ximage), _p(wimage), heads,
+           load().svdq_linear_forward_qk(ctypes.byref(d), M, _p(ximage), _nbytes(ximage),
+                                         _p(wimage), _nbytes(wimage), heads,
                                          _p(q_scale), _p(k_scale), _p(cos), _p(sin), float(eps),
                                          _p(Y), _stream()))
     return Y

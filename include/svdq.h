@@ -253,23 +253,60 @@ svdq_status svdq_pack_weight(const svdq_desc* desc, const uint16_t* W, const flo
  * codes and scales re-laid in the lane order of the gfx950 matrix
  * instructions, together with the low-rank factor (T on the activation
  * side, L2 on the weight side) and, on the weight side, the bias, so that
- * one kernel streams everything it needs with contiguous copies.  The
- * layouts are internal to the library (they depend only on desc and M);
- * callers allocate the sizes below and treat the contents as opaque.
- *   INT4 code blocks: per (64-group, 32 rows) 2048 bytes: the codes as 6-bit
- *        E2M3 fields (value q/8) and the bf16 hi/lo split of the scales.
- *   FP4  code blocks: per (64-group, 32 rows) 1024 bytes of E2M1 codes and
- *        64 bytes of E8M0 scales.
- *   Low-rank blocks: per (16 ranks, 32 rows) T as bf16 hi + lo (2048 bytes);
- *        per (16 ranks, 32 columns) L2 as bf16 (1024 bytes).
+ * one kernel streams everything it needs with contiguous copies.  An image
+ * depends only on desc and M; its size is given by the two size functions
+ * below, and every call that reads or writes one takes its byte count and
+ * returns SVDQ_ERR_ARG unless it is exactly that size (so no access can
+ * leave the caller's buffer).  An image of the right size built for another
+ * descriptor is not detected: the result is then meaningless, but still in
+ * bounds.
+ *
+ * How the row-major ABI tensors map into the images (bit for bit; the
+ * parity tests decode the images and compare them with these tensors):
+ *   G = K/64 groups; rows are grouped in 32-row tiles (activation rows
+ *   padded with zero rows to a multiple of 256, weight rows = output columns
+ *   padded to a multiple of 192 (INT4) or 256 (FP4)); "slot" s = 0..63 of a
+ *   tile stands for row s % 32 of the tile and K half h = s / 32 (elements
+ *   64 g + 32 h .. +31 of the group).
+ *   INT4 code block (g, tile), 2048 bytes, at (g * tiles + tile) * 2048:
+ *     bytes 768 h + 16 r .. +15 and 768 h + 512 + 8 r .. +7 hold, as one
+ *     little-endian 192-bit string, the 32 codes q of row r and K half h,
+ *     element i in bits 6 i .. 6 i + 5 as the sign-magnitude field
+ *     (q < 0 ? 0x20 : 0) | |q| (the E2M3 encoding of q / 8);
+ *     bytes 1536 + 8 s .. +7: the scale of row s % 32 and group g as two
+ *     bf16 halves hi = bf16_RNE(s), lo = bf16_RNE(s - hi):
+ *       activation image: slot s < 32: {hi | lo << 16, hi}, s >= 32: {lo, 0};
+ *       weight image:     slot s < 32: {hi | hi << 16, lo}, s >= 32: {lo, 0}
+ *     (dwords; together they make the K slots of a bf16 outer product hold
+ *     hi*hi, lo*hi, hi*lo and lo*lo).
+ *   FP4 code block (g, tile), 1024 bytes: bytes 16 s .. +15 are the 32
+ *     packed E2M1 codes of row s % 32, K half s / 32, exactly as in the
+ *     row-major codes; FP4 scale block (g, tile), 64 bytes, after all code
+ *     blocks: byte s is the E8M0 scale of that row and 32-element block.
+ *   Activation low-rank blocks (rank > 0), after the code (and scale)
+ *     blocks: per (16-rank slice j, tile) 2048 bytes; slot s: row s % 32,
+ *     ranks 16 j + 8 (s / 32) .. +7: bytes 16 s .. +15 the 8 bf16
+ *     hi = bf16_RNE(T), bytes 1024 + 16 s .. +15 the 8 bf16
+ *     lo = bf16_RNE(T - hi), T being the fp32 down-projection that the T
+ *     output of svdq_quantize_act holds.
  *   Partial sums (activation side, rank > 0): the pass that writes the image
- *        splits K into S ranges of whole 64-groups, S = max(1, min(16,
- *        (K/64)/48, ceil(1024 / (padded rows / 16)))); when S > 1 the image
- *        ends with S fp32 partial sums of T per padded row, which a second
- *        kernel adds in order.
- *   Bias: 64 bytes per 32 columns, then 1024 bytes of zero padding.
- * Rows of the activation image are padded to a multiple of 256 and columns
- * of the weight image to 192 (INT4) or 256 (FP4); padding is zero. */
+ *     splits K into S ranges of whole 64-groups, S = max(1, min(16,
+ *     (K/64)/48, ceil(1024 / (padded rows / 16)))); when S > 1 the image
+ *     ends with S fp32 partial sums of T per padded row, which a second
+ *     kernel adds in order.
+ *   Weight low-rank blocks (rank > 0): per (16-rank slice j, 32-column tile)
+ *     1024 bytes; slot s: column s % 32, bytes 16 s .. +15 the 8 bf16
+ *     lora_up[n][16 j + 8 (s / 32) .. +7] (L2 transposed).
+ *   Bias: 64 bytes (32 bf16) per 32-column tile, zero without a bias, then
+ *     1024 bytes of zero padding.
+ * Storage: an INT4 image keeps each 4-bit code in a 6-bit field, the
+ * narrowest operand of the gfx950 matrix instructions that holds -8..7
+ * exactly, plus the bf16 scale halves: 8 bits per weight element, against
+ * 4.5 bits in the row-major codes and scales (the weight memory is 2x
+ * smaller than bf16 rather than 3.6x).  Re-expanding nibbles inside the
+ * GEMM would add VALU work to a loop whose time is already VALU and MFMA
+ * issue.  FP4 images hold the 4-bit codes as they are (4.25 bits per
+ * element, 3.8x smaller than bf16). */
 
 /* Bytes of the activation image for M rows.  Pure host function. */
 svdq_status svdq_act_image_size(const svdq_desc* desc, int64_t M, size_t* bytes);
@@ -287,24 +324,28 @@ svdq_status svdq_weight_image_size(const svdq_desc* desc, size_t* bytes);
  *   xcodes [M][K/2] and xscales (both or neither): the codes and scales in
  *     the documented row-major layout;
  *   T [M][r] float32: the down-projection (needs lora_down);
- *   ximage: the activation image (svdq_act_image_size bytes) that
- *     svdq_linear_forward reads; with rank > 0 it includes T, so lora_down
- *     is then required.
+ *   ximage: the activation image that svdq_linear_forward reads, of
+ *     ximage_bytes = svdq_act_image_size(desc, M) bytes (0 when ximage is
+ *     NULL; any other count is SVDQ_ERR_ARG); with rank > 0 it includes T,
+ *     so lora_down is then required.
  * With rank == 0, lora_down and T must be NULL.  Codes and scales are
  * bit-identical to the definition; T is accurate to fp32 accumulation. */
 svdq_status svdq_quantize_act(const svdq_desc* desc, int64_t M, const uint16_t* X,
                               const float* lambda, const uint16_t* lora_down, uint8_t* xcodes,
-                              void* xscales, float* T, void* ximage, void* stream);
+                              void* xscales, float* T, void* ximage, size_t ximage_bytes,
+                              void* stream);
 
 /* Offline: the prepared weight of a layer (the one-time packing of the
  * weights into the kernel layout, as the apatero.com page describes for the
  * fused 4-bit kernel) from the codes and scales of svdq_pack_weight, the
  * low-rank factor lora_up (bf16 [N][r]; required when rank > 0, NULL when
  * rank == 0) and the bias (bf16 [N], or NULL for none).  wimage: device
- * buffer of svdq_weight_image_size bytes, written completely. */
+ * buffer of wimage_bytes = svdq_weight_image_size(desc) bytes (any other
+ * count is SVDQ_ERR_ARG), written completely. */
 svdq_status svdq_prepare_weight(const svdq_desc* desc, const uint8_t* wcodes,
                                 const void* wscales, const uint16_t* lora_up,
-                                const uint16_t* bias, void* wimage, void* stream);
+                                const uint16_t* bias, void* wimage, size_t wimage_bytes,
+                                void* stream);
 
 /* The W4A4 GEMM with the up-projection and the bias fused (axbrief.com
  * page, section "The Mechanics ...": 4-bit weights and activations;
@@ -318,9 +359,13 @@ svdq_status svdq_prepare_weight(const svdq_desc* desc, const uint8_t* wcodes,
  * Accuracy: the integer/E2M1 block sums are exact, the rest is fp32
  * arithmetic (INT4: the product of the two group scales carries a relative
  * error below 2^-15; T and L2 enter as bf16 hi/lo splits, within 2^-16).
- * One kernel; no workspace. */
+ * ximage_bytes and wimage_bytes are the sizes of the two buffers and must
+ * equal svdq_act_image_size(desc, M) and svdq_weight_image_size(desc)
+ * (else SVDQ_ERR_ARG, before anything is enqueued).  One kernel; no
+ * workspace. */
 svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const void* ximage,
-                                const void* wimage, void* Y, void* stream);
+                                size_t ximage_bytes, const void* wimage, size_t wimage_bytes,
+                                void* Y, void* stream);
 
 /* Unfused low-rank branch, for comparison with the fused schedule (the
  * apatero.com page quotes the overhead of running the rank-32 branch as
@@ -359,10 +404,11 @@ svdq_status svdq_qk_norm_rope(int64_t M, int32_t heads, int64_t ld, uint16_t* Y,
  * of svdq_qk_norm_rope on its first 2 * heads * 128 columns (ld = N), on the
  * bf16 output: two launches on `stream` (the GEMM, then the in-place pass),
  * in INT4 and FP4 mode alike.  Output bf16 only (SVDQ_FLAG_OUT_F32 is
- * SVDQ_ERR_ARG); 2 * heads * 128 <= N; other limits as for
- * svdq_linear_forward and svdq_qk_norm_rope. */
+ * SVDQ_ERR_ARG); 2 * heads * 128 <= N; image sizes and other limits as
+ * for svdq_linear_forward and svdq_qk_norm_rope. */
 svdq_status svdq_linear_forward_qk(const svdq_desc* desc, int64_t M, const void* ximage,
-                                   const void* wimage, int32_t heads, const uint16_t* q_scale,
+                                   size_t ximage_bytes, const void* wimage, size_t wimage_bytes,
+                                   int32_t heads, const uint16_t* q_scale,
                                    const uint16_t* k_scale, const float* cos, const float* sin,
                                    float eps, void* Y, void* stream);
 

@@ -20,6 +20,20 @@ def _d(mode=0, K=512, N=512, rank=16, flags=0):
     return ctypes.byref(S.SvdqDesc(mode, K, N, rank, flags))
 
 
+def _xb(M=256, **kw):
+    """The activation image size the library gives for _d(**kw) and M (0 if
+    the descriptor or M is invalid)."""
+    n = ctypes.c_size_t(0)
+    st = _lib().svdq_act_image_size(_d(**kw), M, ctypes.byref(n))
+    return n.value if st == 0 else 0
+
+
+def _wb(**kw):
+    n = ctypes.c_size_t(0)
+    st = _lib().svdq_weight_image_size(_d(**kw), ctypes.byref(n))
+    return n.value if st == 0 else 0
+
+
 def test_exports_every_header_symbol():
     lib = _lib()
     names = S.header_symbols()
@@ -103,15 +117,22 @@ def test_weight_image_size_validation():
 
 def test_prepare_weight_validation():
     p = _lib().svdq_prepare_weight
-    assert p(None, A, A, A, A, A, None) == ARG
-    assert p(_d(mode=3), A, A, A, A, A, None) == ARG
-    assert p(_d(K=96), A, A, A, A, A, None) == SHAPE
-    assert p(_d(), None, A, A, A, A, None) == ARG               # codes null
-    assert p(_d(), A, MIS, A, A, A, None) == ARG                # scales misaligned
-    assert p(_d(), A, A, None, A, A, None) == ARG               # rank > 0 needs lora_up
-    assert p(_d(rank=0), A, A, A, A, A, None) == ARG            # rank 0 forbids it
-    assert p(_d(), A, A, A, MIS, A, None) == ARG                # bias misaligned
-    assert p(_d(), A, A, A, A, None, None) == ARG               # image null
+    wb = _wb()
+    assert p(None, A, A, A, A, A, wb, None) == ARG
+    assert p(_d(mode=3), A, A, A, A, A, wb, None) == ARG
+    assert p(_d(K=96), A, A, A, A, A, wb, None) == SHAPE
+    assert p(_d(), None, A, A, A, A, wb, None) == ARG               # codes null
+    assert p(_d(), A, MIS, A, A, A, wb, None) == ARG                # scales misaligned
+    assert p(_d(), A, A, None, A, A, wb, None) == ARG               # rank > 0 needs lora_up
+    assert p(_d(rank=0), A, A, A, A, A, _wb(rank=0), None) == ARG   # rank 0 forbids it
+    assert p(_d(), A, A, A, MIS, A, wb, None) == ARG                # bias misaligned
+    assert p(_d(), A, A, A, A, None, wb, None) == ARG               # image null
+    # the image must be exactly svdq_weight_image_size bytes
+    assert p(_d(), A, A, A, A, A, wb - 16, None) == ARG
+    assert p(_d(), A, A, A, A, A, wb + 16, None) == ARG
+    assert p(_d(), A, A, A, A, A, 0, None) == ARG
+    assert p(_d(), A, A, A, A, A, _wb(rank=32), None) == ARG        # built for another rank
+    assert p(_d(), A, A, A, A, A, _wb(mode=1), None) == ARG         # built for another mode
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -123,45 +144,58 @@ def test_prepare_weight_validation():
 def test_desc_validation(kw, status):
     lib = _lib()
     d = _d(**kw)
-    assert lib.svdq_quantize_act(d, 256, A, A, A, A, A, A, A, None) == status
+    assert lib.svdq_quantize_act(d, 256, A, A, A, A, A, A, A, 1 << 20, None) == status
     assert lib.svdq_pack_weight(d, A, A, A, A, A, A, None) == status
-    assert lib.svdq_prepare_weight(d, A, A, A, A, A, None) == status
-    assert lib.svdq_linear_forward(d, 256, A, A, A, None) == status
+    assert lib.svdq_prepare_weight(d, A, A, A, A, A, 1 << 20, None) == status
+    assert lib.svdq_linear_forward(d, 256, A, 1 << 20, A, 1 << 20, A, None) == status
     assert lib.svdq_lowrank_down(d, 256, A, A, A, A, None) == status
     assert lib.svdq_lowrank_up(d, 256, A, A, A, None) == status
 
 
 def test_null_desc():
     lib = _lib()
-    assert lib.svdq_quantize_act(None, 256, A, A, A, A, A, A, A, None) == ARG
-    assert lib.svdq_linear_forward(None, 256, A, A, A, None) == ARG
+    assert lib.svdq_quantize_act(None, 256, A, A, A, A, A, A, A, _xb(), None) == ARG
+    assert lib.svdq_linear_forward(None, 256, A, _xb(), A, _wb(), A, None) == ARG
 
 
 @pytest.mark.parametrize("M", [0, -1, 1 << 40])
 def test_rows_validation(M):
     lib = _lib()
-    assert lib.svdq_quantize_act(_d(), M, A, A, A, A, A, A, A, None) == SHAPE
-    assert lib.svdq_linear_forward(_d(), M, A, A, A, None) == SHAPE
+    assert lib.svdq_quantize_act(_d(), M, A, A, A, A, A, A, A, _xb(), None) == SHAPE
+    assert lib.svdq_linear_forward(_d(), M, A, _xb(), A, _wb(), A, None) == SHAPE
     assert lib.svdq_calibrate_lambda(M, 512, 512, A, A, A, None) == SHAPE
 
 
 def test_quantize_act_pointer_validation():
     lib = _lib()
-    q = lib.svdq_quantize_act
-    assert q(_d(), 256, None, A, A, A, A, A, A, None) == ARG        # X null
-    assert q(_d(), 256, MIS, A, A, A, A, A, A, None) == ARG         # X misaligned
-    assert q(_d(), 256, A, None, A, A, A, A, A, None) == ARG        # lambda null
-    assert q(_d(), 256, A, A, A, None, A, A, A, None) == ARG        # codes without scales
-    assert q(_d(), 256, A, A, A, A, None, A, A, None) == ARG        # scales without codes
-    assert q(_d(), 256, A, A, None, A, A, A, None, None) == ARG     # T needs lora_down
-    assert q(_d(), 256, A, A, None, A, A, None, A, None) == ARG     # image needs lora_down
-    assert q(_d(), 256, A, A, A, A, A, None, None, None) == ARG     # lora_down unused
-    assert q(_d(), 256, A, A, MIS, A, A, A, A, None) == ARG         # lora_down misaligned
-    assert q(_d(rank=0), 256, A, A, A, A, A, None, A, None) == ARG  # lora_down with rank 0
-    assert q(_d(rank=0), 256, A, A, None, A, A, A, A, None) == ARG  # T with rank 0
-    assert q(_d(), 256, A, A, A, A, A, MIS, A, None) == ARG         # T misaligned
-    assert q(_d(), 256, A, A, A, A, A, A, MIS, None) == ARG         # image misaligned
-    assert q(_d(), 256, A, A, A, None, None, None, None, None) == ARG   # no output
+    xb = _xb()
+
+    def q(d, M, X, lam, ld, xc, xs, T, xi, nb=None):
+        if nb is None:
+            nb = 0 if xi is None else xb
+        return lib.svdq_quantize_act(d, M, X, lam, ld, xc, xs, T, xi, nb, None)
+
+    assert q(_d(), 256, None, A, A, A, A, A, A) == ARG        # X null
+    assert q(_d(), 256, MIS, A, A, A, A, A, A) == ARG         # X misaligned
+    assert q(_d(), 256, A, None, A, A, A, A, A) == ARG        # lambda null
+    assert q(_d(), 256, A, A, A, None, A, A, A) == ARG        # codes without scales
+    assert q(_d(), 256, A, A, A, A, None, A, A) == ARG        # scales without codes
+    assert q(_d(), 256, A, A, None, A, A, A, None) == ARG     # T needs lora_down
+    assert q(_d(), 256, A, A, None, A, A, None, A) == ARG     # image needs lora_down
+    assert q(_d(), 256, A, A, A, A, A, None, None) == ARG     # lora_down unused
+    assert q(_d(), 256, A, A, MIS, A, A, A, A) == ARG         # lora_down misaligned
+    assert q(_d(rank=0), 256, A, A, A, A, A, None, A, _xb(rank=0)) == ARG  # lora_down, rank 0
+    assert q(_d(rank=0), 256, A, A, None, A, A, A, A, _xb(rank=0)) == ARG  # T with rank 0
+    assert q(_d(), 256, A, A, A, A, A, MIS, A) == ARG         # T misaligned
+    assert q(_d(), 256, A, A, A, A, A, A, MIS) == ARG         # image misaligned
+    assert q(_d(), 256, A, A, A, None, None, None, None) == ARG   # no output
+    # the image must be exactly svdq_act_image_size bytes, and 0 without one
+    assert q(_d(), 256, A, A, A, A, A, A, A, xb - 16) == ARG
+    assert q(_d(), 256, A, A, A, A, A, A, A, xb + 1) == ARG
+    assert q(_d(), 256, A, A, A, A, A, A, None, xb) == ARG
+    assert q(_d(), 256, A, A, A, A, A, A, A, _xb(M=512)) == ARG          # another M
+    assert q(_d(), 256, A, A, A, A, A, A, A, _xb(rank=32)) == ARG        # another rank
+    assert q(_d(), 256, A, A, A, A, A, A, A, _xb(mode=1)) == ARG         # another mode
 
 
 def test_pack_weight_pointer_validation():
@@ -177,15 +211,54 @@ def test_pack_weight_pointer_validation():
 
 def test_linear_forward_pointer_validation():
     lib = _lib()
-    f = lib.svdq_linear_forward
-    assert f(_d(), 256, None, A, A, None) == ARG    # activation image null
-    assert f(_d(), 256, MIS, A, A, None) == ARG     # misaligned
-    assert f(_d(), 256, A, None, A, None) == ARG    # weight image null
-    assert f(_d(), 256, A, MIS, A, None) == ARG
-    assert f(_d(), 256, A, A, None, None) == ARG    # Y null
-    assert f(_d(), 256, A, A, MIS, None) == ARG
+    xb, wb = _xb(), _wb()
+
+    def f(d, M, xi, wi, Y, nx=xb, nw=wb):
+        return lib.svdq_linear_forward(d, M, xi, nx, wi, nw, Y, None)
+
+    assert f(_d(), 256, None, A, A) == ARG    # activation image null
+    assert f(_d(), 256, MIS, A, A) == ARG     # misaligned
+    assert f(_d(), 256, A, None, A) == ARG    # weight image null
+    assert f(_d(), 256, A, MIS, A) == ARG
+    assert f(_d(), 256, A, A, None) == ARG    # Y null
+    assert f(_d(), 256, A, A, MIS) == ARG
     # output larger than 2^46 elements
-    assert f(_d(N=1 << 20), 1 << 27, A, A, A, None) == SHAPE
+    assert f(_d(N=1 << 20), 1 << 27, A, A, A) == SHAPE
+
+
+@pytest.mark.parametrize("what,kw", [
+    ("activation image for another M", dict(nx=_xb(M=1024))),
+    ("activation image for another rank", dict(nx=_xb(rank=32))),
+    ("activation image for rank 0", dict(nx=_xb(rank=0))),
+    ("activation image for another mode", dict(nx=_xb(mode=1))),
+    ("activation image for another K", dict(nx=_xb(K=1024))),
+    ("weight image for another rank", dict(nw=_wb(rank=32))),
+    ("weight image for another mode", dict(nw=_wb(mode=1))),
+    ("weight image for another N", dict(nw=_wb(N=1024))),
+    ("weight image for another K", dict(nw=_wb(K=1024))),
+    ("truncated activation image", dict(nx=_xb() - 16)),
+    ("truncated weight image", dict(nw=_wb() - 16)),
+    ("zero sizes", dict(nx=0, nw=0)),
+])
+def test_linear_forward_rejects_mismatched_images(what, kw):
+    """An image whose size is not the one desc and M give is refused on the
+    host (SVDQ_ERR_ARG) before anything is enqueued: a GEMM launched on it
+    would address past the buffer."""
+    lib = _lib()
+    nx, nw = kw.get("nx", _xb()), kw.get("nw", _wb())
+    assert lib.svdq_linear_forward(_d(), 256, A, nx, A, nw, A, None) == ARG, what
+    d = _d(N=9216, rank=16)
+    g = lib.svdq_linear_forward_qk
+    nxq = kw.get("nx", _xb())
+    nwq = kw.get("nw", _wb(N=9216))
+    assert g(d, 256, A, nxq, A, nwq, 24, A, A, A, A, 1e-6, A, None) == ARG, what
+
+
+def test_same_padded_rows_share_an_image_size():
+    """Activation rows are padded to a multiple of 256, so M = 200 and 256
+    give the same image: an image written for one is in bounds for the other
+    (rows past the smaller M are zero)."""
+    assert _xb(M=200) == _xb(M=256) != _xb(M=257)
 
 
 def test_lowrank_pieces_validation():
@@ -296,13 +369,15 @@ def test_qk_norm_rope_validation():
     assert call(ld=9220) == SHAPE            # rows not 16-byte aligned
     g = _lib().svdq_linear_forward_qk
     d = _d(mode=1, K=512, N=9216, rank=32)
-    assert g(d, 64, A, A, 24, A, A, A, A, 1e-6, None, None) == ARG            # Y null
-    assert g(d, 64, None, A, 24, A, A, A, A, 1e-6, A, None) == ARG
-    assert g(_d(mode=1, K=512, N=9216, rank=32, flags=1), 64, A, A, 24, A, A, A, A, 1e-6, A,
-             None) == ARG                                                      # fp32 output
-    assert g(d, 64, A, A, 37, A, A, A, A, 1e-6, A, None) == SHAPE             # 2 H 128 > N
-    assert g(d, 64, A, A, 24, A, A, A, A, 0.0, A, None) == ARG
-    assert g(_d(mode=1, K=500, N=9216), 64, A, A, 24, A, A, A, A, 1e-6, A, None) == SHAPE
+    nx, nw = _xb(M=64, mode=1, rank=32), _wb(mode=1, N=9216, rank=32)
+    assert g(d, 64, A, nx, A, nw, 24, A, A, A, A, 1e-6, None, None) == ARG    # Y null
+    assert g(d, 64, None, nx, A, nw, 24, A, A, A, A, 1e-6, A, None) == ARG
+    assert g(_d(mode=1, K=512, N=9216, rank=32, flags=1), 64, A, nx, A, nw, 24, A, A, A, A, 1e-6,
+             A, None) == ARG                                                   # fp32 output
+    assert g(d, 64, A, nx, A, nw, 37, A, A, A, A, 1e-6, A, None) == SHAPE     # 2 H 128 > N
+    assert g(d, 64, A, nx, A, nw, 24, A, A, A, A, 0.0, A, None) == ARG
+    assert g(_d(mode=1, K=500, N=9216), 64, A, nx, A, nw, 24, A, A, A, A, 1e-6, A,
+             None) == SHAPE
 
 
 def _has_gpu():
@@ -314,18 +389,19 @@ def _has_gpu():
                     "valid-looking fake pointers would be launched on")
 def test_no_device_is_a_hip_error():
     lib = _lib()
-    assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, A, None) == HIP
-    assert lib.svdq_linear_forward(_d(), 256, A, A, A, None) == HIP
-    assert lib.svdq_linear_forward(_d(mode=1), 256, A, A, A, None) == HIP
-    assert lib.svdq_prepare_weight(_d(), A, A, A, None, A, None) == HIP
+    assert lib.svdq_quantize_act(_d(), 256, A, A, A, A, A, A, A, _xb(), None) == HIP
+    assert lib.svdq_linear_forward(_d(), 256, A, _xb(), A, _wb(), A, None) == HIP
+    assert lib.svdq_linear_forward(_d(mode=1), 256, A, _xb(mode=1), A, _wb(mode=1), A,
+                                   None) == HIP
+    assert lib.svdq_prepare_weight(_d(), A, A, A, None, A, _wb(), None) == HIP
     assert lib.svdq_awq_pack_weight(64, 3072, A, A, A, A, None) == HIP
     assert lib.svdq_awq_linear(1, 64, 3072, A, A, A, A, None, 0, A, None) == HIP
     n = ctypes.c_size_t(0)
     assert lib.svdq_lowrank_factors_workspace(512, 512, 16, ctypes.byref(n)) == 0
     assert lib.svdq_lowrank_factors(512, 512, 16, A, A, 1, 2, A, A, None, A, n.value, None) == HIP
     assert lib.svdq_qk_norm_rope(64, 24, 9216, A, A, A, A, A, 1e-6, None) == HIP
-    assert lib.svdq_linear_forward_qk(_d(mode=1, N=9216), 256, A, A, 24, A, A, A, A, 1e-6, A,
-                                      None) == HIP
+    assert lib.svdq_linear_forward_qk(_d(mode=1, N=9216), 256, A, _xb(mode=1), A,
+                                      _wb(mode=1, N=9216), 24, A, A, A, A, 1e-6, A, None) == HIP
 
 
 def test_nvfp4_validation():

@@ -29,15 +29,17 @@ def _g(v):
     return torch.tensor([float(v)], dtype=torch.float32, device=DEV)
 
 
-def _layer(spec, seed, r, out_f32=False, rows=None):
+def _layer(spec, seed, r, out_f32=False, rows=None, g_div=1.0):
     """Oracle and GPU through the whole NVFP4 layer; returns what the tests
-    compare.  rows: the oracle's output only for these rows (large shapes)."""
+    compare.  rows: the oracle's output only for these rows (large shapes).
+    g_div > 1 takes the activation scale below the calibrated one, so that
+    block scales saturate at 448 and codes at 6."""
     S = _S()
     X, W, b = WL.draw(spec, seed=seed)
     xb, wb, bb = WL.bits(X), WL.bits(W), WL.bits(b)
     lam, L1, L2, _, _ = oracle_offline(xb, wb, r, "fp4")
     Xh = O.smooth_act(xb, lam)
-    g_x = O.nvfp4_global_scale(float(np.abs(O.bf16_to_f32(Xh)).max()))
+    g_x = float(np.float32(O.nvfp4_global_scale(float(np.abs(O.bf16_to_f32(Xh)).max())) / g_div))
     xc_o, xs_o, _ = O.nvfp4_quantize_act(xb, lam, g_x)
     wc_o, ws_o, gw_o = O.nvfp4_pack_weight(wb, lam, L1, L2)
     sel = slice(None) if rows is None else rows
@@ -74,6 +76,26 @@ def test_layer_matches_oracle(M, K, N, r, out_f32):
     if r:
         assert_T(*res["T"], "nvfp4 T (fused into the activation pass)")
     assert_y(*res["Y"], out_f32, "nvfp4 Y")
+
+
+@pytest.mark.parametrize("g_div", [4.0, 64.0])
+def test_activation_scale_below_calibration(g_div):
+    """Activations above what the per-tensor scale was calibrated for: the
+    E4M3 block scales saturate at 448 and the codes at 6, identically on both
+    sides."""
+    _say("nvfp4 saturating activation scale", g_div)
+    spec = WL.LinearSpec("nv_sat_300x1024x256", 300, 1024, 256, 16, "fp4", x_outliers=4,
+                         x_factor=30.0, w_outliers=2, w_factor=10.0)
+    res = _layer(spec, seed=9, r=16, g_div=g_div)
+    xs = res["xs"][1]
+    assert np.count_nonzero(xs == 0x7E) > 0, "some block scale saturates at 448"
+    codes = res["xc"][1]
+    mags = np.concatenate([codes & 7, (codes >> 4) & 7])
+    assert np.count_nonzero(mags == 7) > 0, "some code saturates at 6"
+    for k in ("xc", "xs", "wc", "ws"):
+        assert np.array_equal(*res[k]), k
+    assert_T(*res["T"], "nvfp4 T")
+    assert_y(*res["Y"], False, "nvfp4 Y")
 
 
 def test_zero_blocks_and_scale_helper():
