@@ -80,6 +80,10 @@ hipError_t launch_nvfp4_linear(bool out_f32, int64_t M, int N, int K, int rank,
 
 // Randomized truncated SVD of the smoothed weight (lowrank_factors.hip).
 size_t lowrank_factors_workspace_bytes(int N, int K, int rank);
+// Size of the static workspace of svdq_lowrank_factors_noalloc (64 MiB), and
+// the current device's copy of it.
+constexpr size_t LOWRANK_STATIC_WORKSPACE = size_t(64) << 20;
+hipError_t lowrank_static_workspace(void** ptr);
 hipError_t launch_lowrank_factors(int N, int K, int rank, const uint16_t* W, const float* lambda,
                                   uint64_t seed, int power_iters, uint16_t* lora_down,
                                   uint16_t* lora_up, double* sigma, void* workspace,

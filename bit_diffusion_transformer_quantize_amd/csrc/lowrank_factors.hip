@@ -30,6 +30,7 @@
 //     logging every rotation; rsvd_vbuild replays the log to form V;
 //     rsvd_finish orders the eigenpairs and scales the factor columns.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -869,6 +870,32 @@ hipError_t orth(const Ws& w, const double* Psum, int S, int64_t pstride, int T,
 
 size_t lowrank_factors_workspace_bytes(int N, int K, int rank) {
   return make_plan(N, K, rank).total;
+}
+
+// The workspace of the entry point that allocates nothing: a device array of
+// fixed size in this library's code object, one copy per device, held until
+// the process ends.  Host code never uses the array's name as an address;
+// it asks the runtime for each device's copy once (with that device
+// current) and passes that pointer to the kernels like a caller's workspace.
+static __device__ __align__(256) uint8_t scratch[LOWRANK_STATIC_WORKSPACE];
+
+hipError_t lowrank_static_workspace(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_lowrank_factors(int N, int K, int rank, const uint16_t* W, const float* lambda,

@@ -181,6 +181,23 @@ svdq_status svdq_lowrank_factors(int32_t N, int32_t K, int32_t rank, const uint1
                                                lora_up, sigma, workspace, (hipStream_t)stream));
 }
 
+svdq_status svdq_lowrank_factors_noalloc(int32_t N, int32_t K, int32_t rank, const uint16_t* W,
+                                         const float* lambda, uint64_t seed, int32_t power_iters,
+                                         uint16_t* lora_down, uint16_t* lora_up, double* sigma,
+                                         void* stream) {
+  SVDQ_TRY(check_factor_shape(N, K, rank));
+  if (power_iters < 0 || power_iters > 8) return SVDQ_ERR_SHAPE;
+  if (!ptr_ok(W) || !ptr_ok(lambda) || !ptr_ok(lora_down) || !ptr_ok(lora_up) || !opt_ok(sigma))
+    return SVDQ_ERR_ARG;
+  if (svdq::lowrank_factors_workspace_bytes(N, K, rank) > svdq::LOWRANK_STATIC_WORKSPACE)
+    return SVDQ_ERR_SHAPE;
+  SVDQ_TRY(check_device());
+  void* ws = nullptr;
+  SVDQ_TRY(from_hip(svdq::lowrank_static_workspace(&ws)));
+  return from_hip(svdq::launch_lowrank_factors(N, K, rank, W, lambda, seed, power_iters, lora_down,
+                                               lora_up, sigma, ws, (hipStream_t)stream));
+}
+
 svdq_status svdq_act_image_size(const svdq_desc* d, int64_t M, size_t* bytes) {
   SVDQ_TRY(check_desc(d));
   SVDQ_TRY(check_rows_k(M, d->K));

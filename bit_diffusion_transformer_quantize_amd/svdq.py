@@ -80,6 +80,8 @@ _SIGNATURES = {
                                                       ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_lowrank_factors": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, ctypes.c_uint64, _i32, _vp,
                                             _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "svdq_lowrank_factors_noalloc": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, ctypes.c_uint64, _i32,
+                                                    _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -397,6 +399,24 @@ def svdq_lowrank_factors(W, lam, rank: int, seed: int, power_iters: int = 2, lor
            load().svdq_lowrank_factors(N, K, rank, _p(W), _p(lam), ctypes.c_uint64(seed),
                                        power_iters, _p(lora_down), _p(lora_up), _p(sigma),
                                        _p(workspace), workspace.numel(), _stream()))
+    return lora_down, lora_up, sigma
+
+
+def svdq_lowrank_factors_noalloc(W, lam, rank: int, seed: int, power_iters: int, lora_down,
+                                 lora_up, sigma=None):
+    """svdq_lowrank_factors with the library's static workspace: the outputs
+    are the caller's (lora_down bf16 [r][K], lora_up bf16 [N][r], sigma fp64
+    [r] or None); the library allocates nothing."""
+    N, K = W.shape
+    _need(W, "W", torch.bfloat16, (N, K))
+    _need(lam, "lambda", torch.float32, (K,))
+    _need(lora_down, "lora_down", torch.bfloat16, (rank, K))
+    _need(lora_up, "lora_up", torch.bfloat16, (N, rank))
+    _need(sigma, "sigma", torch.float64, (rank,), optional=True)
+    _check("svdq_lowrank_factors_noalloc",
+           load().svdq_lowrank_factors_noalloc(N, K, rank, _p(W), _p(lam), ctypes.c_uint64(seed),
+                                               power_iters, _p(lora_down), _p(lora_up), _p(sigma),
+                                               _stream()))
     return lora_down, lora_up, sigma
 
 

@@ -238,6 +238,22 @@ svdq_status svdq_lowrank_factors(int32_t N, int32_t K, int32_t rank, const uint1
                                  uint16_t* lora_down, uint16_t* lora_up, double* sigma,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* svdq_lowrank_factors for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same results, bit for bit, with the
+ * workspace in a static device array of 64 MiB that the library holds on
+ * each device it runs on until the process ends (no allocation, no workspace
+ * argument).  Shapes whose svdq_lowrank_factors_workspace exceeds 64 MiB
+ * (e.g. 3072 x 3072 at rank 32 fits, 9216 x 3072 does not) give
+ * SVDQ_ERR_SHAPE before anything is enqueued; other arguments and errors as
+ * for svdq_lowrank_factors.  All calls on one device share that array:
+ * calls whose work overlaps on one device (different streams, or threads)
+ * race and must be serialised by the caller. */
+svdq_status svdq_lowrank_factors_noalloc(int32_t N, int32_t K, int32_t rank, const uint16_t* W,
+                                         const float* lambda, uint64_t seed, int32_t power_iters,
+                                         uint16_t* lora_down, uint16_t* lora_up, double* sigma,
+                                         void* stream);
+
 /* Offline weight packing (same two pages; the residual branch of W4A4).
  *   W_hat[n][k] = fp32(W[n][k] * lambda[k]);
  *   acc = 0; for i = 0..r-1: acc = fp32(acc + L1[k][i] * L2[i][n]);

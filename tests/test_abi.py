@@ -343,6 +343,22 @@ def test_lowrank_factors_validation():
     assert call(N=3000) == SHAPE
 
 
+def test_lowrank_factors_noalloc_validation():
+    """The no-allocation SVD refuses, on the host, shapes whose workspace
+    exceeds its 64 MiB static array, and bad pointers, like the workspace
+    entry point."""
+    f = _lib().svdq_lowrank_factors_noalloc
+    assert f(9216, 3072, 32, A, A, 1, 2, A, A, None, None) == SHAPE     # 118 MiB of workspace
+    assert f(3072, 12288, 32, A, A, 1, 2, A, A, None, None) == SHAPE
+    assert f(500, 512, 16, A, A, 1, 2, A, A, None, None) == SHAPE       # N not a multiple of 128
+    assert f(512, 512, 8, A, A, 1, 2, A, A, None, None) == SHAPE        # rank below 16
+    assert f(512, 512, 16, A, A, 1, 9, A, A, None, None) == SHAPE       # power iterations
+    assert f(512, 512, 16, None, A, 1, 2, A, A, None, None) == ARG
+    assert f(512, 512, 16, A, A, 1, 2, MIS, A, None, None) == ARG
+    assert f(512, 512, 16, A, A, 1, 2, A, None, None, None) == ARG
+    assert f(512, 512, 16, A, A, 1, 2, A, A, MIS, None) == ARG
+
+
 def test_qk_norm_rope_validation():
     f = _lib().svdq_qk_norm_rope
     ok = dict(M=64, H=24, ld=9216, Y=A, qs=A, ks=A, c=A, s=A, eps=1e-6)
@@ -399,6 +415,7 @@ def test_no_device_is_a_hip_error():
     n = ctypes.c_size_t(0)
     assert lib.svdq_lowrank_factors_workspace(512, 512, 16, ctypes.byref(n)) == 0
     assert lib.svdq_lowrank_factors(512, 512, 16, A, A, 1, 2, A, A, None, A, n.value, None) == HIP
+    assert lib.svdq_lowrank_factors_noalloc(512, 512, 16, A, A, 1, 2, A, A, None, None) == HIP
     assert lib.svdq_qk_norm_rope(64, 24, 9216, A, A, A, A, A, 1e-6, None) == HIP
     assert lib.svdq_linear_forward_qk(_d(mode=1, N=9216), 256, A, _xb(mode=1), A,
                                       _wb(mode=1, N=9216), 24, A, A, A, A, 1e-6, A, None) == HIP
