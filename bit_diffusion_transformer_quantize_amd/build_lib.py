@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libsvdq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["svdq_api.cpp", "quantize_act.hip", "pack_weight.hip", "images.hip", "gemm_int4.hip",
-           "gemm_fp4.hip", "lowrank_up.hip", "awq.hip", "lowrank_factors.hip", "qk_norm_rope.hip",
+           "gemm_fp4.hip", "gemm_int4_gelu.hip", "lowrank_up.hip", "awq.hip", "lowrank_factors.hip", "qk_norm_rope.hip",
            "nvfp4.hip"]
 
 FLAGS = [

@@ -78,6 +78,14 @@ hipError_t launch_nvfp4_linear(bool out_f32, int64_t M, int N, int K, int rank,
                                const float* T, const uint16_t* lora_up, const uint16_t* bias,
                                void* Y, hipStream_t s);
 
+// The MLP up-projection with the down layer's activation pass fused into
+// its epilogue (gemm_int4_gelu.hip).
+size_t gelu_quantize_workspace_bytes(int64_t M, int N_up, int rank_dn);
+hipError_t launch_gelu_quantize(int64_t M, int N, int K, int rank_up, const void* ximage,
+                                const void* wimage, int rank_dn, const float* lambda_dn,
+                                const uint16_t* lora_dn, void* dimage, uint16_t* Y, float* T,
+                                void* workspace, hipStream_t s);
+
 // Randomized truncated SVD of the smoothed weight (lowrank_factors.hip).
 size_t lowrank_factors_workspace_bytes(int N, int K, int rank);
 // Size of the static workspace of svdq_lowrank_factors_noalloc (64 MiB), and

@@ -34,6 +34,7 @@
 // image the grid also covers the padding rows up to a multiple of 256, which
 // come out as zeros.
 #include "common.h"
+#include "gelu_table.h"
 #include "image.h"
 #include "kernels.h"
 #include "nvfp4_codec.h"
@@ -52,33 +53,41 @@ struct QaShape {
   static constexpr int kThreads = 64 * kWaves;
 };
 
+// The fp64 reciprocals of lambda sit in LDS with 16 bytes of padding after
+// every 16 entries: the four lanes of a row read entries 16 apart, which
+// then fall into different banks.
+__device__ __forceinline__ int rl_idx(int c) { return c + ((c >> 4) << 1); }
+
 // LDS: the reciprocal table during the main loop, the T partials afterwards.
 template <int MODE, int RB>
 struct QaLds {
-  static constexpr int kRcp = QA_KCHUNK * 8;
+  static constexpr int kRcp = (QA_KCHUNK + QA_KCHUNK / 8) * 8;
   static constexpr int kRed = QaShape<MODE, RB>::kWaves * (RB > 0 ? RB : 1) * 4 * 64 * 4;
   static constexpr int kBytes = kRcp > kRed ? kRcp : kRed;
 };
 
-// 16 INT4 codes (nibbles 0..15, two's complement) -> 16 E2M3 fields of
-// 6 bits (sign-magnitude, value q/8) packed little-endian into 96 bits.
-__device__ __forceinline__ void fp6_fields16(const uint32_t (&c)[16], uint32_t& d0, uint32_t& d1,
-                                             uint32_t& d2) {
-  uint64_t lo = 0, hi = 0;
+// 16 INT4 codes as 16 E2M3 fields of 6 bits (sign-magnitude, value q/8)
+// packed little-endian into 96 bits (three dwords), the layout of half a
+// K half of the image, from 16 clamped quotients cq (in [-8, 7]) by the gfx950
+// conversion to FP6 (E2M3): it divides by 2^3 (the exponent of the scale
+// operand 8), rounds to nearest even on the E2M3 grid, whose step is 1/8 on
+// [0, 2), so field i is the E2M3 encoding of rint_even(cq[i]) / 8.  Its two
+// sources are interleaved (field 2i from the first, 2i + 1 from the second);
+// the upper halves of both are left undefined, only fields 0..15 (the low
+// 96 bits) are kept.  A quotient that rounds to zero from below gives the
+// negative-zero field 0x20, which the matrix instruction reads as 0.
+__device__ __forceinline__ void fp6_fields16_hw(const float (&cq)[16], uint32_t& d0, uint32_t& d1,
+                                                uint32_t& d2) {
+  v16f ev, od;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint64_t f = c[i] < 8u ? c[i] : 0x30u - c[i];
-    const int b = 6 * i;
-    if (b < 64) {
-      lo |= f << b;
-      if (b > 58) hi |= f >> (64 - b);
-    } else {
-      hi |= f << (b - 64);
-    }
+  for (int i = 0; i < 8; ++i) {
+    ev[i] = cq[2 * i];
+    od[i] = cq[2 * i + 1];
   }
-  d0 = (uint32_t)lo;
-  d1 = (uint32_t)(lo >> 32);
-  d2 = (uint32_t)hi;
+  const v6i f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+  d0 = (uint32_t)f[0];
+  d1 = (uint32_t)f[1];
+  d2 = (uint32_t)f[2];
 }
 
 // Where a lane writes the activation image: null img = no image.  With
@@ -91,153 +100,6 @@ struct QaImage {
   int S;
   const float* g = nullptr;  // NVFP4: the per-tensor scale (device)
 };
-
-// GELU with the tanh approximation in the cancellation-free form
-//   GELU(x) = x / (1 + e^z),  z = -2 sqrt(2/pi) (x + 0.044715 x^3)
-// (0.5 (1 + tanh y) = 1 / (1 + e^-2y)), every step one IEEE fp32 operation
-// with round-to-nearest-even and no fused multiply-add, so that the bf16
-// rounding of the result, which decides the 4-bit codes, is reproducible.
-// e^z uses Cody and Waite's reduction z = k ln2 + r with ln 2 split as
-// 0.693359375 (10 significant bits, so k * 0.693359375 is exact) plus the
-// fp32 remainder, a degree-7 Taylor polynomial of e^r in Horner form and
-// exact scaling by 2^k; z is clamped to [-104, 104].
-//
-// The input is bf16, so the function has 65536 arguments: the table below
-// holds bf16_RNE(GELU(x)) for every bf16 bit pattern, evaluated by the
-// compiler's constant evaluator, whose float arithmetic is IEEE with
-// round-to-nearest-even, one rounding per operation.  Constant evaluation
-// admits no infinities, so the two places where the fp32 sequence overflows
-// take their results directly: x^3 overflows only when |x| > 2^42, where
-// z is clamped to -104 (x > 0: e^z = 0 in fp32, GELU = x) or to +104
-// (x < 0: e^z = inf, GELU = -0); and p 2^k rounds to inf in fp32 exactly
-// when it reaches 2^128 - 2^103, where GELU = x / inf = -0 (z > 0 there, so
-// x < 0).  Inf and NaN inputs map to themselves.
-namespace gelu_table {
-
-constexpr double kLn2 = 0.69314718055994530942;
-constexpr float kA = (float)0.044715;
-constexpr float kC1 = 0.693359375f;
-constexpr float kC2 = (float)(kLn2 - 0.693359375);
-constexpr float kL = (float)(1.0 / kLn2);
-
-constexpr double csqrt(double v) {  // Newton's iteration to the correctly rounded root
-  double r = v > 1.0 ? v : 1.0;
-  for (int i = 0; i < 200; ++i) r = 0.5 * (r + v / r);
-  // the iteration settles within one ulp; step to the root whose square is closest
-  for (int i = 0; i < 4; ++i) {
-    const double lo = r - r * 0x1p-53, hi = r + r * 0x1p-52;
-    const double e0 = r * r - v, el = lo * lo - v, eh = hi * hi - v;
-    const double a0 = e0 < 0 ? -e0 : e0, al = el < 0 ? -el : el, ah = eh < 0 ? -eh : eh;
-    r = al < a0 ? lo : (ah < a0 ? hi : r);
-  }
-  return r;
-}
-constexpr float kB = (float)(-2.0 * csqrt(2.0 / 3.14159265358979323846));
-
-constexpr float rint_even(float v) {  // round to an integer, ties to even (|v| < 2^23)
-  const float a = v < 0 ? -v : v;
-  const float t = (a + 8388608.0f) - 8388608.0f;
-  return v < 0 ? -t : t;
-}
-constexpr double pow2(int k) {  // 2^k for -1022 <= k <= 1023, from its exponent field
-  return __builtin_bit_cast(double, (uint64_t)(k + 1023) << 52);
-}
-constexpr uint16_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-constexpr uint16_t entry(uint32_t xb) {
-  if ((xb & 0x7F80u) == 0x7F80u) return (uint16_t)xb;           // inf, NaN
-  const float x = __builtin_bit_cast(float, xb << 16);
-  const float ax = x < 0 ? -x : x;
-  if (ax > 0x1p42f) return x > 0 ? (uint16_t)xb : (uint16_t)0x8000u;
-  const float x3 = (x * x) * x;
-  const float u = x + kA * x3;
-  float z = kB * u;
-  z = z < -104.0f ? -104.0f : (z > 104.0f ? 104.0f : z);
-  const float k = rint_even(z * kL);
-  const float r = (z - k * kC1) - k * kC2;
-  float p = (float)(1.0 / 5040.0);
-  p = p * r + (float)(1.0 / 720.0);
-  p = p * r + (float)(1.0 / 120.0);
-  p = p * r + (float)(1.0 / 24.0);
-  p = p * r + (float)(1.0 / 6.0);
-  p = p * r + 0.5f;
-  p = p * r + 1.0f;
-  p = p * r + 1.0f;
-  const double v = (double)p * pow2((int)k);                  // exact
-  if (v >= 0x1p128 - 0x1p103) return (uint16_t)0x8000u;       // e^z = inf, x < 0
-  const float e = (float)v;                                   // one rounding
-  return bf16_rne(x / (1.0f + e));
-}
-// Outside a band of exponents the bf16 GELU follows two rules, checked
-// against the full definition for all 65536 inputs below: |x| < 2^-10 gives
-// bf16_RNE(x / 2) (there e^z = 1 - 1.6 x + ..., so x / (1 + e^z) is within
-// 2^-10 of x / 2, inside half a bf16 ulp), and |x| >= 32 gives x for
-// positive x and -0 for negative x (inf and NaN map to themselves).  Only the
-// 15 binades in between (biased exponents 117..131, both signs: 3840
-// entries) are tabulated.
-constexpr int kLoExp = 117, kHiExp = 131;
-constexpr int kBand = kHiExp - kLoExp + 1;
-constexpr int kEntries = 2 * kBand * 128;
-
-constexpr uint16_t half_rule(uint32_t xb) {
-  return bf16_rne(__builtin_bit_cast(float, xb << 16) * 0.5f);
-}
-constexpr uint16_t rule(uint32_t xb) {  // inputs outside the band
-  const uint32_t e = (xb >> 7) & 0xFFu;
-  if (e < (uint32_t)kLoExp) return half_rule(xb);
-  if (e == 0xFFu || (xb & 0x8000u) == 0) return (uint16_t)xb;
-  return (uint16_t)0x8000u;
-}
-constexpr int band_index(uint32_t xb) {
-  return (int)((xb >> 15) * kBand + (((xb >> 7) & 0xFFu) - kLoExp)) * 128 + (int)(xb & 0x7Fu);
-}
-constexpr bool rules_hold() {
-  for (uint32_t i = 0; i < 65536; ++i) {
-    const uint32_t e = (i >> 7) & 0xFFu;
-    if ((e < (uint32_t)kLoExp || e > (uint32_t)kHiExp) && rule(i) != entry(i)) return false;
-  }
-  return true;
-}
-static_assert(rules_hold(), "the GELU rules outside the tabulated band");
-
-struct Table {
-  uint16_t v[kEntries];
-};
-constexpr Table make() {
-  Table t{};
-  for (uint32_t s = 0; s < 2; ++s)
-    for (uint32_t e = kLoExp; e <= (uint32_t)kHiExp; ++e)
-      for (uint32_t m = 0; m < 128; ++m) {
-        const uint32_t xb = (s << 15) | (e << 7) | m;
-        t.v[band_index(xb)] = entry(xb);
-      }
-  return t;
-}
-
-}  // namespace gelu_table
-
-__device__ constexpr gelu_table::Table kGeluBand = gelu_table::make();
-
-// bf16 GELU of one input (low 16 bits of b) from the band table in LDS and
-// the two rules.  Branch-free: the table index is clamped into range.
-__device__ __forceinline__ uint32_t gelu_one(uint32_t b, const uint16_t* tab) {
-  using namespace gelu_table;
-  const uint32_t e = (b >> 7) & 0xFFu;
-  const bool in_band = e >= (uint32_t)kLoExp && e <= (uint32_t)kHiExp;
-  const uint32_t ec = in_band ? e : (uint32_t)kLoExp;
-  const uint32_t idx = ((b >> 15) * kBand + (ec - kLoExp)) * 128 + (b & 0x7Fu);
-  const uint32_t t = tab[idx];
-  const uint32_t half = f32_to_bf16(__uint_as_float(b << 16) * 0.5f);
-  const uint32_t big = (e == 0xFFu || (b & 0x8000u) == 0) ? b : 0x8000u;
-  return in_band ? t : (e < (uint32_t)kLoExp ? half : big);
-}
-
-__device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w, const uint16_t* tab) {
-  return gelu_one(w & 0xFFFFu, tab) | (gelu_one(w >> 16, tab) << 16);
-}
 
 // MODE 0 = INT4, 1 = FP4, 2 = NVFP4 (row-major codes and scales only, no
 // image).  RB = rank / 16 (0 = no down-projection).
@@ -279,7 +141,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   for (int kc = kbeg; kc < kend; kc += QA_KCHUNK) {
     const int kn = min(QA_KCHUNK, kend - kc);
     __syncthreads();  // the previous chunk is done with the table
-    for (int c = threadIdx.x; c < kn; c += QA_THREADS) rlam[c] = 1.0 / (double)lambda[kc + c];
+    for (int c = threadIdx.x; c < kn; c += QA_THREADS) rlam[rl_idx(c)] = 1.0 / (double)lambda[kc + c];
     __syncthreads();
     const int ntiles = kn >> 6;
     // Loads of a tile without a branch (rows past M and tiles past the chunk
@@ -317,7 +179,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const uint32_t xbits = (xw[i >> 1] >> (e * 16)) & 0xFFFFu;
-          q[e] = (float)((double)bf16_to_f32(xbits) * rlam[kl + i + e]);
+          q[e] = (float)((double)bf16_to_f32(xbits) * rlam[rl_idx(kl + i + e)]);
         }
         // RNE to bf16 (v_cvt_pk_bf16_f32: the same rounding as the
         // bit-level definition for every finite value)
@@ -336,24 +198,23 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           amax = fmaxf(amax, __shfl_xor(amax, 16));
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           const float s = amax / 7.0f;
-          uint32_t c[16];
+          // cq = clamp(fp32(xh / s), -8, 7); the code is rint_even(cq) (the
+          // bounds are integers, so clamping before rounding is the same)
+          float cq[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) c[i] = 0u;
+          for (int i = 0; i < 16; ++i) cq[i] = 0.f;
           if (s != 0.f) {
             const double rs = 1.0 / (double)s;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float q = __builtin_rintf((float)((double)xh[i] * rs));  // = rint(fp32(xh / s))
-              q = fminf(fmaxf(q, -8.0f), 7.0f);
-              c[i] = (uint32_t)(int)q & 0xFu;
-            }
+            for (int i = 0; i < 16; ++i)
+              cq[i] = __builtin_amdgcn_fmed3f((float)((double)xh[i] * rs), -8.0f, 7.0f);
           }
           if (xcodes != nullptr && row_ok) {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              w0 |= c[i] << (4 * i);
-              w1 |= c[8 + i] << (4 * i);
+              w0 |= ((uint32_t)(int)__builtin_rintf(cq[i]) & 0xFu) << (4 * i);
+              w1 |= ((uint32_t)(int)__builtin_rintf(cq[8 + i]) & 0xFu) << (4 * i);
             }
             *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
             if (j == 0) reinterpret_cast<float*>(xscales)[row * (int64_t)(K >> 6) + (k0 >> 6)] = s;
@@ -364,7 +225,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
             uint8_t* blk = qi.img + ((int64_t)(k0 >> 6) * qi.RT + irt) * I4_BLOCK;
             uint8_t* half = blk + (j >> 1) * 768;
             uint32_t d0, d1, d2;
-            fp6_fields16(c, d0, d1, d2);
+            fp6_fields16_hw(cq, d0, d1, d2);
             if ((j & 1) == 0) {
               *reinterpret_cast<v2u*>(half + 16 * irr) = v2u{d0, d1};
               *reinterpret_cast<uint32_t*>(half + 16 * irr + 8) = d2;
@@ -384,12 +245,29 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
           amax = fmaxf(amax, __shfl_xor(amax, 16));
           const int e = e8m0_exponent(amax);
-          const float sc = exp2i(-e);
           uint32_t w0 = 0, w1 = 0;
+          if (e >= -100) {
+            // the gfx950 conversion: E2M1 nearest-even of x * 2^-e (the
+            // exponent of the scale operand), saturating at 6, sign kept
+            const float sc = exp2i(e);
+            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[0], xh[1], sc, 0);
+            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[2], xh[3], sc, 1);
+            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[4], xh[5], sc, 2);
+            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[6], xh[7], sc, 3);
+            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[8], xh[9], sc, 0);
+            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[10], xh[11], sc, 1);
+            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[12], xh[13], sc, 2);
+            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[14], xh[15], sc, 3);
+          } else {
+            // blocks whose maximum is below 2^-98: the scaled values can come
+            // from fp32 subnormals, whose handling by the conversion is not
+            // relied on
+            const float sc = exp2i(-e);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) w0 |= e2m1_code(xh[i] * sc) << (4 * i);
+            for (int i = 0; i < 8; ++i) w0 |= e2m1_code(xh[i] * sc) << (4 * i);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) w1 |= e2m1_code(xh[8 + i] * sc) << (4 * i);
+            for (int i = 0; i < 8; ++i) w1 |= e2m1_code(xh[8 + i] * sc) << (4 * i);
+          }
           if (xcodes != nullptr && row_ok) {
             *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
             if ((j & 1) == 0)

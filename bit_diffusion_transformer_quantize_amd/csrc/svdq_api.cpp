@@ -269,6 +269,61 @@ svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const void* ximag
                                            (hipStream_t)stream));
 }
 
+namespace {
+// An INT4 up layer feeding an INT4 down layer whose input is GELU of the up
+// layer's output (down->K == up->N), down rank at most 128.
+svdq_status check_mlp_pair(const svdq_desc* up, const svdq_desc* down) {
+  SVDQ_TRY(check_desc(up));
+  SVDQ_TRY(check_desc(down));
+  if (up->mode != SVDQ_MODE_INT4 || down->mode != SVDQ_MODE_INT4) return SVDQ_ERR_ARG;
+  if ((down->flags & SVDQ_FLAG_GELU_IN) == 0u) return SVDQ_ERR_ARG;
+  if ((up->flags & SVDQ_FLAG_OUT_F32) != 0u) return SVDQ_ERR_ARG;
+  if (down->K != up->N) return SVDQ_ERR_SHAPE;
+  if (down->rank > 128) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+}  // namespace
+
+svdq_status svdq_gelu_quantize_workspace_size(const svdq_desc* up, int64_t M,
+                                              const svdq_desc* down, size_t* bytes) {
+  SVDQ_TRY(check_mlp_pair(up, down));
+  SVDQ_TRY(check_rows_k(M, up->K));
+  SVDQ_TRY(check_rows_k(M, down->K));
+  if (bytes == nullptr) return SVDQ_ERR_ARG;
+  *bytes = svdq::gelu_quantize_workspace_bytes(M, up->N, down->rank);
+  return SVDQ_OK;
+}
+
+svdq_status svdq_linear_forward_gelu_quantize(const svdq_desc* up, int64_t M, const void* ximage,
+                                              size_t ximage_bytes, const void* wimage,
+                                              size_t wimage_bytes, const svdq_desc* down,
+                                              const float* lambda_down, const uint16_t* lora_down,
+                                              void* ximage_down, size_t ximage_down_bytes,
+                                              uint16_t* Y, float* T, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  SVDQ_TRY(check_mlp_pair(up, down));
+  SVDQ_TRY(check_rows_k(M, up->K));
+  SVDQ_TRY(check_rows_k(M, down->K));
+  if (M > (int64_t(1) << 46) / up->N) return SVDQ_ERR_SHAPE;
+  if (!ptr_ok(ximage) || !ptr_ok(wimage) || !ptr_ok(lambda_down) || !ptr_ok(ximage_down) ||
+      !opt_ok(Y) || !opt_ok(T) || !opt_ok(workspace))
+    return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_images(up, M, ximage_bytes, wimage_bytes));
+  if (ximage_down_bytes != svdq::act_image_bytes(down->mode, M, down->K, down->rank))
+    return SVDQ_ERR_ARG;
+  if (down->rank > 0) {
+    if (!ptr_ok(lora_down) || workspace == nullptr) return SVDQ_ERR_ARG;
+  } else if (lora_down != nullptr || T != nullptr) {
+    return SVDQ_ERR_ARG;
+  }
+  if (workspace_bytes < svdq::gelu_quantize_workspace_bytes(M, up->N, down->rank))
+    return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_device());
+  return from_hip(svdq::launch_gelu_quantize(M, up->N, up->K, up->rank, ximage, wimage,
+                                             down->rank, lambda_down, lora_down, ximage_down, Y,
+                                             T, workspace, (hipStream_t)stream));
+}
+
 svdq_status svdq_lowrank_down(const svdq_desc* d, int64_t M, const uint16_t* X,
                               const float* lambda, const uint16_t* lora_down, float* T,
                               void* stream) {

@@ -60,6 +60,10 @@ _SIGNATURES = {
                                          _vp]),
     "svdq_prepare_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _vp, _vp]),
+    "svdq_gelu_quantize_workspace_size": (ctypes.c_int, [_DESC, _i64, _DESC,
+                                                         ctypes.POINTER(ctypes.c_size_t)]),
+    "svdq_linear_forward_gelu_quantize": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _DESC, _vp,
+                                                         _vp, _vp, _sz, _vp, _vp, _vp, _sz, _vp]),
     "svdq_lowrank_down": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp]),
     "svdq_lowrank_up": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp]),
     "svdq_awq_pack_weight": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -298,6 +302,41 @@ def svdq_linear_forward(d: SvdqDesc, M: int, ximage, wimage, Y=None):
            load().svdq_linear_forward(ctypes.byref(d), M, _p(ximage), _nbytes(ximage), _p(wimage),
                                       _nbytes(wimage), _p(Y), _stream()))
     return Y
+
+
+def svdq_gelu_quantize_workspace_size(up: SvdqDesc, M: int, down: SvdqDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("svdq_gelu_quantize_workspace_size",
+           load().svdq_gelu_quantize_workspace_size(ctypes.byref(up), M, ctypes.byref(down),
+                                                    ctypes.byref(n)))
+    return n.value
+
+
+def svdq_linear_forward_gelu_quantize(up: SvdqDesc, M: int, ximage, wimage, down: SvdqDesc,
+                                      lam_down, lora_down=None, ximage_down=None, Y=None, T=None,
+                                      workspace=None):
+    """The up layer's GEMM whose epilogue applies GELU and writes the down
+    layer's activation image (returns it; Y and T are written when given)."""
+    _need(ximage, "ximage", torch.uint8)
+    _need(wimage, "wimage", torch.uint8)
+    _need(lam_down, "lambda_down", torch.float32, (up.N,))
+    _need(lora_down, "lora_down", torch.bfloat16, (down.rank, up.N), optional=True)
+    if ximage_down is None:
+        ximage_down = torch.empty(svdq_act_image_size(down, M), dtype=torch.uint8,
+                                  device=ximage.device)
+    _need(ximage_down, "ximage_down", torch.uint8)
+    _need(Y, "Y", torch.bfloat16, (M, up.N), optional=True)
+    _need(T, "T", torch.float32, (M, down.rank), optional=True)
+    nws = svdq_gelu_quantize_workspace_size(up, M, down)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=ximage.device)
+    _need(workspace, "workspace", torch.uint8, optional=True)
+    _check("svdq_linear_forward_gelu_quantize",
+           load().svdq_linear_forward_gelu_quantize(
+               ctypes.byref(up), M, _p(ximage), _nbytes(ximage), _p(wimage), _nbytes(wimage),
+               ctypes.byref(down), _p(lam_down), _p(lora_down), _p(ximage_down),
+               _nbytes(ximage_down), _p(Y), _p(T), _p(workspace), _nbytes(workspace), _stream()))
+    return ximage_down
 
 
 def svdq_lowrank_down(d: SvdqDesc, X, lam, lora_down, T=None):

@@ -383,6 +383,44 @@ svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const void* xi
                                 size_t ximage_bytes, const void* wimage, size_t wimage_bytes,
                                 void* Y, void* stream);
 
+/* The MLP up-projection with the next layer's activation pass fused into
+ * its epilogue (Nunchaku Lite page on axbrief.com, section "The Trade-off
+ * Between Fused Kernels and Generality": neighbouring steps of the block
+ * fused into one kernel to cut memory traffic; apatero.com page, section "O
+ * que e Nunchaku ...": the low-rank down-projection shares the quantization
+ * kernel's activations).  `up` is an INT4 layer, `down` the INT4 layer that
+ * reads GELU of its output (down->K == up->N, down->flags has
+ * SVDQ_FLAG_GELU_IN, down->rank <= 128).  In one pass over the up layer's
+ * output tiles, with the up layer's images ximage / wimage (sizes as for
+ * svdq_linear_forward):
+ *   y = the up layer's output, rounded to bf16 exactly as
+ *       svdq_linear_forward writes it (written to Y, bf16 [M][up->N], when Y
+ *       is not NULL);
+ *   x = GELU(y) as SVDQ_FLAG_GELU_IN defines it, then the down layer's
+ *       activation pass on x: ximage_down (svdq_act_image_size(down, M) bytes)
+ *       receives the same codes, scales and T halves that svdq_quantize_act
+ *       of `down` on x writes into the image (T is fp32-accumulated in a
+ *       different order: over 128-column tiles, then over the tiles), and T,
+ *       when not NULL, fp32 [M][down->rank], the down-projection itself.
+ * The bf16 intermediate is never written (unless Y asks for it) nor read.
+ * lambda_down: float32 [up->N]; lora_down: bf16 [down->rank][up->N] (NULL,
+ * like T, when down->rank is 0).  workspace: device memory of at least
+ * svdq_gelu_quantize_workspace_size bytes (the per-tile partial sums of T;
+ * contents undefined afterwards; 0 bytes and NULL allowed when down->rank
+ * is 0).  Two launches on `stream` (the fused GEMM, then the sum of the T
+ * partials).  Other arguments and errors as for svdq_linear_forward; an
+ * up or down descriptor that is not INT4, or a down descriptor without
+ * SVDQ_FLAG_GELU_IN, is SVDQ_ERR_ARG. */
+svdq_status svdq_gelu_quantize_workspace_size(const svdq_desc* up, int64_t M,
+                                              const svdq_desc* down, size_t* bytes);
+svdq_status svdq_linear_forward_gelu_quantize(const svdq_desc* up, int64_t M, const void* ximage,
+                                              size_t ximage_bytes, const void* wimage,
+                                              size_t wimage_bytes, const svdq_desc* down,
+                                              const float* lambda_down, const uint16_t* lora_down,
+                                              void* ximage_down, size_t ximage_down_bytes,
+                                              uint16_t* Y, float* T, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
 /* Unfused low-rank branch, for comparison with the fused schedule (the
  * apatero.com page quotes the overhead of running the rank-32 branch as
  * separate kernels).  svdq_lowrank_down re-reads X and writes

@@ -359,6 +359,46 @@ def test_lowrank_factors_noalloc_validation():
     assert f(512, 512, 16, A, A, 1, 2, A, A, MIS, None) == ARG
 
 
+def test_gelu_quantize_validation():
+    """The fused MLP-up entry point refuses, on the host, descriptors that do
+    not form an INT4 up layer feeding an INT4 GELU-input down layer, and
+    images, workspaces and pointers of the wrong size or alignment."""
+    lib = _lib()
+    f = lib.svdq_linear_forward_gelu_quantize
+    up = dict(mode=0, K=512, N=384, rank=16)
+    dn = dict(mode=0, K=384, N=256, rank=32, flags=2)
+    nx, nw, nd = _xb(M=300, **up), _wb(**up), _xb(M=300, **dn)
+    n = ctypes.c_size_t(0)
+    assert lib.svdq_gelu_quantize_workspace_size(_d(**up), 300, _d(**dn), ctypes.byref(n)) == 0
+    ws = n.value
+    assert ws == 384 // 128 * 512 * 32 * 4
+
+    def call(u=up, d=dn, M=300, xi=A, nx_=nx, wi=A, nw_=nw, lam=A, ld=A, di=A, nd_=nd, Y=None,
+             T=None, w=A, nws=ws):
+        return f(_d(**u), M, xi, nx_, wi, nw_, _d(**d), lam, ld, di, nd_, Y, T, w, nws, None)
+
+    assert call(d=dict(dn, flags=0)) == ARG                 # down layer without the GELU flag
+    assert call(u=dict(up, mode=1)) == ARG                  # FP4 up layer
+    assert call(d=dict(dn, mode=1)) == ARG                  # FP4 down layer
+    assert call(u=dict(up, flags=1)) == ARG                 # fp32 up output
+    assert call(d=dict(dn, K=512)) == SHAPE                 # down K != up N
+    assert call(d=dict(dn, rank=144)) == SHAPE              # down rank above 128
+    assert call(nx_=nx - 16) == ARG                         # up images
+    assert call(nw_=nw + 16) == ARG
+    assert call(nd_=nd - 16) == ARG                         # down image
+    assert call(nd_=_xb(M=300, **dict(dn, rank=16))) == ARG
+    assert call(nws=ws - 4) == ARG                          # workspace too small
+    assert call(w=None) == ARG
+    assert call(ld=None) == ARG                             # down rank > 0 needs lora_down
+    assert call(lam=None) == ARG
+    assert call(di=MIS) == ARG
+    assert call(Y=MIS) == ARG
+    assert call(M=0) == SHAPE
+    d0 = dict(dn, rank=0)
+    assert f(_d(**up), 300, A, nx, A, nw, _d(**d0), A, A, A, _xb(M=300, **d0), None, None, None, 0,
+             None) == ARG                                   # lora_down with rank 0
+
+
 def test_qk_norm_rope_validation():
     f = _lib().svdq_qk_norm_rope
     ok = dict(M=64, H=24, ld=9216, Y=A, qs=A, ks=A, c=A, s=A, eps=1e-6)
