@@ -18,6 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsvdq.so")
+# measurement aid used only by the benchmark (not part of the layer's ABI)
+PROBE_LIB = os.path.join(HERE, "libsvdq_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["svdq_api.cpp", "quantize_act.hip", "pack_weight.hip", "images.hip", "gemm_int4.hip",
@@ -60,8 +63,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    pobjs = [_compile(src) for src in PROBE_SOURCES]
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *pobjs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {PROBE_LIB}", file=sys.stderr)
     return LIB
 
 

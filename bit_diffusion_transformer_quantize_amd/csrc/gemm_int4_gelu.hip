@@ -96,26 +96,11 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
   const int64_t row0 = (int64_t)tm * FG_BM;
   const int col0 = tn * FG_BN;
 
-  // ---- tile constants in LDS: GELU band, lambda reciprocals, L1 slice
-  for (int i = tid; i < gelu_table::kEntries / 2; i += FG_THREADS)
-    reinterpret_cast<uint32_t*>(gtab)[i] = reinterpret_cast<const uint32_t*>(kGeluBand.v)[i];
-  if (tid < FG_BN) rlam[tid] = 1.0 / (double)lambda_dn[col0 + tid];
-  if constexpr (RD4 > 0) {
-    // l1s[j][c] = lora_dn[j][col0 + c] for ranks j < rank_dn, 0 above
-    for (int i = tid; i < RD4 * 32 * (FG_BN / 8); i += FG_THREADS) {
-      const int j = i / (FG_BN / 8), c8 = i - j * (FG_BN / 8);
-      v4u v = {0u, 0u, 0u, 0u};
-      if (j < rank_dn) v = *reinterpret_cast<const v4u*>(lora_dn + (int64_t)j * N + col0 + 8 * c8);
-      *reinterpret_cast<v4u*>(l1s + j * FG_BN + 8 * c8) = v;
-    }
-  }
-
-  __syncthreads();  // the tables are in LDS
-
   // ---- the main product's stream: group g is one stage of a 4-slot DMA
   // ring: 16 KB of X codes (8 row blocks) then 8 KB of W codes (4 column
   // blocks), 24 chunks of 1 KB; wave w moves chunks w, w+8, w+16.  The first
-  // three stages are issued before the bias and low-rank loads.
+  // three stages are issued first, then every other load of the tile, so
+  // that their latencies overlap.
   const uint32_t voff = (uint32_t)(lane * 16);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_fg*)ring;
   const uint8_t* xg0 = ximg + (row0 / 32) * I4_BLOCK;
@@ -136,15 +121,44 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
   if (G > 1) dma_stage(1);
   if (G > 2) dma_stage(2);
 
-  // ---- the accumulator: bias, then T L2 (bf16 hi/lo of T)
-  v16f acc[2][2];
+  // bias of the wave's columns (in the accumulator's column order)
+  v2u bias_w[2][4];
   {
     const uint8_t* bias = wimg + w_bias + (int64_t)(col0 / 32 + wn * 2) * BIAS_BLOCK;
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bias_w[tc][q] = *reinterpret_cast<const v2u*>(bias + tc * BIAS_BLOCK + 2 * (8 * q + 4 * h));
+  }
+  // ---- tile constants in LDS: GELU band, lambda reciprocals, and the
+  // tile's slice of L1 in the lane order of the T MFMA's A operand: fragment
+  // (j4, cg) for ranks 32 j4 .. +31 and tile columns 8 cg .. +7 is 64 lanes
+  // x 8 bytes, lane l holding rank 32 j4 + l%32, columns 8 cg + 4 (l/32) .. +3
+  for (int i = tid; i < gelu_table::kEntries / 2; i += FG_THREADS)
+    reinterpret_cast<uint32_t*>(gtab)[i] = reinterpret_cast<const uint32_t*>(kGeluBand.v)[i];
+  if (tid < FG_BN) rlam[tid] = 1.0 / (double)lambda_dn[col0 + tid];
+  if constexpr (RD4 > 0) {
+    for (int i = tid; i < RD4 * (FG_BN / 8) * 64; i += FG_THREADS) {
+      const int fl = i & 63, frag = i >> 6;
+      const int j4 = frag / (FG_BN / 8), cg = frag - j4 * (FG_BN / 8);
+      const int j = 32 * j4 + (fl & 31);
+      v2u v = {0u, 0u};
+      if (j < rank_dn)
+        v = *reinterpret_cast<const v2u*>(lora_dn + (int64_t)j * N + col0 + 8 * cg + 4 * (fl >> 5));
+      *reinterpret_cast<v2u*>(l1s + 4 * i) = v;
+    }
+  }
+  __syncthreads();  // the tables are in LDS
+
+  // ---- the accumulator: bias, then T L2 (bf16 hi/lo of T)
+  v16f acc[2][2];
+  {
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const v2u w = *reinterpret_cast<const v2u*>(bias + tc * BIAS_BLOCK + 2 * (8 * q + 4 * h));
+        const v2u w = bias_w[tc][q];
         const float b4[4] = {bf16_to_f32(w[0] & 0xFFFFu), bf16_to_f32(w[0] >> 16),
                              bf16_to_f32(w[1] & 0xFFFFu), bf16_to_f32(w[1] >> 16)};
 #pragma unroll
@@ -187,47 +201,76 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
 #pragma unroll
   for (int i = 0; i < 16; ++i) zero[i] = 0.f;
 
-  for (int g = 0; g < G; ++g) {
-    const int ahead = G - 1 - g;  // stages issued after this one
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3));
+  // fragments: A (activation) rows t and B (weight) columns t of the wave,
+  // each with its bf16 scale operand; one set, each fragment reloaded for the
+  // next group right after its last use in the current one
+  v8i af[2], bf[2];
+  v4s_fg sa[2], sb[2];
+  auto load_a = [&](const uint8_t* sp, int t) {
+    const v4u x = *reinterpret_cast<const v4u*>(sp + fa + t * I4_BLOCK);
+    const v2u y = *reinterpret_cast<const v2u*>(sp + fa8 + t * I4_BLOCK);
+    af[t] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
+    sa[t] = *reinterpret_cast<const v4s_fg*>(sp + fsa + t * I4_BLOCK);
+  };
+  auto load_b = [&](const uint8_t* sp, int t) {
+    const v4u x = *reinterpret_cast<const v4u*>(sp + fb + t * I4_BLOCK);
+    const v2u y = *reinterpret_cast<const v2u*>(sp + fb8 + t * I4_BLOCK);
+    bf[t] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
+    sb[t] = *reinterpret_cast<const v4s_fg*>(sp + fsb + t * I4_BLOCK);
+  };
+  auto slot_ptr = [&](int g) { return ring + (g & (FG_NSLOT - 1)) * FG_SLOT; };
+  // wait until stage t has landed (this wave's part: the stages issued after
+  // it, at most two, may still be in flight; the wave's earlier fragment
+  // reads have returned), then every wave's part
+  auto wait_stage = [&](int t) {
+    const int after = min(2, G - 1 - t);
+    if (after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    asm volatile("s_barrier" ::: "memory");
-    if (g + 3 < G) dma_stage(g + 3);
-    const uint8_t* sp = ring + (g & (FG_NSLOT - 1)) * FG_SLOT;
-    v8i af[2], bf[2];
-    v4s_fg sa[2], sb[2];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  v16f p[2], sc[2];
+  auto mf = [&](int t) {  // the MFMAs of tile t = (t / 2, t % 2) into buffer t & 1
+    const int tr = t >> 1, tc = t & 1, bb = t & 1;
+    p[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[tc], af[tr], zero, FG_FP6, FG_FP6,
+                                                            0, FG_SCALE_BYTE, 0, FG_SCALE_BYTE);
+    sc[bb] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sb[tc], sa[tr], zero, 0, 0, 0);
+  };
+  auto fm = [&](int t) {
+    const int tr = t >> 1, tc = t & 1, bb = t & 1;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const v4u x = *reinterpret_cast<const v4u*>(sp + fa + t * I4_BLOCK);
-      const v2u y = *reinterpret_cast<const v2u*>(sp + fa8 + t * I4_BLOCK);
-      af[t] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
-      sa[t] = *reinterpret_cast<const v4s_fg*>(sp + fsa + t * I4_BLOCK);
-      const v4u xw = *reinterpret_cast<const v4u*>(sp + fb + t * I4_BLOCK);
-      const v2u yw = *reinterpret_cast<const v2u*>(sp + fb8 + t * I4_BLOCK);
-      bf[t] = v8i{(int)xw[0], (int)xw[1], (int)xw[2], (int)xw[3], (int)yw[0], (int)yw[1], 0, 0};
-      sb[t] = *reinterpret_cast<const v4s_fg*>(sp + fsb + t * I4_BLOCK);
-    }
-    // tile t = (t / 2, t % 2): MFMAs of tile t + 1 interleaved with the FMAs
-    // of tile t
-    v16f p[2], sc[2];
-    auto mf = [&](int t) {
-      const int tr = t >> 1, tc = t & 1, bb = t & 1;
-      p[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[tc], af[tr], zero, FG_FP6, FG_FP6,
-                                                              0, FG_SCALE_BYTE, 0, FG_SCALE_BYTE);
-      sc[bb] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sb[tc], sa[tr], zero, 0, 0, 0);
-    };
-    auto fm = [&](int t) {
-      const int tr = t >> 1, tc = t & 1, bb = t & 1;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[tr][tc][i] = fmaf(p[bb][i], sc[bb][i], acc[tr][tc][i]);
-    };
+    for (int i = 0; i < 16; ++i) acc[tr][tc][i] = fmaf(p[bb][i], sc[bb][i], acc[tr][tc][i]);
+  };
+
+  // The stream: stage 0's fragments are read before the loop; in group g the
+  // MFMAs of tiles 0 and 1 go first, then (g + 1 < G) the wait and barrier
+  // for stage g + 1 and the DMA of stage g + 4 into the slot of stage g, and
+  // each fragment of stage g + 1 is read as soon as its register is free.
+  wait_stage(0);
+  if (G > 3) dma_stage(3);
+  load_a(slot_ptr(0), 0);
+  load_a(slot_ptr(0), 1);
+  load_b(slot_ptr(0), 0);
+  load_b(slot_ptr(0), 1);
+  for (int g = 0; g < G; ++g) {
+    const bool more = g + 1 < G;
+    const uint8_t* nsp = slot_ptr(g + 1);
     mf(0);
     mf(1);
+    if (more) {
+      wait_stage(g + 1);
+      if (g + 4 < G) dma_stage(g + 4);
+      load_a(nsp, 0);  // row 0: last used by tile 1
+    }
     fm(0);
     mf(2);
+    if (more) load_b(nsp, 0);  // column 0: last used by tile 2
     fm(1);
     mf(3);
+    if (more) {
+      load_a(nsp, 1);
+      load_b(nsp, 1);
+    }
     fm(2);
     fm(3);
   }
@@ -289,10 +332,10 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
         for (int s4 = 0; s4 < 4; ++s4) {
           const v4s_fg xv = {(short)xb[tc][4 * s4], (short)xb[tc][4 * s4 + 1],
                              (short)xb[tc][4 * s4 + 2], (short)xb[tc][4 * s4 + 3]};
-          const int c = wn * 64 + tc * 32 + 8 * s4 + 4 * h;
 #pragma unroll
           for (int j4 = 0; j4 < RD4; ++j4) {
-            const v4s_fg lv = *reinterpret_cast<const v4s_fg*>(l1s + (32 * j4 + l32) * FG_BN + c);
+            const int cg = wn * 8 + tc * 4 + s4;
+            const v4s_fg lv = *reinterpret_cast<const v4s_fg*>(l1s + 4 * ((j4 * (FG_BN / 8) + cg) * 64 + lane));
             tacc[j4] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(lv, xv, tacc[j4], 0, 0, 0);
           }
         }
