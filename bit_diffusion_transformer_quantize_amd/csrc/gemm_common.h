@@ -1,5 +1,5 @@
 // Pieces shared by the W4A4 GEMM kernels: the 32x32 MFMA accumulator
-// layout, the low-rank up-projection epilogue and the output store.
+// layout, the bf16 split of T, the bias and the output store.
 #pragma once
 
 #include "common.h"
@@ -29,95 +29,6 @@ __device__ __forceinline__ void split_bf16x8(const v4f& a, const v4f& b, v8bf& h
     hi[2 * j + 1] = h[1];
     lo[2 * j] = l[0];
     lo[2 * j + 1] = l[1];
-  }
-}
-
-// acc[tr][tc] += T[rows] L2[cols] for a TR x TC block of 32x32 tiles whose
-// top-left output is (mbase, nbase); rows >= M and columns >= N contribute
-// nothing (their outputs are never stored).  T (fp32) is split into a bf16
-// high and low part, so the two bf16 MFMAs per 16-wide slice of the rank
-// keep the branch accurate to about 2^-16 of |T|.  Out-of-range rows and
-// columns read row 0 and are zeroed, so no load sits under a branch.
-// With DB the first two slices are fetched together and each buffer is
-// refilled as soon as it has been consumed; without it (for callers short
-// of registers) each slice is fetched right before it is used.
-template <int TR, int TC, bool DB = true>
-__device__ __forceinline__ void lowrank_up_tiles(v16f (&acc)[TR][TC], int rank, int64_t M,
-                                                 int N, int64_t mbase, int nbase, int lane,
-                                                 const float* __restrict__ T,
-                                                 const uint16_t* __restrict__ lora_up) {
-  const int koff = (lane >> 5) * 8;
-  const float* tp[TR];
-  bool tok[TR];
-#pragma unroll
-  for (int tr = 0; tr < TR; ++tr) {
-    const int64_t m = mbase + tr * 32 + (lane & 31);
-    tok[tr] = m < M;
-    tp[tr] = T + (tok[tr] ? m : 0) * rank + koff;
-  }
-  const uint16_t* lp[TC];
-  bool lok[TC];
-#pragma unroll
-  for (int tc = 0; tc < TC; ++tc) {
-    const int n = nbase + tc * 32 + (lane & 31);
-    lok[tc] = n < N;
-    lp[tc] = lora_up + (int64_t)(lok[tc] ? n : 0) * rank + koff;
-  }
-  v4f ta[DB ? 2 : 1][TR][2];
-  v8bf la[DB ? 2 : 1][TC];
-  auto fetch = [&](int buf, int rb) {
-    if constexpr (!DB) buf = 0;
-#pragma unroll
-    for (int tr = 0; tr < TR; ++tr) {
-      ta[buf][tr][0] = *reinterpret_cast<const v4f*>(tp[tr] + rb);
-      ta[buf][tr][1] = *reinterpret_cast<const v4f*>(tp[tr] + rb + 4);
-    }
-#pragma unroll
-    for (int tc = 0; tc < TC; ++tc) la[buf][tc] = *reinterpret_cast<const v8bf*>(lp[tc] + rb);
-  };
-  auto compute = [&](int buf) {
-    if constexpr (!DB) buf = 0;
-    v8bf thi[TR], tlo[TR], bv[TC];
-#pragma unroll
-    for (int tr = 0; tr < TR; ++tr) {
-      const v4f z = {0.f, 0.f, 0.f, 0.f};
-      split_bf16x8(tok[tr] ? ta[buf][tr][0] : z, tok[tr] ? ta[buf][tr][1] : z, thi[tr], tlo[tr]);
-    }
-#pragma unroll
-    for (int tc = 0; tc < TC; ++tc) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        bv[tc][i] = lok[tc] ? la[buf][tc][i] : __builtin_bit_cast(__bf16, (uint16_t)0);
-    }
-#pragma unroll
-    for (int tr = 0; tr < TR; ++tr)
-#pragma unroll
-      for (int tc = 0; tc < TC; ++tc)
-        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(thi[tr], bv[tc], acc[tr][tc], 0, 0, 0);
-#pragma unroll
-    for (int tr = 0; tr < TR; ++tr)
-#pragma unroll
-      for (int tc = 0; tc < TC; ++tc)
-        acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tlo[tr], bv[tc], acc[tr][tc], 0, 0, 0);
-  };
-  // slices rb (buffer 0) and rb + 16 (buffer 1) per iteration; each
-  // buffer's next slice is fetched as soon as it has been consumed
-  if constexpr (DB) {
-    fetch(0, 0);
-    if (16 < rank) fetch(1, 16);
-    for (int rb = 0; rb < rank; rb += 32) {
-      compute(0);
-      if (rb + 32 < rank) fetch(0, rb + 32);
-      if (rb + 16 < rank) {
-        compute(1);
-        if (rb + 48 < rank) fetch(1, rb + 48);
-      }
-    }
-  } else {
-    for (int rb = 0; rb < rank; rb += 16) {
-      fetch(0, rb);
-      compute(0);
-    }
   }
 }
 
@@ -221,61 +132,6 @@ __device__ __forceinline__ void init_bias_t(v16f (&acc)[TR][TC], const uint8_t* 
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[tr][tc][4 * q + e] = b[e];
     }
-}
-
-// Y[rows, cols] (=|+=) acc + bias for one output type; rows >= M and
-// columns >= N are skipped.  Each (tile row, tile column) keeps one row
-// pointer; the 16 rows of a lane are scalar multiples of N away from it.
-template <int TR, int TC, bool ACCUM, typename OutT>
-__device__ __forceinline__ void store_tiles_as(const v16f (&acc)[TR][TC], int64_t M, int N,
-                                               int64_t mbase, int nbase, int lane,
-                                               const uint16_t* __restrict__ bias,
-                                               OutT* __restrict__ Y) {
-  const int64_t m_lane = mbase + 4 * (lane >> 5);
-  auto put = [&](OutT* y, float v) {
-    if constexpr (sizeof(OutT) == 4) {
-      *y = ACCUM ? *y + v : v;
-    } else {
-      if (ACCUM) v += bf16_to_f32(*y);
-      *y = (uint16_t)f32_to_bf16(v);
-    }
-  };
-#pragma unroll
-  for (int tc = 0; tc < TC; ++tc) {
-    const int n = nbase + tc * 32 + (lane & 31);
-    const bool cols_full = nbase + tc * 32 + 32 <= N;  // wave-uniform
-    if (!cols_full && n >= N) continue;
-    const float b = bias ? bf16_to_f32(bias[n]) : 0.f;
-#pragma unroll
-    for (int tr = 0; tr < TR; ++tr) {
-      const int64_t m_tile = m_lane + tr * 32;
-      OutT* yrow = Y + m_tile * N + n;
-      if (cols_full && mbase + tr * 32 + 32 <= M) {  // whole tile inside: no per-element test
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          put(yrow + (int64_t)(8 * (i >> 2) + (i & 3)) * N, acc[tr][tc][i] + b);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + (i & 3);
-          if (m_tile + r < M) put(yrow + (int64_t)r * N, acc[tr][tc][i] + b);
-        }
-      }
-    }
-  }
-}
-
-// Y[rows, cols] (=|+=) acc + bias, bf16 (RNE) or fp32.
-template <int TR, int TC, bool ACCUM>
-__device__ __forceinline__ void store_tiles(const v16f (&acc)[TR][TC], int64_t M, int N,
-                                            int64_t mbase, int nbase, int lane,
-                                            const uint16_t* __restrict__ bias, bool out_f32,
-                                            void* __restrict__ Y) {
-  if (out_f32)
-    store_tiles_as<TR, TC, ACCUM>(acc, M, N, mbase, nbase, lane, bias, reinterpret_cast<float*>(Y));
-  else
-    store_tiles_as<TR, TC, ACCUM>(acc, M, N, mbase, nbase, lane, bias,
-                                  reinterpret_cast<uint16_t*>(Y));
 }
 
 }  // namespace svdq

@@ -105,6 +105,9 @@ __device__ __forceinline__ int tiles_of4(int b, int nwg, int ntiles) {
   return b < ntiles ? (ntiles - b + nwg - 1) / nwg : 0;
 }
 
+// LR: the layer has a low-rank branch (rank > 0); the two forms are
+// separate kernels so that traces tell the rank-0 launches apart.
+template <bool LR>
 __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
     int64_t M, int N, int K, int rank, int out_f32, const uint8_t* __restrict__ ximg,
     int64_t x_rt, int64_t x_sc, int64_t x_lr, const uint8_t* __restrict__ wimg, int64_t w_ct,
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   const int my_tiles = tiles_of4(b, nwg, ntiles);
   if (my_tiles == 0) return;  // uniform per workgroup: no barrier is reached
   const int S = K >> 7;       // code stages per tile (G/2; K % 128 == 0)
-  const int R16 = rank >> 4;
+  const int R16 = LR ? rank >> 4 : 0;
   // pre-stages per tile: the bias rides in the first, one 16-rank slice of
   // the low-rank branch in each of the first R16; at least two, so that the
   // first two code stages of a tile are among the positions issued ahead
@@ -381,7 +384,13 @@ hipError_t launch_fp4_forward(bool out_f32, int64_t M, int N, int K, int rank,
   const WeightImage w = weight_image(1, N, K, rank);
   const int64_t tiles = (a.RT / (F4_BM / 32)) * (w.CT / (F4_BN / 32));
   const int64_t grid = std::min<int64_t>(tiles, device_cus());
-  hipLaunchKernelGGL(fp4_gemm_kernel, dim3((unsigned)grid), dim3(F4_THREADS), 0, s, M, N, K, rank,
+  if (rank > 0)
+    hipLaunchKernelGGL(fp4_gemm_kernel<true>, dim3((unsigned)grid), dim3(F4_THREADS), 0, s, M, N, K, rank,
+                     (int)out_f32, reinterpret_cast<const uint8_t*>(ximage), a.RT, (int64_t)a.scale,
+                     (int64_t)a.lr, reinterpret_cast<const uint8_t*>(wimage), w.CT,
+                     (int64_t)w.scale, (int64_t)w.lr, (int64_t)w.bias, Y);
+  else
+    hipLaunchKernelGGL(fp4_gemm_kernel<false>, dim3((unsigned)grid), dim3(F4_THREADS), 0, s, M, N, K, rank,
                      (int)out_f32, reinterpret_cast<const uint8_t*>(ximage), a.RT, (int64_t)a.scale,
                      (int64_t)a.lr, reinterpret_cast<const uint8_t*>(wimage), w.CT,
                      (int64_t)w.scale, (int64_t)w.lr, (int64_t)w.bias, Y);
