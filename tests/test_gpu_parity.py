@@ -70,6 +70,21 @@ def test_ranks(mode, rank):
     _full_check(WL.TINY, mode, M=96, rank=rank, seed=rank)
 
 
+# short K (few code stages per tile) with more output tiles than workgroups,
+# so that workgroups walk several tiles and the DMA stream crosses tile
+# boundaries from the pre-stages and the first code groups; 300 tiles take
+# the round-robin tile order, 320 the per-XCD one
+SHORT_K = [("int4", 128, 16, 11520), ("int4", 256, 128, 12288), ("int4", 384, 0, 11520),
+           ("fp4", 128, 16, 16384), ("fp4", 256, 128, 13312), ("fp4", 384, 0, 16384)]
+
+
+@pytest.mark.parametrize("mode,K,rank,N", SHORT_K)
+def test_short_k_many_tiles(mode, K, rank, N):
+    spec = WL.LinearSpec(f"shortk_1100x{K}x{N}", 1100, K, N, rank, mode, x_outliers=4,
+                         x_factor=20.0)
+    _full_check(spec, mode, seed=K + rank, use_lowrank=rank > 0)
+
+
 @pytest.mark.parametrize("mode", ["int4", "fp4"])
 def test_no_lowrank_no_bias(mode):
     _full_check(WL.TINY, mode, M=64, use_lowrank=False, with_bias=False)
