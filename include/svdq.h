@@ -288,7 +288,10 @@ svdq_status svdq_pack_weight(const svdq_desc* desc, const uint16_t* W, const flo
  *     bytes 768 h + 16 r .. +15 and 768 h + 512 + 8 r .. +7 hold, as one
  *     little-endian 192-bit string, the 32 codes q of row r and K half h,
  *     element i in bits 6 i .. 6 i + 5 as the sign-magnitude field
- *     (q < 0 ? 0x20 : 0) | |q| (the E2M3 encoding of q / 8);
+ *     (q < 0 ? 0x20 : 0) | |q| (the E2M3 encoding of q / 8); in the
+ *     activation image a code 0 may also appear as 0x20 (-0: the encoder
+ *     keeps the sign of a value that rounds to zero), which adds nothing
+ *     to the product either;
  *     bytes 1536 + 8 s .. +7: the scale of row s % 32 and group g as two
  *     bf16 halves hi = bf16_RNE(s), lo = bf16_RNE(s - hi):
  *       activation image: slot s < 32: {hi | lo << 16, hi}, s >= 32: {lo, 0};
