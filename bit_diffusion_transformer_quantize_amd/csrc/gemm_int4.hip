@@ -161,10 +161,12 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   const int G = K >> 6;
   const int R16 = LR ? rank >> 4 : 0;
   // pre-stages per tile: the bias rides in the first, one 16-rank slice of
-  // the low-rank branch in each of the first R16; at least four, so that
-  // the first four positions of every tile (whose waits differ) are all
-  // pre-stages and every code stage waits the same way
-  const int P = R16 > 4 ? R16 : 4;
+  // the low-rank branch in each of the first R16 (at least one).  A pre
+  // stage has next to no work, so each one past what the branch needs
+  // would only wait on the DMA stream at the head of the tile; the code
+  // stages among a tile's first four positions wait with the counts of
+  // those positions instead.
+  const int P = R16 > 1 ? R16 : 1;
   const int SPT = P + G;            // stages per tile
   const int total = my_tiles * SPT;
 
@@ -239,7 +241,8 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   // stores of the previous tile, issued behind them (before the first tile,
   // I4_NST dummy DMAs into the pad stand in for them).
   auto wait_stage = [] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); };
-  auto wait_head2 = [] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + I4_NST)); };  // j = 2, 3
+  // positions 2 and 3 (pre or code stages): one stage and the stores are younger
+  auto wait_head2 = [] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + I4_NST)); };
   auto wait_at = [&](int j) {
     if (j == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12 + I4_NST));
     else if (j == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + I4_NST));
@@ -325,7 +328,8 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     step(1, 0, [] {});
     step(2, 1, [&] {  // A tile row 0 is free
       if constexpr (NEXT) {
-        wait_stage();
+        if (P + g + 1 < 4) wait_head2();  // the next position is the tile's third or fourth
+        else wait_stage();
         barrier();
         if (g + 3 < G) dma_code(q + 3);
         else dma_stage(q + 3);
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     for (int jp = 0; jp < P; ++jp, ++q) {
       wait_at(jp);
       barrier();
-      if (jp >= 2) dma_stage(q + 2);
+      if (jp >= 2) dma_stage(q + 2);  // positions 2, 3 were issued at the previous tile's end
       const uint8_t* sp = slot_ptr(q);
       if (jp == 0) init_bias_t<2, 3>(acc, sp + pbias, lane);
       if (jp < R16) {
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     // the first code group: all its fragments, then its first tile's MFMAs
     wait_at(P);
     barrier();
-    dma_stage(q + 2);
+    if (P >= 2) dma_stage(q + 2);  // with P = 1, position 3 is already in flight
     {
       const uint8_t* sp = slot_ptr(q);
       load_a(sp, 0);
