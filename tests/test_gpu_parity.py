@@ -254,3 +254,34 @@ def test_split_k_quantize(mode):
     spec = WL.LinearSpec("split_300x6144x256_r32", 300, 6144, 256, 32, mode,
                          x_outliers=6, x_factor=50.0)
     _full_check(spec, mode, seed=3)
+
+
+@pytest.mark.parametrize("mode", ["int4", "fp4"])
+def test_rows_past_2_31_elements(mode):
+    """X of 2^22 + 77 rows x 512 (more than 2^31 elements, so row offsets
+    need 64 bits): rows at the start, past the 2^31-element mark and at the
+    ragged end equal, bit for bit, the same rows run as a separate 300-row
+    layer (every output depends on its own row of X only, and both calls add
+    in the same order).  Inputs drawn on the GPU; no oracle at this size."""
+    from bit_diffusion_transformer_quantize_amd import svdq as S
+    S.load()
+    M, K, N, r = (1 << 22) + 77, 512, 256, 16
+    _say("rows past 2^31 elements", mode, M, K, N, r)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    X = torch.randn(M, K, generator=g, device=DEV).to(torch.bfloat16)
+    W = (0.02 * torch.randn(N, K, generator=g, device=DEV)).to(torch.bfloat16)
+    b = (0.01 * torch.randn(N, generator=g, device=DEV)).to(torch.bfloat16)
+    lam = S.svdq_calibrate_lambda(X[:4096], W)
+    ld, lu, _ = S.svdq_lowrank_factors(W, lam, r, seed=0, want_sigma=False)
+    d = S.desc(mode, K, N, r)
+    wc, ws = S.svdq_pack_weight(d, W, lam, ld, lu)
+    wi = S.svdq_prepare_weight(d, wc, ws, lu, b)
+    xi = S.svdq_quantize_act(d, X, lam, ld)[3]
+    Y = S.svdq_linear_forward(d, M, xi, wi)
+    for m0 in (0, (1 << 22) - 250, M - 300):
+        xs = S.svdq_quantize_act(d, X[m0:m0 + 300].contiguous(), lam, ld)[3]
+        ys = S.svdq_linear_forward(d, 300, xs, wi)
+        torch.cuda.synchronize()
+        assert torch.equal(Y[m0:m0 + 300], ys), f"rows {m0}..{m0 + 299}"
+    del X, Y, xi
+    torch.cuda.empty_cache()
