@@ -4,13 +4,14 @@
 // The Nunchaku engine fuses the down-projection of the low-rank branch into
 // the quantization kernel so that both branches share one read of the
 // activations (apatero.com page, section "O que e Nunchaku e como acelera
-// modelos Qwen").  Here a workgroup owns 16 rows of X; its eight waves take
-// 64-column tiles round-robin, each prefetching its next tile.  In a tile,
+// modelos Qwen").  Here a workgroup owns 16 rows of X; its waves (16 for
+// INT4, 8 for FP4) take 64-column tiles round-robin, each prefetching its
+// next tile.  In a tile,
 // lane l holds row l%16 and the 16 columns 16*(l/16) .. +15, which is also
 // the A-operand layout of two v_mfma_f32_16x16x32_bf16, so the smoothed
 // bf16 values feed the MFMA straight from registers.  Per-group absmax is a
-// xor-shuffle over the lanes that share a row.  The T partials of the eight
-// waves are summed through LDS at the end.
+// xor-shuffle over the lanes that share a row.  The waves' T partials are
+// summed through LDS at the end.
 //
 // Exact quotients without a division per element.  Both quotients of the
 // contract, fp32(x / lambda) and fp32(x_hat / s), divide a bf16 value
@@ -58,12 +59,15 @@ struct QaShape {
 // then fall into different banks.
 __device__ __forceinline__ int rl_idx(int c) { return c + ((c >> 4) << 1); }
 
-// LDS: the reciprocal table during the main loop, the T partials afterwards.
+// LDS: during the main loop the reciprocal table and, with a down-projection,
+// a 2 KB staging buffer per wave (one 16-rank slice of a lora_down tile);
+// the T partials afterwards.
 template <int MODE, int RB>
 struct QaLds {
   static constexpr int kRcp = (QA_KCHUNK + QA_KCHUNK / 8) * 8;
+  static constexpr int kStage = RB > 0 ? QaShape<MODE, RB>::kWaves * 2048 : 0;
   static constexpr int kRed = QaShape<MODE, RB>::kWaves * (RB > 0 ? RB : 1) * 4 * 64 * 4;
-  static constexpr int kBytes = kRcp > kRed ? kRcp : kRed;
+  static constexpr int kBytes = kRcp + kStage > kRed ? kRcp + kStage : kRed;
 };
 
 // 16 INT4 codes as 16 E2M3 fields of 6 bits (sign-magnitude, value q/8)
@@ -111,6 +115,9 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
     void* __restrict__ xscales, float* __restrict__ T, QaImage qi) {
   constexpr int QA_WAVES = QaShape<MODE, RB>::kWaves;
   constexpr int QA_THREADS = QaShape<MODE, RB>::kThreads;
+  static_assert(QA_KCHUNK % QA_THREADS == 0, "whole table entries per thread");
+  // lora_down slices loaded at the top of a tile (the rest when used)
+  constexpr int QA_EARLY = QA_WAVES == 16 ? (RB <= 2 ? RB : 0) : (RB < 4 ? RB : 4);
   __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<MODE, RB>::kBytes];
   double* rlam = reinterpret_cast<double*>(smem);
   // the GELU band table (7.5 KB), copied once; the first chunk's barrier
@@ -140,9 +147,6 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
 
   for (int kc = kbeg; kc < kend; kc += QA_KCHUNK) {
     const int kn = min(QA_KCHUNK, kend - kc);
-    __syncthreads();  // the previous chunk is done with the table
-    for (int c = threadIdx.x; c < kn; c += QA_THREADS) rlam[rl_idx(c)] = 1.0 / (double)lambda[kc + c];
-    __syncthreads();
     const int ntiles = kn >> 6;
     // Loads of a tile without a branch (rows past M and tiles past the chunk
     // read a valid place; the flag zeroes them when the tile is used), so
@@ -154,13 +158,46 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       xa = *reinterpret_cast<const v4u*>(p);
       xb = *reinterpret_cast<const v4u*>(p + 8);
     };
+    // The first tile's X and this thread's entries of lambda are requested
+    // together, ahead of the table, so that one memory latency covers both.
     v4u na, nb;
     bool nok;
     load_x(wave, na, nb, nok);
+    constexpr int RPT = QA_KCHUNK / QA_THREADS;  // table entries per thread
+    float lv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = threadIdx.x + i * QA_THREADS;
+      lv[i] = lambda[kc + (c < kn ? c : 0)];
+    }
+    __syncthreads();  // the previous chunk is done with the table
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = threadIdx.x + i * QA_THREADS;
+      if (c < kn) rlam[rl_idx(c)] = 1.0 / (double)lv[i];
+    }
+    __syncthreads();
     for (int t = wave; t < ntiles; t += QA_WAVES) {
       const v4u zero4 = v4u{0u, 0u, 0u, 0u};
       const v4u xa = nok ? na : zero4, xb = nok ? nb : zero4;
       uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+      // This tile's lora_down columns, read as whole 128-byte row segments:
+      // load h of slice b gives lane L row b*16 + 8h + L/8 and its 16-byte
+      // chunk L%8, so each load covers 8 cache lines in full.  (In the MFMA
+      // operand order a load would touch 16 lines, half of each, and such
+      // loads measured several times slower.)
+      // The first QA_EARLY slices are requested here, ahead of the tile's
+      // work, the others (large ranks, for want of registers) when used.
+      const uint16_t* l1t = lora_down + (int64_t)(lane >> 3) * K + kc + t * 64 + (lane & 7) * 8;
+      auto load_l1 = [&](int b, int h) {
+        return *reinterpret_cast<const v4u*>(l1t + (int64_t)(b * 16 + 8 * h) * K);
+      };
+      v4u lg[QA_EARLY > 0 ? QA_EARLY : 1][2];
+#pragma unroll
+      for (int b = 0; b < QA_EARLY; ++b) {
+        lg[b][0] = load_l1(b, 0);
+        lg[b][1] = load_l1(b, 1);
+      }
       load_x(t + QA_WAVES, na, nb, nok);  // next tile of this wave
       if constexpr (GELU) {
 #pragma unroll
@@ -170,7 +207,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       const int k0 = kc + kl;          // column within the row
 
       // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
-      uint32_t hb[16];
+      uint32_t hpk[8];  // X_hat as packed bf16 pairs (the T MFMA's A operand)
       float xh[16];
       float amax = 0.f;
 #pragma unroll
@@ -185,8 +222,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         // bit-level definition for every finite value)
         const v2f qv = {q[0], q[1]};
         const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(qv, v2bf));
-        hb[i] = pk & 0xFFFFu;
-        hb[i + 1] = pk >> 16;
+        hpk[i >> 1] = pk;
         xh[i] = __uint_as_float(pk << 16);
         xh[i + 1] = __uint_as_float(pk & 0xFFFF0000u);
         amax = fmaxf(amax, fmaxf(fabsf(xh[i]), fabsf(xh[i + 1])));
@@ -308,17 +344,29 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         // T += X_hat[16 rows, 64 cols] . L1[64 cols, 16*RB]: element i of
         // this lane is column k0 + i; the B operand takes the same columns of
         // lora_down (= L1^T) rows.
-        v8bf a0, a1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          a0[i] = __builtin_bit_cast(__bf16, (uint16_t)hb[i]);
-          a1[i] = __builtin_bit_cast(__bf16, (uint16_t)hb[8 + i]);
-        }
+        const v8bf a0 = __builtin_bit_cast(v8bf, v4u{hpk[0], hpk[1], hpk[2], hpk[3]});
+        const v8bf a1 = __builtin_bit_cast(v8bf, v4u{hpk[4], hpk[5], hpk[6], hpk[7]});
+        // Each slice goes through this wave's staging buffer, 16 rows of 128
+        // bytes whose 16-byte chunk c of row n sits at position c ^ (n % 8),
+        // so that both the row-segment writes and the operand reads (lane l:
+        // row l%16, chunks 2(l/16) and 2(l/16) + 1, the columns of a0 and a1)
+        // meet every bank once per eight lanes.  The wave's LDS operations run
+        // in order, so a slice's writes follow the previous slice's reads
+        // without a wait.
+        uint8_t* stg = smem + QaLds<MODE, RB>::kRcp + wave * 2048;
+        const int wr = lane >> 3, wc = lane & 7;
+        const int rd0 = r16 * 128 + (((2 * j) ^ (r16 & 7)) << 4);
+        const int rd1 = r16 * 128 + (((2 * j + 1) ^ (r16 & 7)) << 4);
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          const uint16_t* ld = lora_down + (int64_t)(b * 16 + r16) * K + k0;
-          const v8bf b0 = *reinterpret_cast<const v8bf*>(ld);
-          const v8bf b1 = *reinterpret_cast<const v8bf*>(ld + 8);
+          const v4u g0 = b < QA_EARLY ? lg[b < QA_EARLY ? b : 0][0] : load_l1(b, 0);
+          const v4u g1 = b < QA_EARLY ? lg[b < QA_EARLY ? b : 0][1] : load_l1(b, 1);
+          *reinterpret_cast<v4u*>(stg + wr * 128 + ((wc ^ wr) << 4)) = g0;
+          *reinterpret_cast<v4u*>(stg + (8 + wr) * 128 + ((wc ^ wr) << 4)) = g1;
+          __builtin_amdgcn_wave_barrier();
+          const v8bf b0 = *reinterpret_cast<const v8bf*>(stg + rd0);
+          const v8bf b1 = *reinterpret_cast<const v8bf*>(stg + rd1);
+          __builtin_amdgcn_wave_barrier();
           tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, tacc[b], 0, 0, 0);
           tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, tacc[b], 0, 0, 0);
         }
@@ -327,7 +375,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   }
 
   if constexpr (RB > 0) {
-    // Sum the eight waves' partial T tiles through LDS (in a fixed order).
+    // Sum the waves' partial T tiles through LDS, wave 0 first.
     __syncthreads();  // the table is no longer read
     float(*red)[RB][4][64] = reinterpret_cast<float(*)[RB][4][64]>(smem);
 #pragma unroll
@@ -335,9 +383,24 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
 #pragma unroll
       for (int q = 0; q < 4; ++q) red[wave][b][q][lane] = tacc[b][q];
     __syncthreads();
-    // One thread per (row, 8 consecutive ranks): the 8 partial sums of a
-    // row and rank chunk are 8 consecutive lanes of one MFMA output register
-    // (lane l, element q -> row 4 (l/16) + q, column l%16).
+    // Four consecutive entries of the wave-0 tile per thread take the sum
+    // over the waves in place (each entry is read and written by its own
+    // thread alone), all loads in flight at once.
+    for (int f = 4 * threadIdx.x; f < RB * 256; f += 4 * QA_THREADS) {
+      v4f part[QA_WAVES];
+#pragma unroll
+      for (int w = 0; w < QA_WAVES; ++w) part[w] = *reinterpret_cast<const v4f*>(&red[w][0][0][0] + f);
+      v4f acc = part[0];
+#pragma unroll
+      for (int w = 1; w < QA_WAVES; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += part[w][i];
+      *reinterpret_cast<v4f*>(&red[0][0][0][0] + f) = acc;
+    }
+    __syncthreads();
+    // One thread per (row, 8 consecutive ranks): the 8 sums of a row and
+    // rank chunk are 8 consecutive lanes of one MFMA output register (lane
+    // l, element q -> row 4 (l/16) + q, column l%16).
     const int rank = RB * 16;
     for (int idx = threadIdx.x; idx < QA_ROWS * (rank / 8); idx += QA_THREADS) {
       const int mr = idx / (rank / 8);
@@ -346,10 +409,6 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = red[0][b][q][l0 + i];
-#pragma unroll
-      for (int w = 1; w < QA_WAVES; ++w)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] += red[w][b][q][l0 + i];
       const int64_t m = (int64_t)blockIdx.x * QA_ROWS + mr;
       if (S > 1) {
         // partial sums of K range blockIdx.y, added by split_t_kernel
