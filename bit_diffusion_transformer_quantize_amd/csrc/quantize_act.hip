@@ -23,9 +23,10 @@
 // correctly rounded fp32(a / b), provided fp64(1/b) is the correctly rounded
 // reciprocal (tests/test_exact_quotient.py checks this on the CPU for every
 // finite bf16 a against thousands of divisors: subnormals, all-ones
-// significands, INT4 scales, NVFP4 s g values).  The fp64 reciprocals of
-// lambda are computed once per workgroup into LDS, the one of s once per
-// lane and group.
+// significands, INT4 scales, NVFP4 s g values).  Each wave computes the fp64
+// reciprocals of its tile's 64 lambdas into its own LDS slot (one per lane),
+// so the waves need no barrier before the T partials are summed; the
+// reciprocal of s is computed once per lane and group.
 //
 // Outputs: the codes, scales and T in the documented row-major layouts
 // (each optional) and/or the activation operand image the GEMM reads
@@ -43,7 +44,7 @@
 namespace svdq {
 
 constexpr int QA_ROWS = 16;
-constexpr int QA_KCHUNK = 4096;  // columns whose reciprocals of lambda sit in LDS at once
+constexpr int QA_RCP = 72;  // fp64 slots of a wave's reciprocals of lambda (64 + padding)
 
 // Waves per 16-row workgroup: INT4 16 (four per SIMD, to keep more of X in
 // flight) unless the T partials of a large rank would not fit in LDS; FP4 8
@@ -54,17 +55,17 @@ struct QaShape {
   static constexpr int kThreads = 64 * kWaves;
 };
 
-// The fp64 reciprocals of lambda sit in LDS with 16 bytes of padding after
-// every 16 entries: the four lanes of a row read entries 16 apart, which
-// then fall into different banks.
+// The fp64 reciprocals of a tile's 64 lambdas sit in LDS with 16 bytes of
+// padding after every 16 entries: the four lanes of a row read entries 16
+// apart, which then fall into different banks.
 __device__ __forceinline__ int rl_idx(int c) { return c + ((c >> 4) << 1); }
 
-// LDS: during the main loop the reciprocal table and, with a down-projection,
-// a 2 KB staging buffer per wave (one 16-rank slice of a lora_down tile);
-// the T partials afterwards.
+// LDS: during the main loop, per wave, the reciprocals of its tile's lambdas
+// and, with a down-projection, a 2 KB staging buffer (one 16-rank slice of a
+// lora_down tile); the T partials afterwards.
 template <int MODE, int RB>
 struct QaLds {
-  static constexpr int kRcp = (QA_KCHUNK + QA_KCHUNK / 8) * 8;
+  static constexpr int kRcp = QaShape<MODE, RB>::kWaves * QA_RCP * 8;
   static constexpr int kStage = RB > 0 ? QaShape<MODE, RB>::kWaves * 2048 : 0;
   static constexpr int kRed = QaShape<MODE, RB>::kWaves * (RB > 0 ? RB : 1) * 4 * 64 * 4;
   static constexpr int kBytes = kRcp + kStage > kRed ? kRcp + kStage : kRed;
@@ -115,20 +116,19 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
     void* __restrict__ xscales, float* __restrict__ T, QaImage qi) {
   constexpr int QA_WAVES = QaShape<MODE, RB>::kWaves;
   constexpr int QA_THREADS = QaShape<MODE, RB>::kThreads;
-  static_assert(QA_KCHUNK % QA_THREADS == 0, "whole table entries per thread");
   // lora_down slices loaded at the top of a tile (the rest when used)
   constexpr int QA_EARLY = QA_WAVES == 16 ? (RB <= 2 ? RB : 0) : (RB < 4 ? RB : 4);
   __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<MODE, RB>::kBytes];
-  double* rlam = reinterpret_cast<double*>(smem);
-  // the GELU band table (7.5 KB), copied once; the first chunk's barrier
-  // orders the copy before any lookup
+  // the GELU band table (7.5 KB), copied once before any lookup
   __shared__ uint16_t gtab[GELU ? gelu_table::kEntries : 2];
   if constexpr (GELU) {
     for (int i = threadIdx.x; i < gelu_table::kEntries / 2; i += QA_THREADS)
       reinterpret_cast<uint32_t*>(gtab)[i] = reinterpret_cast<const uint32_t*>(kGeluBand.v)[i];
+    __syncthreads();
   }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  double* rlam = reinterpret_cast<double*>(smem) + wave * QA_RCP;
   const int r16 = lane & 15;
   const int j = lane >> 4;
   const int64_t row = (int64_t)blockIdx.x * QA_ROWS + r16;
@@ -145,39 +145,31 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
 #pragma unroll
   for (int b = 0; b < (RB > 0 ? RB : 1); ++b) tacc[b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = kbeg; kc < kend; kc += QA_KCHUNK) {
-    const int kn = min(QA_KCHUNK, kend - kc);
-    const int ntiles = kn >> 6;
-    // Loads of a tile without a branch (rows past M and tiles past the chunk
+  // The waves run independently until the T partials are summed: each takes
+  // its tiles of this workgroup's K range round-robin, prefetching the next
+  // one's X and lambdas, and makes its tile's reciprocals of lambda itself
+  // (one per lane) in its own LDS slot.
+  const int ntiles = (kend - kbeg) >> 6;
+  {
+    // Loads of a tile without a branch (rows past M and tiles past the range
     // read a valid place; the flag zeroes them when the tile is used), so
     // that the compiler's wait counts stay exact across the loop.
     auto load_x = [&](int t, v4u& xa, v4u& xb, bool& ok) {
       ok = row_ok && t < ntiles;
       const int tc = t < ntiles ? t : ntiles - 1;
-      const uint16_t* p = xrow + kc + tc * 64 + j * 16;
+      const uint16_t* p = xrow + kbeg + tc * 64 + j * 16;
       xa = *reinterpret_cast<const v4u*>(p);
       xb = *reinterpret_cast<const v4u*>(p + 8);
     };
-    // The first tile's X and this thread's entries of lambda are requested
-    // together, ahead of the table, so that one memory latency covers both.
+    auto load_lam = [&](int t) { return lambda[kbeg + (t < ntiles ? t : ntiles - 1) * 64 + lane]; };
     v4u na, nb;
     bool nok;
     load_x(wave, na, nb, nok);
-    constexpr int RPT = QA_KCHUNK / QA_THREADS;  // table entries per thread
-    float lv[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int c = threadIdx.x + i * QA_THREADS;
-      lv[i] = lambda[kc + (c < kn ? c : 0)];
-    }
-    __syncthreads();  // the previous chunk is done with the table
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int c = threadIdx.x + i * QA_THREADS;
-      if (c < kn) rlam[rl_idx(c)] = 1.0 / (double)lv[i];
-    }
-    __syncthreads();
+    float nlam = load_lam(wave);
     for (int t = wave; t < ntiles; t += QA_WAVES) {
+      // this tile's reciprocals of lambda: column t*64 + lane of the range
+      rlam[rl_idx(lane)] = 1.0 / (double)nlam;
+      __builtin_amdgcn_wave_barrier();
       const v4u zero4 = v4u{0u, 0u, 0u, 0u};
       const v4u xa = nok ? na : zero4, xb = nok ? nb : zero4;
       uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
@@ -188,7 +180,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       // loads measured several times slower.)
       // The first QA_EARLY slices are requested here, ahead of the tile's
       // work, the others (large ranks, for want of registers) when used.
-      const uint16_t* l1t = lora_down + (int64_t)(lane >> 3) * K + kc + t * 64 + (lane & 7) * 8;
+      const uint16_t* l1t = lora_down + (int64_t)(lane >> 3) * K + kbeg + t * 64 + (lane & 7) * 8;
       auto load_l1 = [&](int b, int h) {
         return *reinterpret_cast<const v4u*>(l1t + (int64_t)(b * 16 + 8 * h) * K);
       };
@@ -199,12 +191,13 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         lg[b][1] = load_l1(b, 1);
       }
       load_x(t + QA_WAVES, na, nb, nok);  // next tile of this wave
+      nlam = load_lam(t + QA_WAVES);
       if constexpr (GELU) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) xw[i] = gelu_bf16x2(xw[i], gtab);
       }
-      const int kl = t * 64 + j * 16;  // column within the chunk
-      const int k0 = kc + kl;          // column within the row
+      const int kl = j * 16;                // column within the tile
+      const int k0 = kbeg + t * 64 + kl;  // column within the row
 
       // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
       uint32_t hpk[8];  // X_hat as packed bf16 pairs (the T MFMA's A operand)
@@ -376,7 +369,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
 
   if constexpr (RB > 0) {
     // Sum the waves' partial T tiles through LDS, wave 0 first.
-    __syncthreads();  // the table is no longer read
+    __syncthreads();  // every wave is done with its LDS slots
     float(*red)[RB][4][64] = reinterpret_cast<float(*)[RB][4][64]>(smem);
 #pragma unroll
     for (int b = 0; b < RB; ++b)
