@@ -43,6 +43,8 @@
 
 namespace svdq {
 
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
 constexpr int QA_ROWS = 16;
 constexpr int QA_RCP = 72;  // fp64 slots of a wave's reciprocals of lambda (64 + padding)
 
@@ -133,6 +135,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   const int j = lane >> 4;
   const int64_t row = (int64_t)blockIdx.x * QA_ROWS + r16;
   const bool row_ok = row < M;
+  const bool block_full = (int64_t)blockIdx.x * QA_ROWS + QA_ROWS <= M;
   const int64_t irt = row >> 5;     // image row tile and lane slot of this row
   const int irr = (int)(row & 31);
   const uint16_t* xrow = X + (row_ok ? row : 0) * (int64_t)K;
@@ -170,8 +173,12 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       // this tile's reciprocals of lambda: column t*64 + lane of the range
       rlam[rl_idx(lane)] = 1.0 / (double)nlam;
       __builtin_amdgcn_wave_barrier();
-      const v4u zero4 = v4u{0u, 0u, 0u, 0u};
-      const v4u xa = nok ? na : zero4, xb = nok ? nb : zero4;
+      v4u xa = na, xb = nb;
+      if (!block_full) {  // rows past M read as zeros (uniform: most blocks skip it)
+        const v4u zero4 = v4u{0u, 0u, 0u, 0u};
+        xa = nok ? na : zero4;
+        xb = nok ? nb : zero4;
+      }
       uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
       // This tile's lora_down columns, read as whole 128-byte row segments:
       // load h of slice b gives lane L row b*16 + 8h + L/8 and its 16-byte
@@ -202,7 +209,10 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
       uint32_t hpk[8];  // X_hat as packed bf16 pairs (the T MFMA's A operand)
       float xh[16];
-      float amax = 0.f;
+      // largest |x_hat| of the lane as bf16 bits: for finite values the
+      // order of the magnitudes is that of their bit patterns with the sign
+      // cleared, so a packed 16-bit integer maximum serves
+      us2 am2 = us2{0, 0};
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float q[2];
@@ -218,26 +228,30 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         hpk[i >> 1] = pk;
         xh[i] = __uint_as_float(pk << 16);
         xh[i + 1] = __uint_as_float(pk & 0xFFFF0000u);
-        amax = fmaxf(amax, fmaxf(fabsf(xh[i]), fabsf(xh[i + 1])));
+        am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(us2, pk & 0x7FFF7FFFu));
       }
+      uint32_t amb = am2[0] > am2[1] ? am2[0] : am2[1];
 
       if constexpr (CODES) {
         if constexpr (MODE == 0) {
           // INT4: group of 64 = the four lanes sharing this row.
-          amax = fmaxf(amax, __shfl_xor(amax, 16));
-          amax = fmaxf(amax, __shfl_xor(amax, 32));
-          const float s = amax / 7.0f;
-          // cq = clamp(fp32(xh / s), -8, 7); the code is rint_even(cq) (the
-          // bounds are integers, so clamping before rounding is the same)
+          amb = max(amb, (uint32_t)__shfl_xor((int)amb, 16));
+          amb = max(amb, (uint32_t)__shfl_xor((int)amb, 32));
+          const float amax = __uint_as_float(amb << 16);
+          // s = fp32(amax / 7), exactly: amax is a bf16 value, so the fp64
+          // product with the correctly rounded fp64 1/7 rounds to it (the
+          // exact-quotient note above)
+          const float s = (float)((double)amax * (1.0 / 7.0));
+          // cq = fp32(xh / s); the code is rint_even(clamp(cq, -8, 7)).  The
+          // clamp never acts: |cq| <= amax / s, and s is within a relative
+          // 2^-24 of amax / 7 when normal, and within 2^-150 / (2^-133 / 7)
+          // < 2^-14 when subnormal (a nonzero bf16 amax is at least 2^-133),
+          // so |cq| < 7.0004 and its rounding lies in [-7, 7] either way.
+          // An all-zero group (s = 0) takes 1/s = 0: codes 0.
+          const double rs = s != 0.f ? 1.0 / (double)s : 0.0;
           float cq[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) cq[i] = 0.f;
-          if (s != 0.f) {
-            const double rs = 1.0 / (double)s;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              cq[i] = __builtin_amdgcn_fmed3f((float)((double)xh[i] * rs), -8.0f, 7.0f);
-          }
+          for (int i = 0; i < 16; ++i) cq[i] = (float)((double)xh[i] * rs);
           if (xcodes != nullptr && row_ok) {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -250,29 +264,26 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           }
           if (qi.img != nullptr) {
             // this lane's 16 fields are fields 0..15 (j even) or 16..31 (j odd)
-            // of K half j/2 of group k0/64
+            // of K half j/2 of group k0/64: an 8-byte and a 4-byte store,
+            // chosen without a branch
             uint8_t* blk = qi.img + ((int64_t)(k0 >> 6) * qi.RT + irt) * I4_BLOCK;
             uint8_t* half = blk + (j >> 1) * 768;
             uint32_t d0, d1, d2;
             fp6_fields16_hw(cq, d0, d1, d2);
-            if ((j & 1) == 0) {
-              *reinterpret_cast<v2u*>(half + 16 * irr) = v2u{d0, d1};
-              *reinterpret_cast<uint32_t*>(half + 16 * irr + 8) = d2;
-            } else {
-              *reinterpret_cast<uint32_t*>(half + 16 * irr + 12) = d0;
-              *reinterpret_cast<v2u*>(half + 512 + 8 * irr) = v2u{d1, d2};
-            }
-            // scale operand, X pattern: slot irr {hi | lo << 16, hi}, slot 32 + irr {lo, 0}
-            if (j < 2) {
-              const uint32_t hb = f32_to_bf16(s);
-              const uint32_t lb = f32_to_bf16(s - bf16_to_f32(hb));
-              const v2u so = j == 0 ? v2u{hb | (lb << 16), hb} : v2u{lb, 0u};
-              *reinterpret_cast<v2u*>(blk + 1536 + 8 * (32 * j + irr)) = so;
-            }
+            const bool ev = (j & 1) == 0;
+            *reinterpret_cast<v2u*>(half + (ev ? 16 * irr : 512 + 8 * irr)) = ev ? v2u{d0, d1} : v2u{d1, d2};
+            *reinterpret_cast<uint32_t*>(half + 16 * irr + (ev ? 8 : 12)) = ev ? d2 : d0;
+            // scale operand, X pattern: slot irr {hi | lo << 16, hi}, slot
+            // 32 + irr {lo, 0}; lanes j = 2, 3 store the same bytes as j = 0, 1
+            const uint32_t hb = f32_to_bf16(s);
+            const uint32_t lb = f32_to_bf16(s - bf16_to_f32(hb));
+            const v2u so = ev ? v2u{hb | (lb << 16), hb} : v2u{lb, 0u};
+            *reinterpret_cast<v2u*>(blk + 1536 + 8 * (32 * (j & 1) + irr)) = so;
           }
         } else if constexpr (MODE == 1) {
           // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
-          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amb = max(amb, (uint32_t)__shfl_xor((int)amb, 16));
+          const float amax = __uint_as_float(amb << 16);
           const int e = e8m0_exponent(amax);
           uint32_t w0 = 0, w1 = 0;
           if (e >= -100) {
@@ -308,7 +319,8 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
             const int64_t b = (int64_t)(k0 >> 6) * qi.RT + irt;
             const int slot = 32 * (j >> 1) + irr;
             *reinterpret_cast<v2u*>(qi.img + b * F4_CBLOCK + 16 * slot + 8 * (j & 1)) = v2u{w0, w1};
-            if ((j & 1) == 0) qi.img[qi.scale + b * F4_SBLOCK + slot] = (uint8_t)(e + 127);
+            // both lanes of the pair store the block's scale byte (the same)
+            qi.img[qi.scale + b * F4_SBLOCK + slot] = (uint8_t)(e + 127);
           }
         } else {
           // NVFP4: this lane's 16 elements are one block.  s =
@@ -316,6 +328,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           // fp32(x_hat / d); the quotient comes from d's fp64 reciprocal,
           // exact for a bf16 numerator as x / lambda above.
           const float g = *qi.g;
+          const float amax = __uint_as_float(amb << 16);
           const uint32_t sb = e4m3_encode(amax / __fmul_rn(6.0f, g));
           const float sv = e4m3_value(sb);
           uint32_t w0 = 0, w1 = 0;
