@@ -10,7 +10,7 @@
 // lane l holds row l%16 and the 16 columns 16*(l/16) .. +15, which is also
 // the A-operand layout of two v_mfma_f32_16x16x32_bf16, so the smoothed
 // bf16 values feed the MFMA straight from registers.  Per-group absmax is a
-// xor-shuffle over the lanes that share a row.  The waves' T partials are
+// maximum over the lanes that share a row, exchanged by the gfx950 lane swaps.  The waves' T partials are
 // summed through LDS at the end.
 //
 // Exact quotients without a division per element.  Both quotients of the
@@ -62,12 +62,26 @@ struct QaShape {
 // apart, which then fall into different banks.
 __device__ __forceinline__ int rl_idx(int c) { return c + ((c >> 4) << 1); }
 
+// max(v, v of lane l ^ 16) and max(v, v of lane l ^ 32): v_permlane16_swap
+// exchanges the odd 16-lane rows of one operand with the even rows of the
+// other, v_permlane32_swap the upper half of one with the lower half of the
+// other, so with v in both operands each lane ends up with its own value and
+// its partner's, one in each result.
+__device__ __forceinline__ uint32_t max_xor16(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return p[0] > p[1] ? p[0] : p[1];
+}
+__device__ __forceinline__ uint32_t max_xor32(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return p[0] > p[1] ? p[0] : p[1];
+}
+
 // LDS: during the main loop, per wave, the reciprocals of its tile's lambdas
-// and, with a down-projection, a 2 KB staging buffer (one 16-rank slice of a
+// (two slots: this tile's and the next one's) and, with a down-projection, a 2 KB staging buffer (one 16-rank slice of a
 // lora_down tile); the T partials afterwards.
 template <int MODE, int RB>
 struct QaLds {
-  static constexpr int kRcp = QaShape<MODE, RB>::kWaves * QA_RCP * 8;
+  static constexpr int kRcp = QaShape<MODE, RB>::kWaves * 2 * QA_RCP * 8;
   static constexpr int kStage = RB > 0 ? QaShape<MODE, RB>::kWaves * 2048 : 0;
   static constexpr int kRed = QaShape<MODE, RB>::kWaves * (RB > 0 ? RB : 1) * 4 * 64 * 4;
   static constexpr int kBytes = kRcp + kStage > kRed ? kRcp + kStage : kRed;
@@ -130,7 +144,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  double* rlam = reinterpret_cast<double*>(smem) + wave * QA_RCP;
+  double* rlam = reinterpret_cast<double*>(smem) + wave * 2 * QA_RCP;
   const int r16 = lane & 15;
   const int j = lane >> 4;
   const int64_t row = (int64_t)blockIdx.x * QA_ROWS + r16;
@@ -165,14 +179,18 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       xb = *reinterpret_cast<const v4u*>(p + 8);
     };
     auto load_lam = [&](int t) { return lambda[kbeg + (t < ntiles ? t : ntiles - 1) * 64 + lane]; };
+    // lambda first: waiting for it does not wait for the X loads behind it
+    float nlam = load_lam(wave);
     v4u na, nb;
     bool nok;
     load_x(wave, na, nb, nok);
-    float nlam = load_lam(wave);
+    // the first tile's reciprocals of lambda (column t*64 + lane of the range)
+    rlam[rl_idx(lane)] = 1.0 / (double)nlam;
+    int slot = 0;
     for (int t = wave; t < ntiles; t += QA_WAVES) {
-      // this tile's reciprocals of lambda: column t*64 + lane of the range
-      rlam[rl_idx(lane)] = 1.0 / (double)nlam;
+      const double* rcur = rlam + slot * QA_RCP;
       __builtin_amdgcn_wave_barrier();
+      nlam = load_lam(t + QA_WAVES);  // the next tile's, made into reciprocals at the end
       v4u xa = na, xb = nb;
       if (!block_full) {  // rows past M read as zeros (uniform: most blocks skip it)
         const v4u zero4 = v4u{0u, 0u, 0u, 0u};
@@ -198,7 +216,6 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         lg[b][1] = load_l1(b, 1);
       }
       load_x(t + QA_WAVES, na, nb, nok);  // next tile of this wave
-      nlam = load_lam(t + QA_WAVES);
       if constexpr (GELU) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) xw[i] = gelu_bf16x2(xw[i], gtab);
@@ -219,7 +236,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const uint32_t xbits = (xw[i >> 1] >> (e * 16)) & 0xFFFFu;
-          q[e] = (float)((double)bf16_to_f32(xbits) * rlam[rl_idx(kl + i + e)]);
+          q[e] = (float)((double)bf16_to_f32(xbits) * rcur[rl_idx(kl + i + e)]);
         }
         // RNE to bf16 (v_cvt_pk_bf16_f32: the same rounding as the
         // bit-level definition for every finite value)
@@ -235,8 +252,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       if constexpr (CODES) {
         if constexpr (MODE == 0) {
           // INT4: group of 64 = the four lanes sharing this row.
-          amb = max(amb, (uint32_t)__shfl_xor((int)amb, 16));
-          amb = max(amb, (uint32_t)__shfl_xor((int)amb, 32));
+          amb = max_xor32(max_xor16(amb));
           const float amax = __uint_as_float(amb << 16);
           // s = fp32(amax / 7), exactly: amax is a bf16 value, so the fp64
           // product with the correctly rounded fp64 1/7 rounds to it (the
@@ -247,8 +263,18 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           // 2^-24 of amax / 7 when normal, and within 2^-150 / (2^-133 / 7)
           // < 2^-14 when subnormal (a nonzero bf16 amax is at least 2^-133),
           // so |cq| < 7.0004 and its rounding lies in [-7, 7] either way.
-          // An all-zero group (s = 0) takes 1/s = 0: codes 0.
-          const double rs = s != 0.f ? 1.0 / (double)s : 0.0;
+          // 1/s need not be correctly rounded here: a reciprocal within a
+          // relative 2^-50 keeps fp32(xh * (1/s)) = fp32(xh / s) wherever the
+          // quotient is a normal fp32 value (the margin is about 2^-48), and a
+          // quotient in the subnormal range gives code 0 either way.  So the
+          // hardware reciprocal with two Newton steps serves (each step
+          // squares its relative error).  An all-zero group (s = 0) takes
+          // 1/s = 0: codes 0.
+          const double sd = (double)s;
+          double rs = __builtin_amdgcn_rcp(sd);
+          rs = __builtin_fma(rs, __builtin_fma(-sd, rs, 1.0), rs);
+          rs = __builtin_fma(rs, __builtin_fma(-sd, rs, 1.0), rs);
+          rs = s != 0.f ? rs : 0.0;
           float cq[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) cq[i] = (float)((double)xh[i] * rs);
@@ -282,7 +308,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           }
         } else if constexpr (MODE == 1) {
           // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
-          amb = max(amb, (uint32_t)__shfl_xor((int)amb, 16));
+          amb = max_xor16(amb);
           const float amax = __uint_as_float(amb << 16);
           const int e = e8m0_exponent(amax);
           uint32_t w0 = 0, w1 = 0;
@@ -345,6 +371,11 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           }
         }
       }
+
+      // the next tile's reciprocals of lambda, into the other slot (its
+      // lambda was requested at the top of this tile)
+      slot ^= 1;
+      rlam[slot * QA_RCP + rl_idx(lane)] = 1.0 / (double)nlam;
 
       if constexpr (RB > 0) {
         // T += X_hat[16 rows, 64 cols] . L1[64 cols, 16*RB]: element i of

@@ -96,3 +96,43 @@ def test_a_reciprocal_one_ulp_low_misrounds_exact_subnormal_midpoints():
         low = np.float32(np.float64(a) * np.nextafter(r, 0.0))
     assert exact.view(np.uint32) == ref.view(np.uint32) == 2
     assert low.view(np.uint32) == 1
+
+
+def test_int4_scale_is_the_fp64_product_with_one_seventh():
+    """The INT4 group scale s = fp32(amax / 7) is formed as the fp64 product of
+    amax with the correctly rounded fp64 1/7 (an instance of the identity
+    above, 7 being the divisor): equal for every finite bf16 amax."""
+    am = np.abs(_all_finite_bf16())
+    ref = am / np.float32(7.0)
+    got = (am.astype(np.float64) * (1.0 / 7.0)).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_int4_codes_need_neither_the_clamp_nor_an_exact_reciprocal_of_s():
+    """For INT4 codes rint_even(clamp(fp32(x_hat / s), -8, 7)) with s = fp32(amax
+    / 7) and |x_hat| <= amax: the clamp never acts (|fp32(x_hat / s)| < 7.0004),
+    and a reciprocal of s up to 8 fp64 ulps off the correctly rounded one
+    gives the same codes, so the kernel may take 1/s from the hardware
+    reciprocal with Newton steps.  Every finite bf16 x_hat up to amax, for
+    amax at the smallest subnormals, the largest finite values and a sample in
+    between."""
+    rng = np.random.default_rng(3)
+    a32 = _all_finite_bf16()
+    mags = np.unique(np.abs(a32[a32 != 0]))
+    amaxes = np.concatenate([mags[:8], mags[-4:], rng.choice(mags, 48, replace=False)])
+    worst = 0.0
+    with np.errstate(over="ignore", under="ignore"):
+        for amax in amaxes:
+            s = np.float32(amax) / np.float32(7.0)
+            x = a32[np.abs(a32) <= amax]
+            q = x / s                                            # IEEE fp32 quotient
+            worst = max(worst, float(np.max(np.abs(q))))
+            ref = np.rint(np.clip(q, -8, 7))
+            r = 1.0 / np.float64(s)
+            for k in (-8, -3, -1, 1, 3, 8):
+                rk = r
+                for _ in range(abs(k)):
+                    rk = np.nextafter(rk, np.inf if k > 0 else 0.0)
+                got = np.rint((x.astype(np.float64) * rk).astype(np.float32))
+                assert np.array_equal(got, ref), (float(amax), k)
+    assert worst < 7.0004
