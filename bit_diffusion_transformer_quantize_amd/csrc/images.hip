@@ -9,73 +9,65 @@
 
 namespace svdq {
 
-// 32 two's-complement int4 codes (16 bytes, element 2j in the low nibble of
-// byte j) -> 32 E2M3 sign-magnitude fields of 6 bits (value q/8) packed
-// little-endian into six dwords.  For a nibble x the field is x when x < 8
-// and 0x20 | (16 - x) = 0x30 - x otherwise.
-__device__ __forceinline__ void int4x32_to_fp6x32(const v4u& w, uint32_t (&o)[6]) {
-  uint64_t bits[3] = {0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t x = (w[j >> 3] >> (4 * (j & 7))) & 15u;
-    const uint64_t f = x < 8u ? x : 0x30u - x;
-    const int b = 6 * j;
-    bits[b >> 6] |= f << (b & 63);
-    if ((b & 63) > 58) bits[(b >> 6) + 1] |= f >> (64 - (b & 63));
-  }
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    o[2 * i] = (uint32_t)bits[i];
-    o[2 * i + 1] = (uint32_t)(bits[i] >> 32);
-  }
-}
+// The code blocks are written one wave per (group, 32-row tile); the four
+// waves of a workgroup take four consecutive groups of the same row tile, so
+// that together they read whole 128-byte runs of each row's packed codes.
 
-// INT4 code blocks of the weight: one wave per (group, 32-row tile).  Rows
-// R .. RP-1 are zero.  Scale operand, W pattern: lanes 0..31
-// {hi | hi << 16, lo}, lanes 32..63 {lo, 0}, so that with the activation
-// pattern {hi | lo << 16, hi} / {lo, 0} the K slots 0..3 of the outer-product
-// MFMA hold hi*hi, lo*hi, hi*lo, 0 and slot 4 lo*lo.
-__global__ __launch_bounds__(256) void int4_code_image_kernel(int64_t R, int64_t RT, int K,
-                                                              const uint8_t* __restrict__ codes,
-                                                              const float* __restrict__ scales,
-                                                              uint8_t* __restrict__ image) {
+// INT4 code block: lane l converts the 32 codes of row l%32, K half l/32, to
+// E2M3 sign-magnitude fields of 6 bits (value q/8, exact for every code)
+// packed little-endian into six dwords, by the gfx950 conversion to FP6
+// (scale operand 8: it divides by 2^3; its two sources give the even and
+// the odd fields).  Rows R .. RP-1 are zero.  Scale operand, W pattern:
+// lanes 0..31 {hi | hi << 16, lo}, lanes 32..63 {lo, 0}, so that with the
+// activation pattern {hi | lo << 16, hi} / {lo, 0} the K slots 0..3 of the
+// outer-product MFMA hold hi*hi, lo*hi, hi*lo, 0 and slot 4 lo*lo.
+__device__ __forceinline__ void int4_code_block(int64_t R, int64_t RT, int K, int64_t wv,
+                                                const uint8_t* __restrict__ codes,
+                                                const float* __restrict__ scales,
+                                                uint8_t* __restrict__ image, int lane) {
   const int G = K >> 6;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= (int64_t)G * RT) return;
-  const int g = (int)(blk / RT);
-  const int64_t r = (blk - (int64_t)g * RT) * 32 + (threadIdx.x & 31);
-  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-  uint8_t* out = image + blk * I4_BLOCK;
+  const int64_t rt = wv / G;
+  const int g = (int)(wv - rt * G);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t r = rt * 32 + l32;
+  uint8_t* out = image + ((int64_t)g * RT + rt) * I4_BLOCK;
   v4u w = {0u, 0u, 0u, 0u};
   float sv = 0.f;
   if (r < R) {
     w = *reinterpret_cast<const v4u*>(codes + r * (K >> 1) + g * 32 + h * 16);
     sv = scales[r * G + g];
   }
-  uint32_t o[6];
-  int4x32_to_fp6x32(w, o);
-  *reinterpret_cast<v4u*>(out + h * 768 + l32 * 16) = v4u{o[0], o[1], o[2], o[3]};
-  *reinterpret_cast<v2u*>(out + h * 768 + 512 + l32 * 8) = v2u{o[4], o[5]};
+  v16f ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    // element 2i is the low nibble of byte i, 2i + 1 the high one
+    const uint32_t byte = w[i >> 2] >> (8 * (i & 3));
+    ev[i] = (float)((int32_t)(byte << 28) >> 28);
+    od[i] = (float)((int32_t)(byte << 24) >> 28);
+  }
+  const v6i f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+  *reinterpret_cast<v4u*>(out + h * 768 + l32 * 16) =
+      v4u{(uint32_t)f[0], (uint32_t)f[1], (uint32_t)f[2], (uint32_t)f[3]};
+  *reinterpret_cast<v2u*>(out + h * 768 + 512 + l32 * 8) = v2u{(uint32_t)f[4], (uint32_t)f[5]};
   const uint32_t hb = f32_to_bf16(sv);
   const uint32_t lb = f32_to_bf16(sv - bf16_to_f32(hb));
   const v2u so = h == 0 ? v2u{hb | (hb << 16), lb} : v2u{lb, 0u};
   *reinterpret_cast<v2u*>(out + 1536 + lane * 8) = so;
 }
 
-// FP4 code and scale blocks of the weight: one wave per (group, 32-row
-// tile); lane l copies the 16 code bytes of row l%32, K half l/32, and its
-// E8M0 byte.  Rows R .. RP-1 are zero.
-__global__ __launch_bounds__(256) void fp4_code_image_kernel(int64_t R, int64_t RT, int K,
-                                                             const uint8_t* __restrict__ codes,
-                                                             const uint8_t* __restrict__ scales,
-                                                             uint8_t* __restrict__ image,
-                                                             size_t scale_off) {
+// FP4 code and scale block: lane l copies the 16 code bytes of row l%32,
+// K half l/32, and its E8M0 byte.  Rows R .. RP-1 are zero.
+__device__ __forceinline__ void fp4_code_block(int64_t R, int64_t RT, int K, int64_t wv,
+                                               const uint8_t* __restrict__ codes,
+                                               const uint8_t* __restrict__ scales,
+                                               uint8_t* __restrict__ image, size_t scale_off,
+                                               int lane) {
   const int G = K >> 6;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= (int64_t)G * RT) return;
-  const int g = (int)(blk / RT);
-  const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int64_t r = (blk - (int64_t)g * RT) * 32 + (lane & 31);
+  const int64_t rt = wv / G;
+  const int g = (int)(wv - rt * G);
+  const int h = lane >> 5;
+  const int64_t r = rt * 32 + (lane & 31);
+  const int64_t blk = (int64_t)g * RT + rt;
   v4u w = {0u, 0u, 0u, 0u};
   uint8_t sc = 0;
   if (r < R) {
@@ -86,16 +78,15 @@ __global__ __launch_bounds__(256) void fp4_code_image_kernel(int64_t R, int64_t 
   image[scale_off + blk * F4_SBLOCK + lane] = sc;
 }
 
-// Low-rank and bias blocks of the weight image.  Threads [0, nlr) write one
-// 16-byte lane entry of an L2 block each (slice q, column tile ct, lane l:
-// column 32 ct + l%32, ranks 16 q + 8 (l/32) .. +7); the next threads write
-// the bias blocks and the zero tail, 16 bytes each.
-__global__ __launch_bounds__(256) void lr_bias_image_kernel(int N, int rank, int64_t CT,
-                                                            const uint16_t* __restrict__ lora_up,
-                                                            const uint16_t* __restrict__ bias,
-                                                            uint8_t* __restrict__ lr_out,
-                                                            uint8_t* __restrict__ bias_out) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Low-rank and bias blocks of the weight image.  Thread t < nlr writes one
+// 16-byte lane entry of an L2 block (slice q, column tile ct, lane l: column
+// 32 ct + l%32, ranks 16 q + 8 (l/32) .. +7); the next threads write the
+// bias blocks and the zero tail, 16 bytes each.
+__device__ __forceinline__ void lr_bias_entry(int N, int rank, int64_t CT, int64_t t,
+                                              const uint16_t* __restrict__ lora_up,
+                                              const uint16_t* __restrict__ bias,
+                                              uint8_t* __restrict__ lr_out,
+                                              uint8_t* __restrict__ bias_out) {
   const int64_t nlr = (int64_t)(rank / 16) * CT * 64;
   const int64_t nbias = (CT * BIAS_BLOCK + BIAS_TAIL) / 16;
   if (t < nlr) {
@@ -122,8 +113,30 @@ __global__ __launch_bounds__(256) void lr_bias_image_kernel(int N, int rank, int
   }
 }
 
-size_t weight_image_bytes(int mode, int N, int K, int rank) {
-  return weight_image(mode, N, K, rank).bytes;
+// The whole prepared weight in one launch: workgroups [0, ncode) write the
+// code blocks (four waves each), the rest the low-rank and bias blocks.
+template <int MODE>
+__global__ __launch_bounds__(256) void weight_image_kernel(int N, int K, int rank, int64_t RT,
+                                                           int64_t ncode,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const void* __restrict__ scales,
+                                                           const uint16_t* __restrict__ lora_up,
+                                                           const uint16_t* __restrict__ bias,
+                                                           uint8_t* __restrict__ img,
+                                                           WeightImage wi) {
+  if ((int64_t)blockIdx.x < ncode) {
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= (int64_t)(K >> 6) * RT) return;
+    if constexpr (MODE == 0)
+      int4_code_block(N, RT, K, wv, codes, static_cast<const float*>(scales), img + wi.code,
+                      threadIdx.x & 63);
+    else
+      fp4_code_block(N, RT, K, wv, codes, static_cast<const uint8_t*>(scales), img + wi.code,
+                     wi.scale, threadIdx.x & 63);
+    return;
+  }
+  const int64_t t = ((int64_t)blockIdx.x - ncode) * 256 + threadIdx.x;
+  lr_bias_entry(N, rank, RT, t, lora_up, bias, img + wi.lr, img + wi.bias);
 }
 
 hipError_t launch_prepare_weight(int mode, int N, int K, int rank, const uint8_t* wcodes,
@@ -131,19 +144,20 @@ hipError_t launch_prepare_weight(int mode, int N, int K, int rank, const uint8_t
                                  const uint16_t* bias, void* wimage, hipStream_t s) {
   const WeightImage wi = weight_image(mode, N, K, rank);
   uint8_t* img = reinterpret_cast<uint8_t*>(wimage);
-  const int64_t blocks = ((int64_t)(K / 64) * wi.CT + 3) / 4;
-  if (mode == 0)
-    hipLaunchKernelGGL(int4_code_image_kernel, dim3((unsigned)blocks), dim3(256), 0, s, N, wi.CT,
-                       K, wcodes, static_cast<const float*>(wscales), img + wi.code);
-  else
-    hipLaunchKernelGGL(fp4_code_image_kernel, dim3((unsigned)blocks), dim3(256), 0, s, N, wi.CT,
-                       K, wcodes, static_cast<const uint8_t*>(wscales), img + wi.code, wi.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int64_t ncode = ((int64_t)(K / 64) * wi.CT + 3) / 4;
   const int64_t nthreads = (int64_t)(rank / 16) * wi.CT * 64 + (wi.CT * BIAS_BLOCK + BIAS_TAIL) / 16;
-  hipLaunchKernelGGL(lr_bias_image_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
-                     s, N, rank, wi.CT, lora_up, bias, img + wi.lr, img + wi.bias);
+  const dim3 grid((unsigned)(ncode + (nthreads + 255) / 256));
+  if (mode == 0)
+    hipLaunchKernelGGL(weight_image_kernel<0>, grid, dim3(256), 0, s, N, K, rank, wi.CT, ncode,
+                       wcodes, wscales, lora_up, bias, img, wi);
+  else
+    hipLaunchKernelGGL(weight_image_kernel<1>, grid, dim3(256), 0, s, N, K, rank, wi.CT, ncode,
+                       wcodes, wscales, lora_up, bias, img, wi);
   return hipGetLastError();
+}
+
+size_t weight_image_bytes(int mode, int N, int K, int rank) {
+  return weight_image(mode, N, K, rank).bytes;
 }
 
 }  // namespace svdq

@@ -269,6 +269,29 @@ svdq_status svdq_linear_forward(const svdq_desc* d, int64_t M, const void* ximag
                                            (hipStream_t)stream));
 }
 
+svdq_status svdq_linear_forward_packed(const svdq_desc* d, int64_t M, const void* ximage,
+                                       size_t ximage_bytes, const uint8_t* wcodes,
+                                       const void* wscales, const uint16_t* lora_up,
+                                       const uint16_t* bias, void* wscratch,
+                                       size_t wscratch_bytes, void* Y, void* stream) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows_k(M, d->K));
+  if (M > (int64_t(1) << 46) / d->N) return SVDQ_ERR_SHAPE;
+  if (!ptr_ok(ximage) || !ptr_ok(wcodes) || !ptr_ok(wscales) || !ptr_ok(wscratch) ||
+      !ptr_ok(Y) || !opt_ok(bias))
+    return SVDQ_ERR_ARG;
+  if (d->rank > 0 ? !ptr_ok(lora_up) : lora_up != nullptr) return SVDQ_ERR_ARG;
+  SVDQ_TRY(check_images(d, M, ximage_bytes, wscratch_bytes));
+  const bool f32 = (d->flags & SVDQ_FLAG_OUT_F32) != 0u;
+  SVDQ_TRY(check_device());
+  const hipStream_t s = (hipStream_t)stream;
+  SVDQ_TRY(from_hip(svdq::launch_prepare_weight(d->mode, d->N, d->K, d->rank, wcodes, wscales,
+                                                lora_up, bias, wscratch, s)));
+  if (d->mode == SVDQ_MODE_INT4)
+    return from_hip(svdq::launch_int4_forward(f32, M, d->N, d->K, d->rank, ximage, wscratch, Y, s));
+  return from_hip(svdq::launch_fp4_forward(f32, M, d->N, d->K, d->rank, ximage, wscratch, Y, s));
+}
+
 namespace {
 // An INT4 up layer feeding an INT4 down layer whose input is GELU of the up
 // layer's output (down->K == up->N), down rank at most 128.

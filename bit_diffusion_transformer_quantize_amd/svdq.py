@@ -60,6 +60,8 @@ _SIGNATURES = {
                                          _vp]),
     "svdq_prepare_weight": (ctypes.c_int, [_DESC, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _vp, _vp]),
+    "svdq_linear_forward_packed": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
+                                                  _sz, _vp, _vp]),
     "svdq_gelu_quantize_workspace_size": (ctypes.c_int, [_DESC, _i64, _DESC,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_linear_forward_gelu_quantize": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _DESC, _vp,
@@ -301,6 +303,31 @@ def svdq_linear_forward(d: SvdqDesc, M: int, ximage, wimage, Y=None):
     _check("svdq_linear_forward",
            load().svdq_linear_forward(ctypes.byref(d), M, _p(ximage), _nbytes(ximage), _p(wimage),
                                       _nbytes(wimage), _p(Y), _stream()))
+    return Y
+
+
+def svdq_linear_forward_packed(d: SvdqDesc, M: int, ximage, wcodes, wscales, lora_up=None,
+                               bias=None, wscratch=None, Y=None):
+    """The layer from the packed 4-bit weight (codes, scales), L2 and the bias:
+    the prepared weight is written into wscratch (allocated when None) and the
+    GEMM runs on it; returns Y."""
+    N, K, r = d.N, d.K, d.rank
+    out_dtype = torch.float32 if (d.flags & SVDQ_FLAG_OUT_F32) else torch.bfloat16
+    _need(ximage, "ximage", torch.uint8)
+    _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
+    _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
+    _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=True)
+    _need(bias, "bias", torch.bfloat16, (N,), optional=True)
+    if wscratch is None:
+        wscratch = torch.empty(svdq_weight_image_size(d), dtype=torch.uint8, device=wcodes.device)
+    _need(wscratch, "wscratch", torch.uint8)
+    if Y is None:
+        Y = torch.empty(M, N, dtype=out_dtype, device=ximage.device)
+    _need(Y, "Y", out_dtype, (M, N))
+    _check("svdq_linear_forward_packed",
+           load().svdq_linear_forward_packed(ctypes.byref(d), M, _p(ximage), _nbytes(ximage), _p(wcodes),
+                                             _p(wscales), _p(lora_up), _p(bias), _p(wscratch),
+                                             _nbytes(wscratch), _p(Y), _stream()))
     return Y
 
 

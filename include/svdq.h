@@ -386,6 +386,27 @@ svdq_status svdq_linear_forward(const svdq_desc* desc, int64_t M, const void* xi
                                 size_t ximage_bytes, const void* wimage, size_t wimage_bytes,
                                 void* Y, void* stream);
 
+/* The same layer from weights kept resident in their packed 4-bit form: the
+ * row-major codes and scales of svdq_pack_weight (INT4: 4.5 bits per weight
+ * with the fp32 group scales; FP4: 4.25), L2 and the bias, instead of a
+ * prepared weight (INT4: 8 bits per weight).  This is the memory case of the
+ * pages (axbrief.com page, section "The Mechanics ...": 4-bit weights; the
+ * apatero.com page, section "O que e Nunchaku ...", on the 3.6x smaller
+ * model).  The gfx950 matrix instructions have no 4-bit integer operand, so
+ * each call first writes the prepared weight into wscratch (a device buffer
+ * of wscratch_bytes = svdq_weight_image_size(desc) bytes, else SVDQ_ERR_ARG
+ * before anything is enqueued), then runs svdq_linear_forward on it: two
+ * kernels on the stream, Y bit-identical to svdq_prepare_weight followed by
+ * svdq_linear_forward.  One scratch serves every layer whose image fits, one
+ * call at a time per scratch (calls that overlap on one scratch race).
+ * Arguments as for svdq_prepare_weight and svdq_linear_forward; wscratch
+ * must not overlap the other buffers. */
+svdq_status svdq_linear_forward_packed(const svdq_desc* desc, int64_t M, const void* ximage,
+                                       size_t ximage_bytes, const uint8_t* wcodes,
+                                       const void* wscales, const uint16_t* lora_up,
+                                       const uint16_t* bias, void* wscratch,
+                                       size_t wscratch_bytes, void* Y, void* stream);
+
 /* The MLP up-projection with the next layer's activation pass fused into
  * its epilogue (Nunchaku Lite page on axbrief.com, section "The Trade-off
  * Between Fused Kernels and Generality": neighbouring steps of the block

@@ -226,6 +226,35 @@ def test_linear_forward_pointer_validation():
     assert f(_d(N=1 << 20), 1 << 27, A, A, A) == SHAPE
 
 
+def test_linear_forward_packed_validation():
+    """The packed-weight forward checks its arguments as svdq_prepare_weight and
+    svdq_linear_forward do, the scratch against svdq_weight_image_size, before
+    anything is enqueued."""
+    lib = _lib()
+    xb, wb = _xb(), _wb()
+
+    def f(d, M=256, xi=A, nx=xb, wc=A, ws=A, lu=A, b=A, sc=A, ns=wb, Y=A):
+        return lib.svdq_linear_forward_packed(d, M, xi, nx, wc, ws, lu, b, sc, ns, Y, None)
+
+    assert f(None) == ARG
+    assert f(_d(mode=3)) == ARG
+    assert f(_d(K=96)) == SHAPE
+    assert f(_d(), M=0) == SHAPE
+    assert f(_d(N=1 << 20), M=1 << 27) == SHAPE                   # output past 2^46 elements
+    assert f(_d(), xi=None) == ARG
+    assert f(_d(), xi=MIS) == ARG
+    assert f(_d(), wc=None) == ARG                                # codes null
+    assert f(_d(), ws=MIS) == ARG                                 # scales misaligned
+    assert f(_d(), lu=None) == ARG                                # rank > 0 needs lora_up
+    assert f(_d(rank=0), nx=_xb(rank=0), ns=_wb(rank=0)) == ARG   # rank 0 forbids it
+    assert f(_d(), b=MIS) == ARG                                  # bias misaligned
+    assert f(_d(), sc=None) == ARG                                # scratch null
+    assert f(_d(), Y=None) == ARG
+    assert f(_d(), ns=wb - 16) == ARG                             # scratch of another size
+    assert f(_d(), ns=_wb(mode=1)) == ARG
+    assert f(_d(), nx=_xb(M=1024)) == ARG                         # activation image for another M
+
+
 @pytest.mark.parametrize("what,kw", [
     ("activation image for another M", dict(nx=_xb(M=1024))),
     ("activation image for another rank", dict(nx=_xb(rank=32))),
@@ -450,6 +479,8 @@ def test_no_device_is_a_hip_error():
     assert lib.svdq_linear_forward(_d(mode=1), 256, A, _xb(mode=1), A, _wb(mode=1), A,
                                    None) == HIP
     assert lib.svdq_prepare_weight(_d(), A, A, A, None, A, _wb(), None) == HIP
+    assert lib.svdq_linear_forward_packed(_d(), 256, A, _xb(), A, A, A, None, A, _wb(), A,
+                                          None) == HIP
     assert lib.svdq_awq_pack_weight(64, 3072, A, A, A, A, None) == HIP
     assert lib.svdq_awq_linear(1, 64, 3072, A, A, A, A, None, 0, A, None) == HIP
     n = ctypes.c_size_t(0)
