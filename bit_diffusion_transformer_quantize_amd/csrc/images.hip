@@ -9,34 +9,26 @@
 
 namespace svdq {
 
-// The code blocks are written one wave per (group, 32-row tile); the four
-// waves of a workgroup take four consecutive groups of the same row tile, so
-// that together they read whole 128-byte runs of each row's packed codes.
+// The code blocks are written one wave per (group, 32-row tile).  A
+// workgroup of four waves takes one row tile and four consecutive groups:
+// it first stages the 32 rows' 128-byte runs of packed codes (and their
+// scales) in LDS, each load covering whole row segments (8 lanes per row:
+// 8 cache lines in full, where loading in the lanes' final order touches 32
+// lines, a quarter of each), then each wave reads its group's block back in
+// lane order.  The 16-byte chunk c of staged row n sits at position
+// c ^ (n % 8), so both sides meet every bank once per eight lanes.
 
-// INT4 code block: lane l converts the 32 codes of row l%32, K half l/32, to
-// E2M3 sign-magnitude fields of 6 bits (value q/8, exact for every code)
+// INT4 code block: lane l converts the 32 codes w of row l%32, K half l/32,
+// to E2M3 sign-magnitude fields of 6 bits (value q/8, exact for every code)
 // packed little-endian into six dwords, by the gfx950 conversion to FP6
 // (scale operand 8: it divides by 2^3; its two sources give the even and
-// the odd fields).  Rows R .. RP-1 are zero.  Scale operand, W pattern:
-// lanes 0..31 {hi | hi << 16, lo}, lanes 32..63 {lo, 0}, so that with the
-// activation pattern {hi | lo << 16, hi} / {lo, 0} the K slots 0..3 of the
+// the odd fields).  Scale operand, W pattern: lanes 0..31
+// {hi | hi << 16, lo}, lanes 32..63 {lo, 0}, so that with the activation
+// pattern {hi | lo << 16, hi} / {lo, 0} the K slots 0..3 of the
 // outer-product MFMA hold hi*hi, lo*hi, hi*lo, 0 and slot 4 lo*lo.
-__device__ __forceinline__ void int4_code_block(int64_t R, int64_t RT, int K, int64_t wv,
-                                                const uint8_t* __restrict__ codes,
-                                                const float* __restrict__ scales,
-                                                uint8_t* __restrict__ image, int lane) {
-  const int G = K >> 6;
-  const int64_t rt = wv / G;
-  const int g = (int)(wv - rt * G);
+__device__ __forceinline__ void int4_code_block(uint8_t* __restrict__ out, int lane, const v4u& w,
+                                                float sv) {
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t r = rt * 32 + l32;
-  uint8_t* out = image + ((int64_t)g * RT + rt) * I4_BLOCK;
-  v4u w = {0u, 0u, 0u, 0u};
-  float sv = 0.f;
-  if (r < R) {
-    w = *reinterpret_cast<const v4u*>(codes + r * (K >> 1) + g * 32 + h * 16);
-    sv = scales[r * G + g];
-  }
   v16f ev, od;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -55,27 +47,56 @@ __device__ __forceinline__ void int4_code_block(int64_t R, int64_t RT, int K, in
   *reinterpret_cast<v2u*>(out + 1536 + lane * 8) = so;
 }
 
-// FP4 code and scale block: lane l copies the 16 code bytes of row l%32,
-// K half l/32, and its E8M0 byte.  Rows R .. RP-1 are zero.
-__device__ __forceinline__ void fp4_code_block(int64_t R, int64_t RT, int K, int64_t wv,
-                                               const uint8_t* __restrict__ codes,
-                                               const uint8_t* __restrict__ scales,
-                                               uint8_t* __restrict__ image, size_t scale_off,
-                                               int lane) {
+// The code blocks of row tile rt, groups 4 quad .. 4 quad + 3 (MODE 0 INT4,
+// 1 FP4: the 16 code bytes as they are and the E8M0 byte of row l%32, K half
+// l/32).  Rows R .. RP-1 and groups past G come out as zeros.
+template <int MODE>
+__device__ __forceinline__ void code_blocks(int64_t R, int64_t RT, int K, int64_t rt, int quad,
+                                            const uint8_t* __restrict__ codes,
+                                            const void* __restrict__ scales,
+                                            uint8_t* __restrict__ image, size_t scale_off) {
+  __shared__ v4u cst[32][8];
+  __shared__ uint32_t sst[32][9];  // INT4: fp32 scale bits [row][group]; FP4: bytes [row][2 group + half]
   const int G = K >> 6;
-  const int64_t rt = wv / G;
-  const int g = (int)(wv - rt * G);
-  const int h = lane >> 5;
-  const int64_t r = rt * 32 + (lane & 31);
-  const int64_t blk = (int64_t)g * RT + rt;
-  v4u w = {0u, 0u, 0u, 0u};
-  uint8_t sc = 0;
-  if (r < R) {
-    w = *reinterpret_cast<const v4u*>(codes + r * (K >> 1) + g * 32 + h * 16);
-    sc = scales[r * (K >> 5) + 2 * g + h];
+  const int t = threadIdx.x;
+  {
+    const int row = t >> 3, c = t & 7;
+    const int64_t r = rt * 32 + row;
+    v4u v = {0u, 0u, 0u, 0u};
+    if (r < R && quad * 4 + (c >> 1) < G)
+      v = *reinterpret_cast<const v4u*>(codes + r * (K >> 1) + quad * 128 + c * 16);
+    cst[row][c ^ (row & 7)] = v;
+    if constexpr (MODE == 0) {
+      if (t < 128) {
+        const int row2 = t >> 2, j = t & 3;
+        const int64_t r2 = rt * 32 + row2;
+        const int g = quad * 4 + j;
+        sst[row2][j] = (r2 < R && g < G)
+                           ? __float_as_uint(static_cast<const float*>(scales)[r2 * G + g])
+                           : 0u;
+      }
+    } else {
+      // lane t: row t/8, byte t%8 of the row's run of scale bytes
+      const int64_t r2 = rt * 32 + row;
+      const int b = quad * 8 + c;
+      sst[row][c] = (r2 < R && b < 2 * G)
+                        ? (uint32_t) static_cast<const uint8_t*>(scales)[r2 * (K >> 5) + b]
+                        : 0u;
+    }
   }
-  *reinterpret_cast<v4u*>(image + blk * F4_CBLOCK + lane * 16) = w;
-  image[scale_off + blk * F4_SBLOCK + lane] = sc;
+  __syncthreads();
+  const int w = t >> 6, lane = t & 63;
+  const int g = quad * 4 + w;
+  if (g >= G) return;
+  const int h = lane >> 5, l32 = lane & 31;
+  const v4u cw = cst[l32][(2 * w + h) ^ (l32 & 7)];
+  const int64_t blk = (int64_t)g * RT + rt;
+  if constexpr (MODE == 0) {
+    int4_code_block(image + blk * I4_BLOCK, lane, cw, __uint_as_float(sst[l32][w]));
+  } else {
+    *reinterpret_cast<v4u*>(image + blk * F4_CBLOCK + lane * 16) = cw;
+    image[scale_off + blk * F4_SBLOCK + lane] = (uint8_t)sst[l32][2 * w + h];
+  }
 }
 
 // Low-rank and bias blocks of the weight image.  Thread t < nlr writes one
@@ -114,7 +135,8 @@ __device__ __forceinline__ void lr_bias_entry(int N, int rank, int64_t CT, int64
 }
 
 // The whole prepared weight in one launch: workgroups [0, ncode) write the
-// code blocks (four waves each), the rest the low-rank and bias blocks.
+// code blocks (one per row tile and four groups), the rest the low-rank and
+// bias blocks.
 template <int MODE>
 __global__ __launch_bounds__(256) void weight_image_kernel(int N, int K, int rank, int64_t RT,
                                                            int64_t ncode,
@@ -125,14 +147,10 @@ __global__ __launch_bounds__(256) void weight_image_kernel(int N, int K, int ran
                                                            uint8_t* __restrict__ img,
                                                            WeightImage wi) {
   if ((int64_t)blockIdx.x < ncode) {
-    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wv >= (int64_t)(K >> 6) * RT) return;
-    if constexpr (MODE == 0)
-      int4_code_block(N, RT, K, wv, codes, static_cast<const float*>(scales), img + wi.code,
-                      threadIdx.x & 63);
-    else
-      fp4_code_block(N, RT, K, wv, codes, static_cast<const uint8_t*>(scales), img + wi.code,
-                     wi.scale, threadIdx.x & 63);
+    const int nq = ((K >> 6) + 3) >> 2;  // group quads per row tile
+    const int64_t rt = (int64_t)blockIdx.x / nq;
+    code_blocks<MODE>(N, RT, K, rt, (int)((int64_t)blockIdx.x - rt * nq), codes, scales,
+                      img + wi.code, wi.scale);
     return;
   }
   const int64_t t = ((int64_t)blockIdx.x - ncode) * 256 + threadIdx.x;
@@ -144,7 +162,7 @@ hipError_t launch_prepare_weight(int mode, int N, int K, int rank, const uint8_t
                                  const uint16_t* bias, void* wimage, hipStream_t s) {
   const WeightImage wi = weight_image(mode, N, K, rank);
   uint8_t* img = reinterpret_cast<uint8_t*>(wimage);
-  const int64_t ncode = ((int64_t)(K / 64) * wi.CT + 3) / 4;
+  const int64_t ncode = (int64_t)((K / 64 + 3) / 4) * wi.CT;
   const int64_t nthreads = (int64_t)(rank / 16) * wi.CT * 64 + (wi.CT * BIAS_BLOCK + BIAS_TAIL) / 16;
   const dim3 grid((unsigned)(ncode + (nthreads + 255) / 256));
   if (mode == 0)
