@@ -134,9 +134,34 @@ constexpr Table make() {
   return t;
 }
 
+// The activation pass's wider band: |x| in [2^-24, 2^14) (biased exponents
+// 103..140), where nearly every activation falls, so that the rules above
+// are needed only for zeros, tiny or huge values, which the pass handles on
+// a rarely taken branch.  Per sign: 38 binades of 128 entries, then one
+// sentinel entry, the index that every out-of-band input is clamped to.
+constexpr int kWLoExp = 103, kWHiExp = 140;
+constexpr int kWBand = kWHiExp - kWLoExp + 1;
+constexpr int kWHalf = kWBand * 128 + 1;
+constexpr int kWEntries = 2 * kWHalf;
+static_assert(kWLoExp <= kLoExp && kWHiExp >= kHiExp, "the rules hold outside the wide band");
+struct WideTable {
+  uint16_t v[kWEntries];
+};
+constexpr WideTable make_wide() {
+  WideTable t{};
+  for (uint32_t s = 0; s < 2; ++s)
+    for (uint32_t e = kWLoExp; e <= (uint32_t)kWHiExp; ++e)
+      for (uint32_t m = 0; m < 128; ++m) {
+        const uint32_t xb = (s << 15) | (e << 7) | m;
+        t.v[s * kWHalf + (e - kWLoExp) * 128 + m] = entry(xb);
+      }
+  return t;
+}
+
 }  // namespace gelu_table
 
 __device__ constexpr gelu_table::Table kGeluBand = gelu_table::make();
+__device__ constexpr gelu_table::WideTable kGeluWide = gelu_table::make_wide();
 
 // bf16 GELU of one input (low 16 bits of b) from the band table in LDS and
 // the two rules.  Branch-free: the table index is clamped into range.
@@ -154,6 +179,16 @@ __device__ __forceinline__ uint32_t gelu_one(uint32_t b, const uint16_t* tab) {
 
 __device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w, const uint16_t* tab) {
   return gelu_one(w & 0xFFFFu, tab) | (gelu_one(w >> 16, tab) << 16);
+}
+
+// The bf16 GELU of the inputs outside the wide band (low 16 bits of b):
+// |x| < 2^-24 (zeros included) gives bf16_RNE(x / 2), |x| >= 2^14 gives x
+// for positive x and -0 for negative x; inf and NaN map to themselves.
+__device__ __forceinline__ uint32_t gelu_rule(uint32_t b) {
+  const uint32_t e = (b >> 7) & 0xFFu;
+  const uint32_t half = f32_to_bf16(__uint_as_float(b << 16) * 0.5f);
+  const uint32_t big = (e == 0xFFu || (b & 0x8000u) == 0) ? b : 0x8000u;
+  return e < (uint32_t)gelu_table::kWLoExp ? half : big;
 }
 
 }  // namespace svdq

@@ -135,11 +135,11 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   // lora_down slices loaded at the top of a tile (the rest when used)
   constexpr int QA_EARLY = QA_WAVES == 16 ? (RB <= 2 ? RB : 0) : (RB < 4 ? RB : 4);
   __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<MODE, RB>::kBytes];
-  // the GELU band table (7.5 KB), copied once before any lookup
-  __shared__ uint16_t gtab[GELU ? gelu_table::kEntries : 2];
+  // the wide GELU band table (19 KB), copied once before any lookup
+  __shared__ uint16_t gtab[GELU ? gelu_table::kWEntries : 2];
   if constexpr (GELU) {
-    for (int i = threadIdx.x; i < gelu_table::kEntries / 2; i += QA_THREADS)
-      reinterpret_cast<uint32_t*>(gtab)[i] = reinterpret_cast<const uint32_t*>(kGeluBand.v)[i];
+    for (int i = threadIdx.x; i < gelu_table::kWEntries / 2; i += QA_THREADS)
+      reinterpret_cast<uint32_t*>(gtab)[i] = reinterpret_cast<const uint32_t*>(kGeluWide.v)[i];
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
@@ -217,8 +217,37 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       }
       load_x(t + QA_WAVES, na, nb, nok);  // next tile of this wave
       if constexpr (GELU) {
+        // GELU of the 16 inputs from the wide band table, two at a time with
+        // packed 16-bit index arithmetic: the offset into the band, clamped
+        // to the sentinel for inputs outside it, plus the sign's half.  The
+        // rare out-of-band inputs are redone by the rules, on a branch that
+        // the whole wave skips when none of its inputs needs it.
+        using namespace gelu_table;
+        const us2 lo_off = us2{(unsigned short)(kWLoExp * 128), (unsigned short)(kWLoExp * 128)};
+        const us2 sent = us2{(unsigned short)(kWBand * 128), (unsigned short)(kWBand * 128)};
+        const us2 half_sz = us2{(unsigned short)kWHalf, (unsigned short)kWHalf};
+        uint32_t xin[8];
+        us2 worst = us2{0, 0};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xw[i] = gelu_bf16x2(xw[i], gtab);
+        for (int i = 0; i < 8; ++i) {
+          xin[i] = xw[i];
+          const us2 off = __builtin_elementwise_min(
+              __builtin_bit_cast(us2, xw[i] & 0x7FFF7FFFu) - lo_off, sent);
+          worst = __builtin_elementwise_max(worst, off);
+          const us2 idx = off + __builtin_bit_cast(us2, (xw[i] >> 15) & 0x00010001u) * half_sz;
+          xw[i] = (uint32_t)gtab[idx[0]] | ((uint32_t)gtab[idx[1]] << 16);
+        }
+        if (__any((worst[0] == sent[0]) | (worst[1] == sent[1]))) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t b = (xin[i] >> (16 * h)) & 0xFFFFu;
+              const uint32_t e = (b >> 7) & 0xFFu;
+              if (e < (uint32_t)kWLoExp || e > (uint32_t)kWHiExp)
+                xw[i] = (xw[i] & (0xFFFF0000u >> (16 * h))) | (gelu_rule(b) << (16 * h));
+            }
+        }
       }
       const int kl = j * 16;                // column within the tile
       const int k0 = kbeg + t * 64 + kl;  // column within the row
