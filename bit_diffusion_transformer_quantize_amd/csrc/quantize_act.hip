@@ -6,12 +6,13 @@
 // activations (apatero.com page, section "O que e Nunchaku e como acelera
 // modelos Qwen").  Here a workgroup owns 16 rows of X; its waves (16 for
 // INT4, 8 for FP4) take 64-column tiles round-robin, each prefetching its
-// next tile.  In a tile,
-// lane l holds row l%16 and the 16 columns 16*(l/16) .. +15, which is also
-// the A-operand layout of two v_mfma_f32_16x16x32_bf16, so the smoothed
-// bf16 values feed the MFMA straight from registers.  Per-group absmax is a
-// maximum over the lanes that share a row, exchanged by the gfx950 lane swaps.  The waves' T partials are
-// summed through LDS at the end.
+// next tile.  In a tile, lane l holds row l%16 and the 16 columns
+// 16*(l/16) .. +15, which is also the A-operand layout of two
+// v_mfma_f32_16x16x32_bf16, so the smoothed bf16 values feed the MFMA
+// straight from registers; lora_down reaches the B operand through a
+// per-wave LDS staging buffer.  The per-group absmax is a maximum over the
+// lanes that share a row, exchanged by the gfx950 lane swaps.  The waves' T
+// partials are summed through LDS at the end.
 //
 // Exact quotients without a division per element.  Both quotients of the
 // contract, fp32(x / lambda) and fp32(x_hat / s), divide a bf16 value
@@ -25,8 +26,9 @@
 // finite bf16 a against thousands of divisors: subnormals, all-ones
 // significands, INT4 scales, NVFP4 s g values).  Each wave computes the fp64
 // reciprocals of its tile's 64 lambdas into its own LDS slot (one per lane),
-// so the waves need no barrier before the T partials are summed; the
-// reciprocal of s is computed once per lane and group.
+// so the waves need no barrier before the T partials are summed.  The
+// reciprocal of s is computed once per lane and group (for INT4 codes only
+// to within a relative 2^-50, which is enough there; see the code).
 //
 // Outputs: the codes, scales and T in the documented row-major layouts
 // (each optional) and/or the activation operand image the GEMM reads
