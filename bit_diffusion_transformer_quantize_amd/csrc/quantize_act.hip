@@ -4,9 +4,9 @@
 // The Nunchaku engine fuses the down-projection of the low-rank branch into
 // the quantization kernel so that both branches share one read of the
 // activations (apatero.com page, section "O que e Nunchaku e como acelera
-// modelos Qwen").  Here a workgroup owns 16 rows of X; its waves (16 for
-// INT4, 8 for FP4) take 64-column tiles round-robin, each prefetching its
-// next tile.  In a tile, lane l holds row l%16 and the 16 columns
+// modelos Qwen").  Here a workgroup owns one or two 16-row blocks of X (see
+// QaShape); its waves take 64-column tiles round-robin, each prefetching its
+// next tile.  In a tile, lane l holds row l%16 of a block and the 16 columns
 // 16*(l/16) .. +15, which is also the A-operand layout of two
 // v_mfma_f32_16x16x32_bf16, so the smoothed bf16 values feed the MFMA
 // straight from registers; lora_down reaches the B operand through a
@@ -47,16 +47,21 @@ namespace svdq {
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-constexpr int QA_ROWS = 16;
 constexpr int QA_RCP = 72;  // fp64 slots of a wave's reciprocals of lambda (64 + padding)
 
-// Waves per 16-row workgroup: INT4 16 (four per SIMD, to keep more of X in
-// flight) unless the T partials of a large rank would not fit in LDS; FP4 8
-// (measured faster).
+// Rows and waves of a workgroup.  Ranks up to 32: one 16-row block, with
+// 16 waves for INT4 (four per SIMD, to keep more of X in flight) and 8 for
+// FP4 (measured faster).  Ranks 48..128 (not NVFP4): two 16-row blocks on
+// 8 waves, so that each lora_down slice a wave stages serves both blocks'
+// MFMAs: the whole K range of L1 streams through every workgroup, and at
+// rank 128 that stream, not X, bounds the pass.  Larger ranks: one block on
+// 8 waves (the T partials of two blocks would not fit in LDS).
 template <int MODE, int RB>
 struct QaShape {
-  static constexpr int kWaves = (MODE == 0 && RB <= 8) ? 16 : 8;
+  static constexpr int kBlocks = (MODE != 2 && RB > 2 && RB <= 8) ? 2 : 1;
+  static constexpr int kWaves = kBlocks == 2 ? 8 : ((MODE == 0 && RB <= 8) ? 16 : 8);
   static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = 16 * kBlocks;
 };
 
 // The fp64 reciprocals of a tile's 64 lambdas sit in LDS with 16 bytes of
@@ -85,7 +90,8 @@ template <int MODE, int RB>
 struct QaLds {
   static constexpr int kRcp = QaShape<MODE, RB>::kWaves * 2 * QA_RCP * 8;
   static constexpr int kStage = RB > 0 ? QaShape<MODE, RB>::kWaves * 2048 : 0;
-  static constexpr int kRed = QaShape<MODE, RB>::kWaves * (RB > 0 ? RB : 1) * 4 * 64 * 4;
+  static constexpr int kRed =
+      QaShape<MODE, RB>::kWaves * QaShape<MODE, RB>::kBlocks * (RB > 0 ? RB : 1) * 4 * 64 * 4;
   static constexpr int kBytes = kRcp + kStage > kRed ? kRcp + kStage : kRed;
 };
 
@@ -134,6 +140,8 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
     void* __restrict__ xscales, float* __restrict__ T, QaImage qi) {
   constexpr int QA_WAVES = QaShape<MODE, RB>::kWaves;
   constexpr int QA_THREADS = QaShape<MODE, RB>::kThreads;
+  constexpr int NB = QaShape<MODE, RB>::kBlocks;     // 16-row blocks of the workgroup
+  constexpr int QA_WROWS = QaShape<MODE, RB>::kRows;
   // lora_down slices loaded at the top of a tile (the rest when used)
   constexpr int QA_EARLY = QA_WAVES == 16 ? (RB <= 2 ? RB : 0) : (RB < 4 ? RB : 4);
   __shared__ __attribute__((aligned(16))) uint8_t smem[QaLds<MODE, RB>::kBytes];
@@ -149,20 +157,19 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   double* rlam = reinterpret_cast<double*>(smem) + wave * 2 * QA_RCP;
   const int r16 = lane & 15;
   const int j = lane >> 4;
-  const int64_t row = (int64_t)blockIdx.x * QA_ROWS + r16;
-  const bool row_ok = row < M;
-  const bool block_full = (int64_t)blockIdx.x * QA_ROWS + QA_ROWS <= M;
-  const int64_t irt = row >> 5;     // image row tile and lane slot of this row
-  const int irr = (int)(row & 31);
-  const uint16_t* xrow = X + (row_ok ? row : 0) * (int64_t)K;
+  // this lane's row in block 0 (block sb adds 16 sb)
+  const int64_t row0 = (int64_t)blockIdx.x * QA_WROWS + r16;
+  const bool block_full = (int64_t)blockIdx.x * QA_WROWS + QA_WROWS <= M;
   // this workgroup's K range: groups [G s / S, G (s + 1) / S)
   const int S = qi.S > 1 ? qi.S : 1;
   const int kbeg = (int)((int64_t)(K >> 6) * blockIdx.y / S) * 64;
   const int kend = (int)((int64_t)(K >> 6) * (blockIdx.y + 1) / S) * 64;
 
-  v4f tacc[RB > 0 ? RB : 1];
+  v4f tacc[NB][RB > 0 ? RB : 1];
 #pragma unroll
-  for (int b = 0; b < (RB > 0 ? RB : 1); ++b) tacc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int sb = 0; sb < NB; ++sb)
+#pragma unroll
+    for (int b = 0; b < (RB > 0 ? RB : 1); ++b) tacc[sb][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // The waves run independently until the T partials are summed: each takes
   // its tiles of this workgroup's K range round-robin, prefetching the next
@@ -173,19 +180,21 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
     // Loads of a tile without a branch (rows past M and tiles past the range
     // read a valid place; the flag zeroes them when the tile is used), so
     // that the compiler's wait counts stay exact across the loop.
-    auto load_x = [&](int t, v4u& xa, v4u& xb, bool& ok) {
-      ok = row_ok && t < ntiles;
+    auto load_x = [&](int sb, int t, v4u& xa, v4u& xb, bool& ok) {
+      const int64_t rw = row0 + 16 * sb;
+      ok = rw < M && t < ntiles;
       const int tc = t < ntiles ? t : ntiles - 1;
-      const uint16_t* p = xrow + kbeg + tc * 64 + j * 16;
+      const uint16_t* p = X + (rw < M ? rw : 0) * (int64_t)K + kbeg + tc * 64 + j * 16;
       xa = *reinterpret_cast<const v4u*>(p);
       xb = *reinterpret_cast<const v4u*>(p + 8);
     };
     auto load_lam = [&](int t) { return lambda[kbeg + (t < ntiles ? t : ntiles - 1) * 64 + lane]; };
     // lambda first: waiting for it does not wait for the X loads behind it
     float nlam = load_lam(wave);
-    v4u na, nb;
-    bool nok;
-    load_x(wave, na, nb, nok);
+    v4u na[NB], nb[NB];
+    bool nok[NB];
+#pragma unroll
+    for (int sb = 0; sb < NB; ++sb) load_x(sb, wave, na[sb], nb[sb], nok[sb]);
     // the first tile's reciprocals of lambda (column t*64 + lane of the range)
     rlam[rl_idx(lane)] = 1.0 / (double)nlam;
     int slot = 0;
@@ -193,13 +202,18 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
       const double* rcur = rlam + slot * QA_RCP;
       __builtin_amdgcn_wave_barrier();
       nlam = load_lam(t + QA_WAVES);  // the next tile's, made into reciprocals at the end
-      v4u xa = na, xb = nb;
-      if (!block_full) {  // rows past M read as zeros (uniform: most blocks skip it)
-        const v4u zero4 = v4u{0u, 0u, 0u, 0u};
-        xa = nok ? na : zero4;
-        xb = nok ? nb : zero4;
+      uint32_t xwb[NB][8];
+#pragma unroll
+      for (int sb = 0; sb < NB; ++sb) {
+        v4u xa = na[sb], xb = nb[sb];
+        if (!block_full) {  // rows past M read as zeros (uniform: most blocks skip it)
+          const v4u zero4 = v4u{0u, 0u, 0u, 0u};
+          xa = nok[sb] ? na[sb] : zero4;
+          xb = nok[sb] ? nb[sb] : zero4;
+        }
+        xwb[sb][0] = xa[0]; xwb[sb][1] = xa[1]; xwb[sb][2] = xa[2]; xwb[sb][3] = xa[3];
+        xwb[sb][4] = xb[0]; xwb[sb][5] = xb[1]; xwb[sb][6] = xb[2]; xwb[sb][7] = xb[3];
       }
-      uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
       // This tile's lora_down columns, read as whole 128-byte row segments:
       // load h of slice b gives lane L row b*16 + 8h + L/8 and its 16-byte
       // chunk L%8, so each load covers 8 cache lines in full.  (In the MFMA
@@ -217,188 +231,198 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         lg[b][0] = load_l1(b, 0);
         lg[b][1] = load_l1(b, 1);
       }
-      load_x(t + QA_WAVES, na, nb, nok);  // next tile of this wave
-      if constexpr (GELU) {
-        // GELU of the 16 inputs from the wide band table, two at a time with
-        // packed 16-bit index arithmetic: the offset into the band, clamped
-        // to the sentinel for inputs outside it, plus the sign's half.  The
-        // rare out-of-band inputs are redone by the rules, on a branch that
-        // the whole wave skips when none of its inputs needs it.
-        using namespace gelu_table;
-        const us2 lo_off = us2{(unsigned short)(kWLoExp * 128), (unsigned short)(kWLoExp * 128)};
-        const us2 sent = us2{(unsigned short)(kWBand * 128), (unsigned short)(kWBand * 128)};
-        const us2 half_sz = us2{(unsigned short)kWHalf, (unsigned short)kWHalf};
-        uint32_t xin[8];
-        us2 worst = us2{0, 0};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          xin[i] = xw[i];
-          const us2 off = __builtin_elementwise_min(
-              __builtin_bit_cast(us2, xw[i] & 0x7FFF7FFFu) - lo_off, sent);
-          worst = __builtin_elementwise_max(worst, off);
-          const us2 idx = off + __builtin_bit_cast(us2, (xw[i] >> 15) & 0x00010001u) * half_sz;
-          xw[i] = (uint32_t)gtab[idx[0]] | ((uint32_t)gtab[idx[1]] << 16);
-        }
-        if (__any((worst[0] == sent[0]) | (worst[1] == sent[1]))) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const uint32_t b = (xin[i] >> (16 * h)) & 0xFFFFu;
-              const uint32_t e = (b >> 7) & 0xFFu;
-              if (e < (uint32_t)kWLoExp || e > (uint32_t)kWHiExp)
-                xw[i] = (xw[i] & (0xFFFF0000u >> (16 * h))) | (gelu_rule(b) << (16 * h));
-            }
-        }
-      }
+      for (int sb = 0; sb < NB; ++sb) load_x(sb, t + QA_WAVES, na[sb], nb[sb], nok[sb]);  // next tile
       const int kl = j * 16;                // column within the tile
       const int k0 = kbeg + t * 64 + kl;  // column within the row
 
-      // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
-      uint32_t hpk[8];  // X_hat as packed bf16 pairs (the T MFMA's A operand)
-      float xh[16];
-      // largest |x_hat| of the lane as bf16 bits: for finite values the
-      // order of the magnitudes is that of their bit patterns with the sign
-      // cleared, so a packed 16-bit integer maximum serves
-      us2 am2 = us2{0, 0};
+      // X_hat as packed bf16 pairs, per block (the T MFMA's A operands)
+      uint32_t hpk[NB][8];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float q[2];
+      for (int sb = 0; sb < NB; ++sb) {
+        uint32_t* xw = xwb[sb];
+        const int64_t row = row0 + 16 * sb;
+        const bool row_ok = row < M;
+        const int64_t irt = row >> 5;  // image row tile and lane slot of this row
+        const int irr = (int)(row & 31);
+        if constexpr (GELU) {
+          // GELU of the 16 inputs from the wide band table, two at a time with
+          // packed 16-bit index arithmetic: the offset into the band, clamped
+          // to the sentinel for inputs outside it, plus the sign's half.  The
+          // rare out-of-band inputs are redone by the rules, on a branch that
+          // the whole wave skips when none of its inputs needs it.
+          using namespace gelu_table;
+          const us2 lo_off = us2{(unsigned short)(kWLoExp * 128), (unsigned short)(kWLoExp * 128)};
+          const us2 sent = us2{(unsigned short)(kWBand * 128), (unsigned short)(kWBand * 128)};
+          const us2 half_sz = us2{(unsigned short)kWHalf, (unsigned short)kWHalf};
+          uint32_t xin[8];
+          us2 worst = us2{0, 0};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t xbits = (xw[i >> 1] >> (e * 16)) & 0xFFFFu;
-          q[e] = (float)((double)bf16_to_f32(xbits) * rcur[rl_idx(kl + i + e)]);
+          for (int i = 0; i < 8; ++i) {
+            xin[i] = xw[i];
+            const us2 off = __builtin_elementwise_min(
+                __builtin_bit_cast(us2, xw[i] & 0x7FFF7FFFu) - lo_off, sent);
+            worst = __builtin_elementwise_max(worst, off);
+            const us2 idx = off + __builtin_bit_cast(us2, (xw[i] >> 15) & 0x00010001u) * half_sz;
+            xw[i] = (uint32_t)gtab[idx[0]] | ((uint32_t)gtab[idx[1]] << 16);
+          }
+          if (__any((worst[0] == sent[0]) | (worst[1] == sent[1]))) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const uint32_t b = (xin[i] >> (16 * h)) & 0xFFFFu;
+                const uint32_t e = (b >> 7) & 0xFFu;
+                if (e < (uint32_t)kWLoExp || e > (uint32_t)kWHiExp)
+                  xw[i] = (xw[i] & (0xFFFF0000u >> (16 * h))) | (gelu_rule(b) << (16 * h));
+              }
+          }
         }
-        // RNE to bf16 (v_cvt_pk_bf16_f32: the same rounding as the
-        // bit-level definition for every finite value)
-        const v2f qv = {q[0], q[1]};
-        const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(qv, v2bf));
-        hpk[i >> 1] = pk;
-        xh[i] = __uint_as_float(pk << 16);
-        xh[i + 1] = __uint_as_float(pk & 0xFFFF0000u);
-        am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(us2, pk & 0x7FFF7FFFu));
-      }
-      uint32_t amb = am2[0] > am2[1] ? am2[0] : am2[1];
+        // X_hat = bf16_RNE(fp32(X / lambda)), kept as bf16 bits and as fp32.
+        float xh[16];
+        // largest |x_hat| of the lane as bf16 bits: for finite values the
+        // order of the magnitudes is that of their bit patterns with the sign
+        // cleared, so a packed 16-bit integer maximum serves
+        us2 am2 = us2{0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          float q[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t xbits = (xw[i >> 1] >> (e * 16)) & 0xFFFFu;
+            q[e] = (float)((double)bf16_to_f32(xbits) * rcur[rl_idx(kl + i + e)]);
+          }
+          // RNE to bf16 (v_cvt_pk_bf16_f32: the same rounding as the
+          // bit-level definition for every finite value)
+          const v2f qv = {q[0], q[1]};
+          const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(qv, v2bf));
+          hpk[sb][i >> 1] = pk;
+          xh[i] = __uint_as_float(pk << 16);
+          xh[i + 1] = __uint_as_float(pk & 0xFFFF0000u);
+          am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(us2, pk & 0x7FFF7FFFu));
+        }
+        uint32_t amb = am2[0] > am2[1] ? am2[0] : am2[1];
 
-      if constexpr (CODES) {
-        if constexpr (MODE == 0) {
-          // INT4: group of 64 = the four lanes sharing this row.
-          amb = max_xor32(max_xor16(amb));
-          const float amax = __uint_as_float(amb << 16);
-          // s = fp32(amax / 7), exactly: amax is a bf16 value, so the fp64
-          // product with the correctly rounded fp64 1/7 rounds to it (the
-          // exact-quotient note above)
-          const float s = (float)((double)amax * (1.0 / 7.0));
-          // cq = fp32(xh / s); the code is rint_even(clamp(cq, -8, 7)).  The
-          // clamp never acts: |cq| <= amax / s, and s is within a relative
-          // 2^-24 of amax / 7 when normal, and within 2^-150 / (2^-133 / 7)
-          // < 2^-14 when subnormal (a nonzero bf16 amax is at least 2^-133),
-          // so |cq| < 7.0004 and its rounding lies in [-7, 7] either way.
-          // 1/s need not be correctly rounded here: a reciprocal within a
-          // relative 2^-50 keeps fp32(xh * (1/s)) = fp32(xh / s) wherever the
-          // quotient is a normal fp32 value (the margin is about 2^-48), and a
-          // quotient in the subnormal range gives code 0 either way.  So the
-          // hardware reciprocal with two Newton steps serves (each step
-          // squares its relative error).  An all-zero group (s = 0) takes
-          // 1/s = 0: codes 0.
-          const double sd = (double)s;
-          double rs = __builtin_amdgcn_rcp(sd);
-          rs = __builtin_fma(rs, __builtin_fma(-sd, rs, 1.0), rs);
-          rs = __builtin_fma(rs, __builtin_fma(-sd, rs, 1.0), rs);
-          rs = s != 0.f ? rs : 0.0;
-          float cq[16];
+        if constexpr (CODES) {
+          if constexpr (MODE == 0) {
+            // INT4: group of 64 = the four lanes sharing this row.
+            amb = max_xor32(max_xor16(amb));
+            const float amax = __uint_as_float(amb << 16);
+            // s = fp32(amax / 7), exactly: amax is a bf16 value, so the fp64
+            // product with the correctly rounded fp64 1/7 rounds to it (the
+            // exact-quotient note above)
+            const float s = (float)((double)amax * (1.0 / 7.0));
+            // cq = fp32(xh / s); the code is rint_even(clamp(cq, -8, 7)).  The
+            // clamp never acts: |cq| <= amax / s, and s is within a relative
+            // 2^-24 of amax / 7 when normal, and within 2^-150 / (2^-133 / 7)
+            // < 2^-14 when subnormal (a nonzero bf16 amax is at least 2^-133),
+            // so |cq| < 7.0004 and its rounding lies in [-7, 7] either way.
+            // 1/s need not be correctly rounded here: a reciprocal within a
+            // relative 2^-50 keeps fp32(xh * (1/s)) = fp32(xh / s) wherever the
+            // quotient is a normal fp32 value (the margin is about 2^-48), and a
+            // quotient in the subnormal range gives code 0 either way.  So the
+            // hardware reciprocal with two Newton steps serves (each step
+            // squares its relative error).  An all-zero group (s = 0) takes
+            // 1/s = 0: codes 0.
+            const double sd = (double)s;
+            double rs = __builtin_amdgcn_rcp(sd);
+            rs = __builtin_fma(rs, __builtin_fma(-sd, rs, 1.0), rs);
+            rs = __builtin_fma(rs, __builtin_fma(-sd, rs, 1.0), rs);
+            rs = s != 0.f ? rs : 0.0;
+            float cq[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) cq[i] = (float)((double)xh[i] * rs);
-          if (xcodes != nullptr && row_ok) {
-            uint32_t w0 = 0, w1 = 0;
+            for (int i = 0; i < 16; ++i) cq[i] = (float)((double)xh[i] * rs);
+            if (xcodes != nullptr && row_ok) {
+              uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              w0 |= ((uint32_t)(int)__builtin_rintf(cq[i]) & 0xFu) << (4 * i);
-              w1 |= ((uint32_t)(int)__builtin_rintf(cq[8 + i]) & 0xFu) << (4 * i);
+              for (int i = 0; i < 8; ++i) {
+                w0 |= ((uint32_t)(int)__builtin_rintf(cq[i]) & 0xFu) << (4 * i);
+                w1 |= ((uint32_t)(int)__builtin_rintf(cq[8 + i]) & 0xFu) << (4 * i);
+              }
+              *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
+              if (j == 0) reinterpret_cast<float*>(xscales)[row * (int64_t)(K >> 6) + (k0 >> 6)] = s;
             }
-            *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
-            if (j == 0) reinterpret_cast<float*>(xscales)[row * (int64_t)(K >> 6) + (k0 >> 6)] = s;
-          }
-          if (qi.img != nullptr) {
-            // this lane's 16 fields are fields 0..15 (j even) or 16..31 (j odd)
-            // of K half j/2 of group k0/64: an 8-byte and a 4-byte store,
-            // chosen without a branch
-            uint8_t* blk = qi.img + ((int64_t)(k0 >> 6) * qi.RT + irt) * I4_BLOCK;
-            uint8_t* half = blk + (j >> 1) * 768;
-            uint32_t d0, d1, d2;
-            fp6_fields16_hw(cq, d0, d1, d2);
-            const bool ev = (j & 1) == 0;
-            *reinterpret_cast<v2u*>(half + (ev ? 16 * irr : 512 + 8 * irr)) = ev ? v2u{d0, d1} : v2u{d1, d2};
-            *reinterpret_cast<uint32_t*>(half + 16 * irr + (ev ? 8 : 12)) = ev ? d2 : d0;
-            // scale operand, X pattern: slot irr {hi | lo << 16, hi}, slot
-            // 32 + irr {lo, 0}; lanes j = 2, 3 store the same bytes as j = 0, 1
-            const uint32_t hb = f32_to_bf16(s);
-            const uint32_t lb = f32_to_bf16(s - bf16_to_f32(hb));
-            const v2u so = ev ? v2u{hb | (lb << 16), hb} : v2u{lb, 0u};
-            *reinterpret_cast<v2u*>(blk + 1536 + 8 * (32 * (j & 1) + irr)) = so;
-          }
-        } else if constexpr (MODE == 1) {
-          // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
-          amb = max_xor16(amb);
-          const float amax = __uint_as_float(amb << 16);
-          const int e = e8m0_exponent(amax);
-          uint32_t w0 = 0, w1 = 0;
-          if (e >= -100) {
-            // the gfx950 conversion: E2M1 nearest-even of x * 2^-e (the
-            // exponent of the scale operand), saturating at 6, sign kept
-            const float sc = exp2i(e);
-            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[0], xh[1], sc, 0);
-            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[2], xh[3], sc, 1);
-            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[4], xh[5], sc, 2);
-            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[6], xh[7], sc, 3);
-            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[8], xh[9], sc, 0);
-            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[10], xh[11], sc, 1);
-            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[12], xh[13], sc, 2);
-            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[14], xh[15], sc, 3);
+            if (qi.img != nullptr) {
+              // this lane's 16 fields are fields 0..15 (j even) or 16..31 (j odd)
+              // of K half j/2 of group k0/64: an 8-byte and a 4-byte store,
+              // chosen without a branch
+              uint8_t* blk = qi.img + ((int64_t)(k0 >> 6) * qi.RT + irt) * I4_BLOCK;
+              uint8_t* half = blk + (j >> 1) * 768;
+              uint32_t d0, d1, d2;
+              fp6_fields16_hw(cq, d0, d1, d2);
+              const bool ev = (j & 1) == 0;
+              *reinterpret_cast<v2u*>(half + (ev ? 16 * irr : 512 + 8 * irr)) = ev ? v2u{d0, d1} : v2u{d1, d2};
+              *reinterpret_cast<uint32_t*>(half + 16 * irr + (ev ? 8 : 12)) = ev ? d2 : d0;
+              // scale operand, X pattern: slot irr {hi | lo << 16, hi}, slot
+              // 32 + irr {lo, 0}; lanes j = 2, 3 store the same bytes as j = 0, 1
+              const uint32_t hb = f32_to_bf16(s);
+              const uint32_t lb = f32_to_bf16(s - bf16_to_f32(hb));
+              const v2u so = ev ? v2u{hb | (lb << 16), hb} : v2u{lb, 0u};
+              *reinterpret_cast<v2u*>(blk + 1536 + 8 * (32 * (j & 1) + irr)) = so;
+            }
+          } else if constexpr (MODE == 1) {
+            // FP4: block of 32 = lane pairs (j = 0,1) and (j = 2,3).
+            amb = max_xor16(amb);
+            const float amax = __uint_as_float(amb << 16);
+            const int e = e8m0_exponent(amax);
+            uint32_t w0 = 0, w1 = 0;
+            if (e >= -100) {
+              // the gfx950 conversion: E2M1 nearest-even of x * 2^-e (the
+              // exponent of the scale operand), saturating at 6, sign kept
+              const float sc = exp2i(e);
+              w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[0], xh[1], sc, 0);
+              w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[2], xh[3], sc, 1);
+              w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[4], xh[5], sc, 2);
+              w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[6], xh[7], sc, 3);
+              w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[8], xh[9], sc, 0);
+              w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[10], xh[11], sc, 1);
+              w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[12], xh[13], sc, 2);
+              w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[14], xh[15], sc, 3);
+            } else {
+              // blocks whose maximum is below 2^-98: the scaled values can come
+              // from fp32 subnormals, whose handling by the conversion is not
+              // relied on
+              const float sc = exp2i(-e);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) w0 |= e2m1_code(xh[i] * sc) << (4 * i);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) w1 |= e2m1_code(xh[8 + i] * sc) << (4 * i);
+            }
+            if (xcodes != nullptr && row_ok) {
+              *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
+              if ((j & 1) == 0)
+                reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 5) + (k0 >> 5)] =
+                    (uint8_t)(e + 127);
+            }
+            if (qi.img != nullptr) {
+              // lane slot 32 h + row of the (group, row tile) block, h = j/2
+              const int64_t b = (int64_t)(k0 >> 6) * qi.RT + irt;
+              const int slot = 32 * (j >> 1) + irr;
+              *reinterpret_cast<v2u*>(qi.img + b * F4_CBLOCK + 16 * slot + 8 * (j & 1)) = v2u{w0, w1};
+              // both lanes of the pair store the block's scale byte (the same)
+              qi.img[qi.scale + b * F4_SBLOCK + slot] = (uint8_t)(e + 127);
+            }
           } else {
-            // blocks whose maximum is below 2^-98: the scaled values can come
-            // from fp32 subnormals, whose handling by the conversion is not
-            // relied on
-            const float sc = exp2i(-e);
+            // NVFP4: this lane's 16 elements are one block.  s =
+            // E4M3_RNE_sat(fp32(amax / fp32(6 g))), d = fp32(s g), codes of
+            // fp32(x_hat / d); the quotient comes from d's fp64 reciprocal,
+            // exact for a bf16 numerator as x / lambda above.
+            const float g = *qi.g;
+            const float amax = __uint_as_float(amb << 16);
+            const uint32_t sbits = e4m3_encode(amax / __fmul_rn(6.0f, g));
+            const float sv = e4m3_value(sbits);
+            uint32_t w0 = 0, w1 = 0;
+            if (sv > 0.f) {
+              const double rd = 1.0 / (double)__fmul_rn(sv, g);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w0 |= e2m1_code(xh[i] * sc) << (4 * i);
+              for (int i = 0; i < 8; ++i) w0 |= e2m1_code((float)((double)xh[i] * rd)) << (4 * i);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w1 |= e2m1_code(xh[8 + i] * sc) << (4 * i);
-          }
-          if (xcodes != nullptr && row_ok) {
-            *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
-            if ((j & 1) == 0)
-              reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 5) + (k0 >> 5)] =
-                  (uint8_t)(e + 127);
-          }
-          if (qi.img != nullptr) {
-            // lane slot 32 h + row of the (group, row tile) block, h = j/2
-            const int64_t b = (int64_t)(k0 >> 6) * qi.RT + irt;
-            const int slot = 32 * (j >> 1) + irr;
-            *reinterpret_cast<v2u*>(qi.img + b * F4_CBLOCK + 16 * slot + 8 * (j & 1)) = v2u{w0, w1};
-            // both lanes of the pair store the block's scale byte (the same)
-            qi.img[qi.scale + b * F4_SBLOCK + slot] = (uint8_t)(e + 127);
-          }
-        } else {
-          // NVFP4: this lane's 16 elements are one block.  s =
-          // E4M3_RNE_sat(fp32(amax / fp32(6 g))), d = fp32(s g), codes of
-          // fp32(x_hat / d); the quotient comes from d's fp64 reciprocal,
-          // exact for a bf16 numerator as x / lambda above.
-          const float g = *qi.g;
-          const float amax = __uint_as_float(amb << 16);
-          const uint32_t sb = e4m3_encode(amax / __fmul_rn(6.0f, g));
-          const float sv = e4m3_value(sb);
-          uint32_t w0 = 0, w1 = 0;
-          if (sv > 0.f) {
-            const double rd = 1.0 / (double)__fmul_rn(sv, g);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w0 |= e2m1_code((float)((double)xh[i] * rd)) << (4 * i);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w1 |= e2m1_code((float)((double)xh[8 + i] * rd)) << (4 * i);
-          }
-          if (xcodes != nullptr && row_ok) {
-            *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
-            reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 4) + (k0 >> 4)] = (uint8_t)sb;
+              for (int i = 0; i < 8; ++i) w1 |= e2m1_code((float)((double)xh[8 + i] * rd)) << (4 * i);
+            }
+            if (xcodes != nullptr && row_ok) {
+              *reinterpret_cast<v2u*>(xcodes + row * (int64_t)(K >> 1) + (k0 >> 1)) = v2u{w0, w1};
+              reinterpret_cast<uint8_t*>(xscales)[row * (int64_t)(K >> 4) + (k0 >> 4)] = (uint8_t)sbits;
+            }
           }
         }
       }
@@ -412,8 +436,12 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         // T += X_hat[16 rows, 64 cols] . L1[64 cols, 16*RB]: element i of
         // this lane is column k0 + i; the B operand takes the same columns of
         // lora_down (= L1^T) rows.
-        const v8bf a0 = __builtin_bit_cast(v8bf, v4u{hpk[0], hpk[1], hpk[2], hpk[3]});
-        const v8bf a1 = __builtin_bit_cast(v8bf, v4u{hpk[4], hpk[5], hpk[6], hpk[7]});
+        v8bf a0[NB], a1[NB];
+#pragma unroll
+        for (int sb = 0; sb < NB; ++sb) {
+          a0[sb] = __builtin_bit_cast(v8bf, v4u{hpk[sb][0], hpk[sb][1], hpk[sb][2], hpk[sb][3]});
+          a1[sb] = __builtin_bit_cast(v8bf, v4u{hpk[sb][4], hpk[sb][5], hpk[sb][6], hpk[sb][7]});
+        }
         // Each slice goes through this wave's staging buffer, 16 rows of 128
         // bytes whose 16-byte chunk c of row n sits at position c ^ (n % 8),
         // so that both the row-segment writes and the operand reads (lane l:
@@ -435,8 +463,11 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
           const v8bf b0 = *reinterpret_cast<const v8bf*>(stg + rd0);
           const v8bf b1 = *reinterpret_cast<const v8bf*>(stg + rd1);
           __builtin_amdgcn_wave_barrier();
-          tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, tacc[b], 0, 0, 0);
-          tacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, tacc[b], 0, 0, 0);
+#pragma unroll
+          for (int sb = 0; sb < NB; ++sb) {
+            tacc[sb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[sb], b0, tacc[sb][b], 0, 0, 0);
+            tacc[sb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[sb], b1, tacc[sb][b], 0, 0, 0);
+          }
         }
       }
     }
@@ -445,39 +476,43 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
   if constexpr (RB > 0) {
     // Sum the waves' partial T tiles through LDS, wave 0 first.
     __syncthreads();  // every wave is done with its LDS slots
-    float(*red)[RB][4][64] = reinterpret_cast<float(*)[RB][4][64]>(smem);
+    float(*red)[NB][RB][4][64] = reinterpret_cast<float(*)[NB][RB][4][64]>(smem);
 #pragma unroll
-    for (int b = 0; b < RB; ++b)
+    for (int sb = 0; sb < NB; ++sb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) red[wave][b][q][lane] = tacc[b][q];
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[wave][sb][b][q][lane] = tacc[sb][b][q];
     __syncthreads();
     // Four consecutive entries of the wave-0 tile per thread take the sum
     // over the waves in place (each entry is read and written by its own
     // thread alone), all loads in flight at once.
-    for (int f = 4 * threadIdx.x; f < RB * 256; f += 4 * QA_THREADS) {
+    for (int f = 4 * threadIdx.x; f < NB * RB * 256; f += 4 * QA_THREADS) {
       v4f part[QA_WAVES];
 #pragma unroll
-      for (int w = 0; w < QA_WAVES; ++w) part[w] = *reinterpret_cast<const v4f*>(&red[w][0][0][0] + f);
+      for (int w = 0; w < QA_WAVES; ++w)
+        part[w] = *reinterpret_cast<const v4f*>(&red[w][0][0][0][0] + f);
       v4f acc = part[0];
 #pragma unroll
       for (int w = 1; w < QA_WAVES; ++w)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] += part[w][i];
-      *reinterpret_cast<v4f*>(&red[0][0][0][0] + f) = acc;
+      *reinterpret_cast<v4f*>(&red[0][0][0][0][0] + f) = acc;
     }
     __syncthreads();
     // One thread per (row, 8 consecutive ranks): the 8 sums of a row and
     // rank chunk are 8 consecutive lanes of one MFMA output register (lane
     // l, element q -> row 4 (l/16) + q, column l%16).
     const int rank = RB * 16;
-    for (int idx = threadIdx.x; idx < QA_ROWS * (rank / 8); idx += QA_THREADS) {
-      const int mr = idx / (rank / 8);
+    for (int idx = threadIdx.x; idx < QA_WROWS * (rank / 8); idx += QA_THREADS) {
+      const int mr = idx / (rank / 8);  // row of the workgroup
       const int c8 = idx - mr * (rank / 8);
-      const int b = c8 >> 1, q = mr & 3, l0 = 16 * (mr >> 2) + 8 * (c8 & 1);
+      const int sb = mr >> 4, m16 = mr & 15;
+      const int b = c8 >> 1, q = m16 & 3, l0 = 16 * (m16 >> 2) + 8 * (c8 & 1);
       float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = red[0][b][q][l0 + i];
-      const int64_t m = (int64_t)blockIdx.x * QA_ROWS + mr;
+      for (int i = 0; i < 8; ++i) v[i] = red[0][sb][b][q][l0 + i];
+      const int64_t m = (int64_t)blockIdx.x * QA_WROWS + mr;
       if (S > 1) {
         // partial sums of K range blockIdx.y, added by split_t_kernel
         float* tp = reinterpret_cast<float*>(qi.img + qi.tpart) +
@@ -552,14 +587,18 @@ __global__ __launch_bounds__(256) void split_t_kernel(int64_t M, int rank, float
   *reinterpret_cast<v4u*>(blk + 1024 + 16 * slot) = v4u{lo[0], lo[1], lo[2], lo[3]};
 }
 
+// rows: the rows the grid covers (M, or the image's padded rows); gy: the K
+// ranges.
 template <int MODE, bool CODES, bool GELU>
-static hipError_t launch_qa_rank(int rb, dim3 grid, hipStream_t s, int64_t M, int K,
-                                 const uint16_t* X, const float* lam, const uint16_t* ld,
+static hipError_t launch_qa_rank(int rb, int64_t rows, unsigned gy, hipStream_t s, int64_t M,
+                                 int K, const uint16_t* X, const float* lam, const uint16_t* ld,
                                  uint8_t* xc, void* xs, float* T, QaImage qi) {
-#define SVDQ_QA_CASE(R)                                                                   \
-  case R:                                                                                 \
-    hipLaunchKernelGGL((quantize_act_kernel<MODE, R, CODES, GELU>), grid, dim3(QaShape<MODE, R>::kThreads), 0, \
-                       s, M, K, X, lam, ld, xc, xs, T, qi);                               \
+#define SVDQ_QA_CASE(R)                                                                      \
+  case R:                                                                                    \
+    hipLaunchKernelGGL((quantize_act_kernel<MODE, R, CODES, GELU>),                          \
+                       dim3((unsigned)((rows + QaShape<MODE, R>::kRows - 1) /                \
+                                       QaShape<MODE, R>::kRows), gy),                        \
+                       dim3(QaShape<MODE, R>::kThreads), 0, s, M, K, X, lam, ld, xc, xs, T, qi); \
     break;
   switch (rb) {
     SVDQ_QA_CASE(0) SVDQ_QA_CASE(1) SVDQ_QA_CASE(2) SVDQ_QA_CASE(3) SVDQ_QA_CASE(4)
@@ -578,8 +617,7 @@ hipError_t launch_nvfp4_quantize_act(int64_t M, int K, int rank, const uint16_t*
                                      const uint16_t* lora_down, uint8_t* xcodes, uint8_t* xscales,
                                      float* T, hipStream_t s) {
   QaImage qi{nullptr, 0, 0, 0, 0, 1, g};
-  const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
-  return launch_qa_rank<2, true, false>(lora_down ? rank / 16 : 0, grid, s, M, K, X, lambda,
+  return launch_qa_rank<2, true, false>(lora_down ? rank / 16 : 0, M, 1, s, M, K, X, lambda,
                                         lora_down, xcodes, xscales, T, qi);
 }
 
@@ -599,17 +637,17 @@ hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint1
     rows = a.RT * 32;  // cover the padding rows too
   }
   const int rb = lora_down ? rank / 16 : 0;
-  const dim3 grid((unsigned)((rows + QA_ROWS - 1) / QA_ROWS), (unsigned)qi.S);
+  const unsigned gy = (unsigned)qi.S;
   hipError_t e;
   if (mode == 0)
-    e = gelu ? launch_qa_rank<0, true, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+    e = gelu ? launch_qa_rank<0, true, true>(rb, rows, gy, s, M, K, X, lambda, lora_down, xcodes,
                                              xscales, T, qi)
-             : launch_qa_rank<0, true, false>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+             : launch_qa_rank<0, true, false>(rb, rows, gy, s, M, K, X, lambda, lora_down, xcodes,
                                               xscales, T, qi);
   else
-    e = gelu ? launch_qa_rank<1, true, true>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+    e = gelu ? launch_qa_rank<1, true, true>(rb, rows, gy, s, M, K, X, lambda, lora_down, xcodes,
                                              xscales, T, qi)
-             : launch_qa_rank<1, true, false>(rb, grid, s, M, K, X, lambda, lora_down, xcodes,
+             : launch_qa_rank<1, true, false>(rb, rows, gy, s, M, K, X, lambda, lora_down, xcodes,
                                               xscales, T, qi);
   if (e != hipSuccess || rb == 0 || qi.S <= 1) return e;
   const int64_t n = qi.RT * 32 * (rank / 8);
@@ -621,11 +659,10 @@ hipError_t launch_quantize_act(int mode, int rank, int64_t M, int K, const uint1
 hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down, float* T,
                                bool gelu, hipStream_t s) {
-  const dim3 grid((unsigned)((M + QA_ROWS - 1) / QA_ROWS));
   const QaImage qi{nullptr, 0, 0, 0, 0, 1};
-  return gelu ? launch_qa_rank<0, false, true>(rank / 16, grid, s, M, K, X, lambda, lora_down,
+  return gelu ? launch_qa_rank<0, false, true>(rank / 16, M, 1, s, M, K, X, lambda, lora_down,
                                                nullptr, nullptr, T, qi)
-              : launch_qa_rank<0, false, false>(rank / 16, grid, s, M, K, X, lambda, lora_down,
+              : launch_qa_rank<0, false, false>(rank / 16, M, 1, s, M, K, X, lambda, lora_down,
                                                 nullptr, nullptr, T, qi);
 }
 

@@ -70,6 +70,17 @@ def test_ranks(mode, rank):
     _full_check(WL.TINY, mode, M=96, rank=rank, seed=rank)
 
 
+# Ranks 48..128 run the activation pass on 32-row workgroups: rows past M
+# inside the second 16-row block, and 96 groups of K, which the pass splits
+# into two K ranges whose partial T sums a second pass adds.
+@pytest.mark.parametrize("mode", ["int4", "fp4"])
+@pytest.mark.parametrize("M,rank", [(17, 64), (40, 96), (300, 128)])
+def test_large_rank_ragged_split(mode, M, rank):
+    spec = WL.LinearSpec(f"lr_{M}x6144x256_r{rank}", M, 6144, 256, rank, mode, x_outliers=4,
+                         x_factor=20.0)
+    _full_check(spec, mode, seed=M + rank)
+
+
 # short K (few code stages per tile) with more output tiles than workgroups,
 # so that workgroups walk several tiles and the DMA stream crosses tile
 # boundaries from the pre-stages and the first code groups; 300 tiles take
