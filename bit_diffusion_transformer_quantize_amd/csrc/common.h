@@ -18,6 +18,19 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
+// v_mfma_scale_f32_32x32x64_f8f6f4 with each operand as wide as its format
+// reads: 4 registers of E2M1 codes, 6 of E2M3.  clang's builtin takes 8 for
+// every format, so a narrower fragment would be padded with registers the
+// instruction never reads; the LLVM intrinsic is overloaded on the operand
+// width.  Arguments: A, B, C, format of A, format of B, A scale selector,
+// A scales (E8M0, one byte per lane), B scale selector, B scales.
+extern "C" __device__ v16f svdq_mfma_scale_e2m1(v4i a, v4i b, v16f c, int fmt_a, int fmt_b,
+                                                int sel_a, int scale_a, int sel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v4i32");
+extern "C" __device__ v16f svdq_mfma_scale_e2m3(v6i a, v6i b, v16f c, int fmt_a, int fmt_b,
+                                                int sel_a, int scale_a, int sel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
+
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);

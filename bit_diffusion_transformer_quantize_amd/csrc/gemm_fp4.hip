@@ -236,7 +236,7 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   const int fb = 8 * F4_CBLOCK + (wn * 4) * F4_CBLOCK + lane * 16;
   const int fsb = F4_WS + (wn * 4) * F4_SBLOCK + lane;
   struct Frags {
-    v8i a[2], b[4];
+    v4i a[2], b[4];
     int sa[2], sb[4];
   };
   // fragments of group gh (0, 1) of the stage at position q
@@ -245,13 +245,13 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr) {
       const v4u x = *reinterpret_cast<const v4u*>(sp + fa + tr * F4_CBLOCK);
-      f.a[tr] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+      f.a[tr] = v4i{(int)x[0], (int)x[1], (int)x[2], (int)x[3]};
       f.sa[tr] = sp[fsa + tr * F4_SBLOCK];
     }
 #pragma unroll
     for (int tc = 0; tc < 4; ++tc) {
       const v4u x = *reinterpret_cast<const v4u*>(sp + fb + tc * F4_CBLOCK);
-      f.b[tc] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+      f.b[tc] = v4i{(int)x[0], (int)x[1], (int)x[2], (int)x[3]};
       f.sb[tc] = sp[fsb + tc * F4_SBLOCK];
     }
   };
@@ -262,8 +262,8 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int tc = 0; tc < 4; ++tc)
-        acc[tr][tc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            f.b[tc], f.a[tr], acc[tr][tc], FP4_FMT, FP4_FMT, 0, f.sb[tc], 0, f.sa[tr]);
+        acc[tr][tc] = svdq_mfma_scale_e2m1(f.b[tc], f.a[tr], acc[tr][tc], FP4_FMT, FP4_FMT, 0,
+                                           f.sb[tc], 0, f.sa[tr]);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -287,14 +287,18 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
   // slot, group 2s+1 (f1) the second; with NEXT the next stage's wait,
   // barrier and DMA issue sit between them (GEN: the DMA issued, position
   // q + 3, is not a code stage of this tile and takes the generic form)
-  auto code_stage = [&](int q, int s, auto next_tag, auto gen_tag) {
+  // (BODY: a stage past the tile's fourth position, whose wait needs no
+  // branch, so that the loop over such stages is one basic block)
+  auto code_stage = [&](int q, int s, auto next_tag, auto gen_tag, auto body_tag) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr bool GEN = decltype(gen_tag)::value;
+    constexpr bool BODY = decltype(body_tag)::value;
     load_frags(f1, q, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(f0);
     if constexpr (NEXT) {
-      if (P + s + 1 >= 4) wait_stage();  // else covered by the first code stage's wait
+      if constexpr (BODY) wait_stage();
+      else if (P + s + 1 >= 4) wait_stage();  // else covered by the first code stage's wait
       barrier();
       if constexpr (GEN) dma_stage(q + 3);
       else dma_code(q + 3);
@@ -349,13 +353,17 @@ __global__ __launch_bounds__(F4_THREADS) void fp4_gemm_kernel(
     // code stage s reads position P + s + 1 and issues P + s + 3 (stage s + 3)
     using T_ = std::true_type;
     using F_ = std::false_type;
+    int s = 0;
+    // a stage whose next position is among the tile's first four
 #pragma nounroll
-    for (int s = 0; s + 3 < S; ++s, ++q) code_stage(q, s, T_{}, F_{});
+    for (; s < 3 - P && s + 3 < S; ++s, ++q) code_stage(q, s, T_{}, F_{}, F_{});
+#pragma nounroll
+    for (; s + 3 < S; ++s, ++q) code_stage(q, s, T_{}, F_{}, T_{});
     // the last two stages with a successor issue beyond the tile's code
     // stages (S == 2: one, S == 1: none)
-    if (S > 2) code_stage(q++, S - 3, T_{}, T_{});
-    if (S > 1) code_stage(q++, S - 2, T_{}, T_{});
-    code_stage(q, S - 1, F_{}, F_{});
+    if (S > 2) code_stage(q++, S - 3, T_{}, T_{}, F_{});
+    if (S > 1) code_stage(q++, S - 2, T_{}, T_{}, F_{});
+    code_stage(q, S - 1, F_{}, F_{}, F_{});
     ++q;
 
     const int64_t mbase = (int64_t)cur_t.tm * F4_BM + wm * 64;

@@ -259,18 +259,18 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   const int fb8 = SLOT_A + (wn * 3) * I4_BLOCK + h * 768 + 512 + l32 * 8;
   const int fsb = SLOT_A + (wn * 3) * I4_BLOCK + 1536 + lane * 8;
 
-  v8i af[2], bf[3];
+  v6i af[2], bf[3];
   v4s sa[2], sb[3];
   auto load_a = [&](const uint8_t* sp, int tr) {
     const v4u x = *reinterpret_cast<const v4u*>(sp + fa + tr * I4_BLOCK);
     const v2u y = *reinterpret_cast<const v2u*>(sp + fa8 + tr * I4_BLOCK);
-    af[tr] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
+    af[tr] = v6i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
     sa[tr] = *reinterpret_cast<const v4s*>(sp + fsa + tr * I4_BLOCK);
   };
   auto load_b = [&](const uint8_t* sp, int tc) {
     const v4u x = *reinterpret_cast<const v4u*>(sp + fb + tc * I4_BLOCK);
     const v2u y = *reinterpret_cast<const v2u*>(sp + fb8 + tc * I4_BLOCK);
-    bf[tc] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
+    bf[tc] = v6i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
     sb[tc] = *reinterpret_cast<const v4s*>(sp + fsb + tc * I4_BLOCK);
   };
   auto slot_ptr = [&](int q) { return lds + (q & (I4_NSLOT - 1)) * SLOT_BYTES; };
@@ -284,8 +284,8 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   // tile t of a wave = (t / 3, t % 3); its P and S live in p/sc[t & 1]
   auto mfma_p = [&](int t) {
     const int tr = t / 3, tc = t % 3, bb = t & 1;
-    p[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[tc], af[tr], zero, FP6_FMT, FP6_FMT,
-                                                            0, I4_SCALE_BYTE, 0, I4_SCALE_BYTE);
+    p[bb] = svdq_mfma_scale_e2m3(bf[tc], af[tr], zero, FP6_FMT, FP6_FMT,
+                                 0, I4_SCALE_BYTE, 0, I4_SCALE_BYTE);
   };
   auto mfma_s = [&](int t) {
     const int tr = t / 3, tc = t % 3, bb = t & 1;
@@ -322,17 +322,29 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
   // its stage is in registers once tile 2's MFMAs have issued: LDS reads
   // return in order), moves the DMA window to the next tile and issues that
   // tile's third and fourth positions, ahead of the output stores.
-  auto group = [&](int q, int g, auto next_tag, int k) {
+  // BODY: a group known to be neither among a tile's first four positions
+  // nor one of its last three, so that its wait and DMA take the body forms
+  // without a branch: the loop over such groups is one basic block, and the
+  // compiler keeps each step's MFMAs where they are written instead of
+  // sinking them past the barrier into the block that reads their results.
+  auto group = [&](int q, int g, auto next_tag, auto body_tag, int k) {
     constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr bool BODY = decltype(body_tag)::value;
     const uint8_t* nsp = slot_ptr(q + 1);
     step(1, 0, [] {});
     step(2, 1, [&] {  // A tile row 0 is free
       if constexpr (NEXT) {
-        if (P + g + 1 < 4) wait_head2();  // the next position is the tile's third or fourth
-        else wait_stage();
-        barrier();
-        if (g + 3 < G) dma_code(q + 3);
-        else dma_stage(q + 3);
+        if constexpr (BODY) {
+          wait_stage();
+          barrier();
+          dma_code(q + 3);
+        } else {
+          if (P + g + 1 < 4) wait_head2();  // the next position is the tile's third or fourth
+          else wait_stage();
+          barrier();
+          if (g + 3 < G) dma_code(q + 3);
+          else dma_stage(q + 3);
+        }
         load_a(nsp, 0);
       } else if (k + 1 < my_tiles) {
         barrier();
@@ -427,9 +439,16 @@ __global__ __launch_bounds__(I4_THREADS) void int4_gemm_kernel(
     const int64_t mbase = (int64_t)cur_t.tm * I4_BM + wm * 64;
     const int nbase = cur_t.tn * I4_BN + wn * 96;
     int g = 0;
+    // the groups whose next position is among the tile's first four
+    // (g < 3 - P), the body, then the two groups whose DMA lies past the
+    // tile's code groups, and the last
 #pragma nounroll
-    for (; g + 1 < G; ++g, ++q) group(q, g, T_{}, k);
-    group(q, g, F_{}, k);
+    for (; g < 3 - P && g + 1 < G; ++g, ++q) group(q, g, T_{}, F_{}, k);
+#pragma nounroll
+    for (; g + 3 < G; ++g, ++q) group(q, g, T_{}, T_{}, k);
+#pragma nounroll
+    for (; g + 1 < G; ++g, ++q) group(q, g, T_{}, F_{}, k);
+    group(q, g, F_{}, F_{}, k);
     ++q;
 
     store_tiles_t<2, 3>(acc, M, N, mbase, nbase, lane, out_f32 != 0, Y);

@@ -204,18 +204,18 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
   // fragments: A (activation) rows t and B (weight) columns t of the wave,
   // each with its bf16 scale operand; one set, each fragment reloaded for the
   // next group right after its last use in the current one
-  v8i af[2], bf[2];
+  v6i af[2], bf[2];
   v4s_fg sa[2], sb[2];
   auto load_a = [&](const uint8_t* sp, int t) {
     const v4u x = *reinterpret_cast<const v4u*>(sp + fa + t * I4_BLOCK);
     const v2u y = *reinterpret_cast<const v2u*>(sp + fa8 + t * I4_BLOCK);
-    af[t] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
+    af[t] = v6i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
     sa[t] = *reinterpret_cast<const v4s_fg*>(sp + fsa + t * I4_BLOCK);
   };
   auto load_b = [&](const uint8_t* sp, int t) {
     const v4u x = *reinterpret_cast<const v4u*>(sp + fb + t * I4_BLOCK);
     const v2u y = *reinterpret_cast<const v2u*>(sp + fb8 + t * I4_BLOCK);
-    bf[t] = v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
+    bf[t] = v6i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
     sb[t] = *reinterpret_cast<const v4s_fg*>(sp + fsb + t * I4_BLOCK);
   };
   auto slot_ptr = [&](int g) { return ring + (g & (FG_NSLOT - 1)) * FG_SLOT; };
@@ -232,8 +232,8 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
   v16f p[2], sc[2];
   auto mf = [&](int t) {  // the MFMAs of tile t = (t / 2, t % 2) into buffer t & 1
     const int tr = t >> 1, tc = t & 1, bb = t & 1;
-    p[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[tc], af[tr], zero, FG_FP6, FG_FP6,
-                                                            0, FG_SCALE_BYTE, 0, FG_SCALE_BYTE);
+    p[bb] = svdq_mfma_scale_e2m3(bf[tc], af[tr], zero, FG_FP6, FG_FP6,
+                                 0, FG_SCALE_BYTE, 0, FG_SCALE_BYTE);
     sc[bb] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sb[tc], sa[tr], zero, 0, 0, 0);
   };
   auto fm = [&](int t) {
