@@ -33,6 +33,8 @@
 // are added in tile order by fg_finish_t_kernel into the image's T halves.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "gelu_table.h"
 #include "image.h"
@@ -252,14 +254,24 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
   load_a(slot_ptr(0), 1);
   load_b(slot_ptr(0), 0);
   load_b(slot_ptr(0), 1);
-  for (int g = 0; g < G; ++g) {
-    const bool more = g + 1 < G;
+  // BODY: g + 4 < G, so the wait counts two younger stages and a DMA is
+  // issued; the loop over such groups then has no branch and the compiler
+  // keeps the MFMAs ahead of the barrier as written
+  auto group = [&](int g, auto body_tag) {
+    constexpr bool BODY = decltype(body_tag)::value;
+    const bool more = BODY || g + 1 < G;
     const uint8_t* nsp = slot_ptr(g + 1);
     mf(0);
     mf(1);
     if (more) {
-      wait_stage(g + 1);
-      if (g + 4 < G) dma_stage(g + 4);
+      if constexpr (BODY) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        dma_stage(g + 4);
+      } else {
+        wait_stage(g + 1);
+        if (g + 4 < G) dma_stage(g + 4);
+      }
       load_a(nsp, 0);  // row 0: last used by tile 1
     }
     fm(0);
@@ -273,7 +285,12 @@ __global__ __launch_bounds__(FG_THREADS) void fg_gemm_kernel(
     }
     fm(2);
     fm(3);
-  }
+  };
+  int g = 0;
+#pragma nounroll
+  for (; g + 4 < G; ++g) group(g, std::true_type{});
+#pragma nounroll
+  for (; g < G; ++g) group(g, std::false_type{});
 
   // ---- epilogue: the ring is free once every wave is past the last group
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
