@@ -26,6 +26,9 @@ namespace svdq {
 // {hi | hi << 16, lo}, lanes 32..63 {lo, 0}, so that with the activation
 // pattern {hi | lo << 16, hi} / {lo, 0} the K slots 0..3 of the
 // outer-product MFMA hold hi*hi, lo*hi, hi*lo, 0 and slot 4 lo*lo.
+// ACT: the activation pattern of the scale operand instead of the weight
+// one (lanes 0..31 {hi | lo << 16, hi}, lanes 32..63 {lo, 0}).
+template <bool ACT>
 __device__ __forceinline__ void int4_code_block(uint8_t* __restrict__ out, int lane, const v4u& w,
                                                 float sv) {
   const int h = lane >> 5, l32 = lane & 31;
@@ -43,14 +46,14 @@ __device__ __forceinline__ void int4_code_block(uint8_t* __restrict__ out, int l
   *reinterpret_cast<v2u*>(out + h * 768 + 512 + l32 * 8) = v2u{(uint32_t)f[4], (uint32_t)f[5]};
   const uint32_t hb = f32_to_bf16(sv);
   const uint32_t lb = f32_to_bf16(sv - bf16_to_f32(hb));
-  const v2u so = h == 0 ? v2u{hb | (hb << 16), lb} : v2u{lb, 0u};
+  const v2u so = h == 0 ? (ACT ? v2u{hb | (lb << 16), hb} : v2u{hb | (hb << 16), lb}) : v2u{lb, 0u};
   *reinterpret_cast<v2u*>(out + 1536 + lane * 8) = so;
 }
 
 // The code blocks of row tile rt, groups 4 quad .. 4 quad + 3 (MODE 0 INT4,
 // 1 FP4: the 16 code bytes as they are and the E8M0 byte of row l%32, K half
 // l/32).  Rows R .. RP-1 and groups past G come out as zeros.
-template <int MODE>
+template <int MODE, bool ACT>
 __device__ __forceinline__ void code_blocks(int64_t R, int64_t RT, int K, int64_t rt, int quad,
                                             const uint8_t* __restrict__ codes,
                                             const void* __restrict__ scales,
@@ -92,7 +95,7 @@ __device__ __forceinline__ void code_blocks(int64_t R, int64_t RT, int K, int64_
   const v4u cw = cst[l32][(2 * w + h) ^ (l32 & 7)];
   const int64_t blk = (int64_t)g * RT + rt;
   if constexpr (MODE == 0) {
-    int4_code_block(image + blk * I4_BLOCK, lane, cw, __uint_as_float(sst[l32][w]));
+    int4_code_block<ACT>(image + blk * I4_BLOCK, lane, cw, __uint_as_float(sst[l32][w]));
   } else {
     *reinterpret_cast<v4u*>(image + blk * F4_CBLOCK + lane * 16) = cw;
     image[scale_off + blk * F4_SBLOCK + lane] = (uint8_t)sst[l32][2 * w + h];
@@ -149,8 +152,8 @@ __global__ __launch_bounds__(256) void weight_image_kernel(int N, int K, int ran
   if ((int64_t)blockIdx.x < ncode) {
     const int nq = ((K >> 6) + 3) >> 2;  // group quads per row tile
     const int64_t rt = (int64_t)blockIdx.x / nq;
-    code_blocks<MODE>(N, RT, K, rt, (int)((int64_t)blockIdx.x - rt * nq), codes, scales,
-                      img + wi.code, wi.scale);
+    code_blocks<MODE, false>(N, RT, K, rt, (int)((int64_t)blockIdx.x - rt * nq), codes, scales,
+                             img + wi.code, wi.scale);
     return;
   }
   const int64_t t = ((int64_t)blockIdx.x - ncode) * 256 + threadIdx.x;
@@ -171,6 +174,73 @@ hipError_t launch_prepare_weight(int mode, int N, int K, int rank, const uint8_t
   else
     hipLaunchKernelGGL(weight_image_kernel<1>, grid, dim3(256), 0, s, N, K, rank, wi.CT, ncode,
                        wcodes, wscales, lora_up, bias, img, wi);
+  return hipGetLastError();
+}
+
+// The activation image from the row-major codes, scales and T (rather than
+// from X, as the activation pass writes it): workgroups [0, ncode) write the
+// code blocks as for the weight image, with the activation pattern of the
+// INT4 scale operand; the rest the low-rank blocks, one 16-byte lane entry
+// of T hi and of T lo per thread (slice q, row tile rt, lane l: row
+// 32 rt + l%32, ranks 16 q + 8 (l/32) .. +7; rows past M are zero).  The
+// partial-sum region of the image is not used by the GEMM and is left as
+// it is.
+template <int MODE>
+__global__ __launch_bounds__(256) void act_image_kernel(int64_t M, int K, int rank, int64_t ncode,
+                                                        const uint8_t* __restrict__ codes,
+                                                        const void* __restrict__ scales,
+                                                        const float* __restrict__ T,
+                                                        uint8_t* __restrict__ img, ActImage ai) {
+  if ((int64_t)blockIdx.x < ncode) {
+    const int nq = ((K >> 6) + 3) >> 2;  // group quads per row tile
+    const int64_t rt = (int64_t)blockIdx.x / nq;
+    code_blocks<MODE, true>(M, ai.RT, K, rt, (int)((int64_t)blockIdx.x - rt * nq), codes, scales,
+                            img + ai.code, ai.scale);
+    return;
+  }
+  const int64_t t = ((int64_t)blockIdx.x - ncode) * 256 + threadIdx.x;
+  const int64_t nlr = (int64_t)(rank / 16) * ai.RT * 64;
+  if (t >= nlr) return;
+  const int64_t blk = t >> 6;  // (q, rt)
+  const int l = (int)(t & 63);
+  const int q = (int)(blk / ai.RT);
+  const int64_t rt = blk - (int64_t)q * ai.RT;
+  const int64_t m = rt * 32 + (l & 31);
+  v4f a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+  if (m < M) {
+    const float* tr = T + m * rank + 16 * q + 8 * (l >> 5);
+    a = *reinterpret_cast<const v4f*>(tr);
+    b = *reinterpret_cast<const v4f*>(tr + 4);
+  }
+  // hi = bf16_RNE(T), lo = bf16_RNE(T - hi), as the activation pass writes them
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+    hi[i] = h0 | (h1 << 16);
+    lo[i] = f32_to_bf16(v[2 * i] - bf16_to_f32(h0)) |
+            (f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1)) << 16);
+  }
+  uint8_t* out = img + ai.lr + blk * LR_XBLOCK;
+  *reinterpret_cast<v4u*>(out + 16 * l) = v4u{hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<v4u*>(out + 1024 + 16 * l) = v4u{lo[0], lo[1], lo[2], lo[3]};
+}
+
+hipError_t launch_act_image_from_codes(int mode, int64_t M, int K, int rank, const uint8_t* xcodes,
+                                       const void* xscales, const float* T, void* ximage,
+                                       hipStream_t s) {
+  const ActImage ai = act_image(mode, M, K, rank);
+  uint8_t* img = reinterpret_cast<uint8_t*>(ximage);
+  const int64_t ncode = (int64_t)((K / 64 + 3) / 4) * ai.RT;
+  const int64_t nthreads = (int64_t)(rank / 16) * ai.RT * 64;
+  const dim3 grid((unsigned)(ncode + (nthreads + 255) / 256));
+  if (mode == 0)
+    hipLaunchKernelGGL(act_image_kernel<0>, grid, dim3(256), 0, s, M, K, rank, ncode, xcodes,
+                       xscales, T, img, ai);
+  else
+    hipLaunchKernelGGL(act_image_kernel<1>, grid, dim3(256), 0, s, M, K, rank, ncode, xcodes,
+                       xscales, T, img, ai);
   return hipGetLastError();
 }
 

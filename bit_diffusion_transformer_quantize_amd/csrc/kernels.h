@@ -37,6 +37,12 @@ hipError_t launch_lowrank_down(int rank, int64_t M, int K, const uint16_t* X,
                                const float* lambda, const uint16_t* lora_down, float* T,
                                bool gelu, hipStream_t s);
 
+// The activation image from the row-major codes, scales and T (T null when
+// rank == 0); the partial-sum region is not written.
+hipError_t launch_act_image_from_codes(int mode, int64_t M, int K, int rank, const uint8_t* xcodes,
+                                       const void* xscales, const float* T, void* ximage,
+                                       hipStream_t s);
+
 hipError_t launch_prepare_weight(int mode, int N, int K, int rank, const uint8_t* wcodes,
                                  const void* wscales, const uint16_t* lora_up,
                                  const uint16_t* bias, void* wimage, hipStream_t s);

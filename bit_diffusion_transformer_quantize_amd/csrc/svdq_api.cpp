@@ -293,6 +293,52 @@ svdq_status svdq_linear_forward_packed(const svdq_desc* d, int64_t M, const void
 }
 
 namespace {
+// The row-major form's workspace: the activation image, then (at a 256-byte
+// boundary) the prepared weight.
+size_t rowmajor_xbytes(const svdq_desc* d, int64_t M) {
+  return (svdq::act_image_bytes(d->mode, M, d->K, d->rank) + 255) / 256 * 256;
+}
+}  // namespace
+
+svdq_status svdq_linear_rowmajor_workspace_size(const svdq_desc* d, int64_t M, size_t* bytes) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows_k(M, d->K));
+  if (bytes == nullptr) return SVDQ_ERR_ARG;
+  *bytes = rowmajor_xbytes(d, M) + svdq::weight_image_bytes(d->mode, d->N, d->K, d->rank);
+  return SVDQ_OK;
+}
+
+svdq_status svdq_linear_forward_rowmajor(const svdq_desc* d, int64_t M, const uint8_t* xcodes,
+                                         const void* xscales, const float* T,
+                                         const uint8_t* wcodes, const void* wscales,
+                                         const uint16_t* lora_up, const uint16_t* bias, void* Y,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  SVDQ_TRY(check_desc(d));
+  SVDQ_TRY(check_rows_k(M, d->K));
+  if (M > (int64_t(1) << 46) / d->N) return SVDQ_ERR_SHAPE;
+  if (!ptr_ok(xcodes) || !ptr_ok(xscales) || !ptr_ok(wcodes) || !ptr_ok(wscales) ||
+      !ptr_ok(Y) || !ptr_ok(workspace) || !opt_ok(bias))
+    return SVDQ_ERR_ARG;
+  if (d->rank > 0 ? (!ptr_ok(T) || !ptr_ok(lora_up)) : (T != nullptr || lora_up != nullptr))
+    return SVDQ_ERR_ARG;
+  const size_t xb = rowmajor_xbytes(d, M);
+  if (workspace_bytes < xb + svdq::weight_image_bytes(d->mode, d->N, d->K, d->rank))
+    return SVDQ_ERR_ARG;
+  const bool f32 = (d->flags & SVDQ_FLAG_OUT_F32) != 0u;
+  SVDQ_TRY(check_device());
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* ximage = reinterpret_cast<uint8_t*>(workspace);
+  uint8_t* wimage = ximage + xb;
+  SVDQ_TRY(from_hip(svdq::launch_act_image_from_codes(d->mode, M, d->K, d->rank, xcodes, xscales,
+                                                      T, ximage, s)));
+  SVDQ_TRY(from_hip(svdq::launch_prepare_weight(d->mode, d->N, d->K, d->rank, wcodes, wscales,
+                                                lora_up, bias, wimage, s)));
+  if (d->mode == SVDQ_MODE_INT4)
+    return from_hip(svdq::launch_int4_forward(f32, M, d->N, d->K, d->rank, ximage, wimage, Y, s));
+  return from_hip(svdq::launch_fp4_forward(f32, M, d->N, d->K, d->rank, ximage, wimage, Y, s));
+}
+
+namespace {
 // An INT4 up layer feeding an INT4 down layer whose input is GELU of the up
 // layer's output (down->K == up->N), down rank at most 128.
 svdq_status check_mlp_pair(const svdq_desc* up, const svdq_desc* down) {

@@ -62,6 +62,10 @@ _SIGNATURES = {
     "svdq_linear_forward": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _vp, _vp]),
     "svdq_linear_forward_packed": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _vp, _vp, _vp, _vp,
                                                   _sz, _vp, _vp]),
+    "svdq_linear_rowmajor_workspace_size": (ctypes.c_int, [_DESC, _i64,
+                                                           ctypes.POINTER(ctypes.c_size_t)]),
+    "svdq_linear_forward_rowmajor": (ctypes.c_int, [_DESC, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _vp, _vp, _vp, _sz, _vp]),
     "svdq_gelu_quantize_workspace_size": (ctypes.c_int, [_DESC, _i64, _DESC,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_linear_forward_gelu_quantize": (ctypes.c_int, [_DESC, _i64, _vp, _sz, _vp, _sz, _DESC, _vp,
@@ -337,6 +341,41 @@ def svdq_gelu_quantize_workspace_size(up: SvdqDesc, M: int, down: SvdqDesc) -> i
            load().svdq_gelu_quantize_workspace_size(ctypes.byref(up), M, ctypes.byref(down),
                                                     ctypes.byref(n)))
     return n.value
+
+
+def svdq_linear_rowmajor_workspace_size(d: SvdqDesc, M: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("svdq_linear_rowmajor_workspace_size",
+           load().svdq_linear_rowmajor_workspace_size(ctypes.byref(d), M, ctypes.byref(n)))
+    return n.value
+
+
+def svdq_linear_forward_rowmajor(d: SvdqDesc, xcodes, xscales, T, wcodes, wscales, lora_up=None,
+                                 bias=None, workspace=None, Y=None):
+    """The layer from the row-major codes, scales and T of both sides (the
+    images are written into workspace, allocated when None); returns Y."""
+    M = xcodes.shape[0]
+    N, K, r = d.N, d.K, d.rank
+    out_dtype = torch.float32 if (d.flags & SVDQ_FLAG_OUT_F32) else torch.bfloat16
+    _need(xcodes, "xcodes", torch.uint8, (M, K // 2))
+    _need(xscales, "xscales", scale_dtype(d.mode), (M, scale_cols(d.mode, K)))
+    _need(T, "T", torch.float32, (M, r), optional=r == 0)
+    _need(wcodes, "wcodes", torch.uint8, (N, K // 2))
+    _need(wscales, "wscales", scale_dtype(d.mode), (N, scale_cols(d.mode, K)))
+    _need(lora_up, "lora_up", torch.bfloat16, (N, r), optional=r == 0)
+    _need(bias, "bias", torch.bfloat16, (N,), optional=True)
+    if workspace is None:
+        workspace = torch.empty(svdq_linear_rowmajor_workspace_size(d, M), dtype=torch.uint8,
+                                device=xcodes.device)
+    _need(workspace, "workspace", torch.uint8)
+    if Y is None:
+        Y = torch.empty(M, N, dtype=out_dtype, device=xcodes.device)
+    _need(Y, "Y", out_dtype, (M, N))
+    _check("svdq_linear_forward_rowmajor",
+           load().svdq_linear_forward_rowmajor(ctypes.byref(d), M, _p(xcodes), _p(xscales), _p(T),
+                                               _p(wcodes), _p(wscales), _p(lora_up), _p(bias), _p(Y),
+                                               _p(workspace), _nbytes(workspace), _stream()))
+    return Y
 
 
 def svdq_linear_forward_gelu_quantize(up: SvdqDesc, M: int, ximage, wimage, down: SvdqDesc,

@@ -407,6 +407,31 @@ svdq_status svdq_linear_forward_packed(const svdq_desc* desc, int64_t M, const v
                                        const uint16_t* bias, void* wscratch,
                                        size_t wscratch_bytes, void* Y, void* stream);
 
+/* The layer from the tensors of the row-major ABI: the activation codes and
+ * scales of svdq_quantize_act (xcodes [M][K/2], xscales [M][K/64] float32
+ * (INT4) or [M][K/32] uint8 (FP4)), its down-projection T (float32 [M][r]),
+ * the weight codes and scales of svdq_pack_weight, lora_up (bf16 [N][r])
+ * and the bias (bf16 [N] or NULL): the forward of the axbrief.com page,
+ * section "The Mechanics of 4-Bit Efficiency and SVDQuant" (4-bit weights
+ * and activations with a 16-bit low-rank branch), for callers that keep
+ * these tensors rather than the operand images.  Each call writes the
+ * activation image (codes, scales and T as above; a code 0 is written as
+ * +0) and the prepared weight into `workspace`, a device buffer of at least
+ * svdq_linear_rowmajor_workspace_size(desc, M) bytes (fewer is
+ * SVDQ_ERR_ARG, before anything is enqueued), then runs the GEMM: three
+ * kernels on the stream.  Y equals svdq_linear_forward on the images that
+ * svdq_quantize_act and svdq_prepare_weight write for the same tensors (up
+ * to the sign of an exact zero); T and lora_up are both required when
+ * rank > 0 and both NULL when rank == 0.  The workspace must not overlap
+ * the other buffers, and calls that share one overlap-free workspace run
+ * one at a time (overlapping calls race). */
+svdq_status svdq_linear_rowmajor_workspace_size(const svdq_desc* desc, int64_t M, size_t* bytes);
+svdq_status svdq_linear_forward_rowmajor(const svdq_desc* desc, int64_t M, const uint8_t* xcodes,
+                                         const void* xscales, const float* T,
+                                         const uint8_t* wcodes, const void* wscales,
+                                         const uint16_t* lora_up, const uint16_t* bias, void* Y,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* The MLP up-projection with the next layer's activation pass fused into
  * its epilogue (Nunchaku Lite page on axbrief.com, section "The Trade-off
  * Between Fused Kernels and Generality": neighbouring steps of the block

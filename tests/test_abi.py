@@ -255,6 +255,49 @@ def test_linear_forward_packed_validation():
     assert f(_d(), nx=_xb(M=1024)) == ARG                         # activation image for another M
 
 
+def _rb(M=256, **kw):
+    n = ctypes.c_size_t(0)
+    st = _lib().svdq_linear_rowmajor_workspace_size(_d(**kw), M, ctypes.byref(n))
+    return n.value if st == 0 else 0
+
+
+def test_linear_forward_rowmajor_validation():
+    """The row-major forward checks every tensor pointer, the rank rule for T
+    and lora_up, and the workspace against svdq_linear_rowmajor_workspace_size
+    (the activation image rounded up to 256 bytes, then the prepared weight),
+    before anything is enqueued."""
+    lib = _lib()
+    for kw in (dict(), dict(mode=1), dict(rank=0), dict(K=3072, N=9216, rank=32)):
+        for M in (1, 256, 300):
+            xb = (_xb(M=M, **kw) + 255) // 256 * 256
+            assert _rb(M=M, **kw) == xb + _wb(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.svdq_linear_rowmajor_workspace_size(_d(), 256, None) == ARG
+    assert lib.svdq_linear_rowmajor_workspace_size(_d(K=96), 256, ctypes.byref(n)) == SHAPE
+    assert lib.svdq_linear_rowmajor_workspace_size(_d(), 0, ctypes.byref(n)) == SHAPE
+    rb = _rb()
+
+    def f(d, M=256, xc=A, xs=A, T=A, wc=A, ws=A, lu=A, b=A, Y=A, w=A, nw=rb):
+        return lib.svdq_linear_forward_rowmajor(d, M, xc, xs, T, wc, ws, lu, b, Y, w, nw, None)
+
+    assert f(None) == ARG
+    assert f(_d(mode=3)) == ARG
+    assert f(_d(K=96)) == SHAPE
+    assert f(_d(), M=0) == SHAPE
+    assert f(_d(N=1 << 20), M=1 << 27) == SHAPE                   # output past 2^46 elements
+    for name in ("xc", "xs", "wc", "ws", "Y", "w"):
+        assert f(_d(), **{name: None}) == ARG, name
+        assert f(_d(), **{name: MIS}) == ARG, name
+    assert f(_d(), b=MIS) == ARG                                  # bias misaligned
+    assert f(_d(), T=None) == ARG                                 # rank > 0 needs T
+    assert f(_d(), lu=None) == ARG                                # and lora_up
+    assert f(_d(), T=MIS) == ARG
+    assert f(_d(rank=0), nw=_rb(rank=0)) == ARG                   # rank 0 takes neither
+    assert f(_d(rank=0), lu=None, nw=_rb(rank=0)) == ARG
+    assert f(_d(), nw=rb - 1) == ARG                              # workspace too small
+    assert f(_d(), M=300, nw=_rb(M=256)) == ARG                   # one sized for fewer rows
+
+
 @pytest.mark.parametrize("what,kw", [
     ("activation image for another M", dict(nx=_xb(M=1024))),
     ("activation image for another rank", dict(nx=_xb(rank=32))),
@@ -481,6 +524,8 @@ def test_no_device_is_a_hip_error():
     assert lib.svdq_prepare_weight(_d(), A, A, A, None, A, _wb(), None) == HIP
     assert lib.svdq_linear_forward_packed(_d(), 256, A, _xb(), A, A, A, None, A, _wb(), A,
                                           None) == HIP
+    assert lib.svdq_linear_forward_rowmajor(_d(), 256, A, A, A, A, A, A, None, A, A, _rb(),
+                                            None) == HIP
     assert lib.svdq_awq_pack_weight(64, 3072, A, A, A, A, None) == HIP
     assert lib.svdq_awq_linear(1, 64, 3072, A, A, A, A, None, 0, A, None) == HIP
     n = ctypes.c_size_t(0)

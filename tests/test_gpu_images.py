@@ -90,3 +90,64 @@ def test_images_decode_to_the_oracle(mode, M, K, N, rank):
         assert not w["lora_up"][N:].any()
     assert np.array_equal(w["bias"][:N], bb), "bias in the image"
     assert not w["bias"][N:].any() and not w["tail"].any(), "bias padding and tail"
+
+
+@pytest.mark.parametrize("mode,M,K,N,rank", [CASES[0], CASES[1], CASES[3], CASES[4]])
+def test_rowmajor_workspace_images_decode_to_the_oracle(mode, M, K, N, rank):
+    """svdq_linear_forward_rowmajor writes both images into its workspace
+    (the activation image, then the prepared weight at the next 256-byte
+    boundary) from the oracle's own row-major tensors: decoded, they hold
+    those tensors bit for bit (T's halves: the split of the fp32 T handed
+    over), zero padding included."""
+    from bit_diffusion_transformer_quantize_amd import svdq as S
+    from image_decode import act_layout, weight_layout
+    from layer_util import to_dev_bf16
+    print("[case] rowmajor workspace images", mode, M, K, N, rank, flush=True)
+    spec = WL.LinearSpec(f"rmimg_{mode}_{M}x{K}x{N}_r{rank}", M, K, N, rank, mode,
+                         x_outliers=4, x_factor=50.0)
+    X, W, b = WL.draw(spec, seed=13)
+    xb, wb, bb = WL.bits(X), WL.bits(W), WL.bits(b)
+    if rank > 0:
+        lam, L1, L2, wc_o, ws_o = oracle_offline(xb, wb, rank, mode)
+    else:
+        lam = O.calibrate_lambda(xb, wb)
+        L1 = np.zeros((K, 0), np.uint16)
+        L2 = np.zeros((0, N), np.uint16)
+        wc_o, ws_o = O.pack_weight(wb, lam, L1, L2, mode)
+    xc_o, xs_o, T_o, _ = O.quantize_act(xb, lam, L1 if rank > 0 else None, mode)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    T32 = T_o.astype(np.float32) if rank > 0 else None
+    d = S.desc(mode, K, N, rank)
+    ws = torch.full((S.svdq_linear_rowmajor_workspace_size(d, M),), 0xA5, dtype=torch.uint8,
+                    device=DEV)
+    S.svdq_linear_forward_rowmajor(d, t(xc_o), t(xs_o), None if T32 is None else t(T32), t(wc_o),
+                                   t(ws_o), to_dev_bf16(L2.T, DEV) if rank > 0 else None,
+                                   b.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    buf = np_(ws)
+    al, wl = act_layout(mode, M, K, rank), weight_layout(mode, N, K, rank)
+    xoff = (al["bytes"] + 255) // 256 * 256
+    # the partial-sum region of the activation image is not the GEMM's input
+    # and is not written; compare up to it
+    a = decode_act_image(np.concatenate([buf[:al["tpart"]],
+                                         np.zeros(al["bytes"] - al["tpart"], np.uint8)]),
+                         mode, M, K, rank)
+    assert np.array_equal(a["codes"][:M], xc_o), "activation codes"
+    assert not a["codes"][M:].any(), "padding rows of the activation image"
+    if mode == "int4":
+        assert np.array_equal(a["scales"][:M], _scale_dwords(xs_o, "act")), "activation scales"
+    else:
+        assert np.array_equal(a["scales"][:M], xs_o), "activation scale bytes"
+    assert not a["scales"][M:].any()
+    if rank > 0:
+        hi, lo = _split_bf16(T32)
+        assert np.array_equal(a["t_hi"][:M], hi), "T high halves"
+        assert np.array_equal(a["t_lo"][:M], lo), "T low halves"
+        assert not a["t_hi"][M:].any() and not a["t_lo"][M:].any(), "T of padding rows"
+    w = decode_weight_image(buf[xoff:xoff + wl["bytes"]], mode, N, K, rank)
+    assert np.array_equal(w["codes"][:N], wc_o), "weight codes"
+    if mode == "int4":
+        assert np.array_equal(w["scales"][:N], _scale_dwords(ws_o, "weight")), "weight scales"
+    else:
+        assert np.array_equal(w["scales"][:N], ws_o), "weight scale bytes"
+    assert np.array_equal(w["bias"][:N], bb), "bias"
