@@ -197,11 +197,32 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
     for (int sb = 0; sb < NB; ++sb) load_x(sb, wave, na[sb], nb[sb], nok[sb]);
     // the first tile's reciprocals of lambda (column t*64 + lane of the range)
     rlam[rl_idx(lane)] = 1.0 / (double)nlam;
+    // The tiles of a wave: round-robin over the waves, except that with 16
+    // waves (four per SIMD) each of waves 12..15 hands its last tile (when
+    // it has two or more) to wave w - 12, which takes it after its own.  A
+    // SIMD issues its oldest ready wave first, so otherwise the youngest
+    // four waves finish about a tile and a half behind the oldest four and
+    // the workgroup waits for them at the T reduction.  Static, so the T
+    // sums keep one order from run to run.
+    auto next_tile = [&](int t) -> int {
+      if constexpr (QA_WAVES == 16) {
+        if (wave >= 12) return t + 32 < ntiles ? t + 16 : ntiles;
+        if (wave < 4) {
+          const int d0 = wave + 12;  // the donor's first tile
+          if ((t & 15) == d0) return ntiles;  // the donated tile comes last
+          if (t + 16 < ntiles) return t + 16;
+          if (d0 + 16 >= ntiles) return ntiles;  // the donor keeps its only tile
+          return d0 + 16 * ((ntiles - 1 - d0) / 16);
+        }
+      }
+      return t + QA_WAVES;
+    };
     int slot = 0;
-    for (int t = wave; t < ntiles; t += QA_WAVES) {
+    for (int t = wave; t < ntiles; t = next_tile(t)) {
       const double* rcur = rlam + slot * QA_RCP;
       __builtin_amdgcn_wave_barrier();
-      nlam = load_lam(t + QA_WAVES);  // the next tile's, made into reciprocals at the end
+      const int tn = next_tile(t);
+      nlam = load_lam(tn);  // the next tile's, made into reciprocals at the end
       uint32_t xwb[NB][8];
 #pragma unroll
       for (int sb = 0; sb < NB; ++sb) {
@@ -232,7 +253,7 @@ __global__ __launch_bounds__((QaShape<MODE, RB>::kThreads)) void quantize_act_ke
         lg[b][1] = load_l1(b, 1);
       }
 #pragma unroll
-      for (int sb = 0; sb < NB; ++sb) load_x(sb, t + QA_WAVES, na[sb], nb[sb], nok[sb]);  // next tile
+      for (int sb = 0; sb < NB; ++sb) load_x(sb, tn, na[sb], nb[sb], nok[sb]);  // next tile
       const int kl = j * 16;                // column within the tile
       const int k0 = kbeg + t * 64 + kl;  // column within the row
 
