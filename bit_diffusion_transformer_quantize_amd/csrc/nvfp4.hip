@@ -121,24 +121,28 @@ __global__ __launch_bounds__(256) void nvfp4_weight_quant_kernel(
 
 // ------------------------------------------------------------------ GEMM
 // A 256 x 256 output tile per workgroup (8 waves of 64 x 128, 2 x 4 MFMA
-// tiles each), K in steps of 32 (two blocks): every thread dequantizes one
-// block of 16 of X and one of W to bf16 in LDS (the next step's codes and
+// tiles each), K in steps of 64 (four blocks): every thread loads 16 bytes
+// of codes (two blocks of 16) and their two scale bytes of one X row and
+// one W row and dequantizes them to bf16 in LDS (the next step's codes and
 // scales are loaded while the current step runs), then each wave issues
-// 16 v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the
-// transposed accumulator layout of gemm_common.h).  The dequantization is
-// VALU work per element, so the tile is as large as the registers allow:
-// 128 elements dequantized per matrix instruction.  Epilogue: * g_x g_w,
-// + T L2 on the same instruction (T as a bf16 hi/lo split), + bias.
-constexpr int NV_BM = 256, NV_BN = 256, NV_KS = 32, NV_THREADS = 512;
+// 32 v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the
+// transposed accumulator layout of gemm_common.h).  Steps of 64 rather than
+// 32 halve the strided row loads and the barriers per K (14% less time at
+// the fused-projection shape; steps of 128 were slower again).  The
+// dequantization is VALU work per element, so the tile is as large as the
+// registers allow: 128 elements dequantized per matrix instruction.
+// Epilogue: * g_x g_w, + T L2 on the same instruction (T as a bf16 hi/lo
+// split), + bias.
+constexpr int NV_BM = 256, NV_BN = 256, NV_KS = 64, NV_THREADS = 512;
 // LDS holds each operand tile in the matrix instruction's fragment order:
-// 16-byte unit ((r / 32) * 2 + kb) * 64 + r % 32 + 32 * h holds row r's
-// eight values of half h of block kb, so a wave reads a fragment as 64
-// consecutive units and a thread writes its block as two units of a
-// lane-consecutive run (no bank conflicts either way).
-constexpr int NV_TILE_UNITS = NV_BM / 32 * 2 * 64;
+// 16-byte unit ((r / 32) * 4 + kb) * 64 + r % 32 + 32 * h holds row r's
+// eight values of half h of block kb of the step, so a wave reads a
+// fragment as 64 consecutive units and a thread writes each of its blocks
+// as two units of a lane-consecutive run (no bank conflicts either way).
+constexpr int NV_TILE_UNITS = NV_BM / 32 * 4 * 64;
 
 struct NvRaw {
-  v2u xc, wc;
+  v4u xc, wc;
   uint32_t xs, ws;
 };
 
@@ -195,23 +199,23 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
   const int64_t m0 = (int64_t)blockIdx.x * NV_BM;
   const int n0 = blockIdx.y * NV_BN;
   const int nbk = K / NV_BLOCK;
-  // this thread's block of each operand: row 32 * wave + lane % 32, block
-  // lane / 32 of the step; rows past M or N are read from the last row (their
+  // this thread's blocks of each operand: row 32 * wave + lane % 32, blocks
+  // 2 (lane / 32) and 2 (lane / 32) + 1 of the step; rows past M or N are read from the last row (their
   // outputs are not stored)
   const int lr = 32 * wave + (lane & 31), kb = lane >> 5;
   const int64_t xrow = std::min<int64_t>(m0 + lr, M - 1);
   const int64_t wrow = std::min(n0 + lr, N - 1);
-  const uint8_t* xcp = xcodes + xrow * (K / 2) + kb * 8;
-  const uint8_t* xsp = xscales + xrow * nbk + kb;
-  const uint8_t* wcp = wcodes + wrow * (K / 2) + kb * 8;
-  const uint8_t* wsp = wscales + wrow * nbk + kb;
+  const uint8_t* xcp = xcodes + xrow * (K / 2) + kb * 16;
+  const uint8_t* xsp = xscales + xrow * nbk + kb * 2;
+  const uint8_t* wcp = wcodes + wrow * (K / 2) + kb * 16;
+  const uint8_t* wsp = wscales + wrow * nbk + kb * 2;
   auto load = [&](int ks, NvRaw& r) {
-    r.xc = *reinterpret_cast<const v2u*>(xcp + ks * (NV_KS / 2));
-    r.wc = *reinterpret_cast<const v2u*>(wcp + ks * (NV_KS / 2));
-    r.xs = xsp[ks * 2];
-    r.ws = wsp[ks * 2];
+    r.xc = *reinterpret_cast<const v4u*>(xcp + ks * (NV_KS / 2));
+    r.wc = *reinterpret_cast<const v4u*>(wcp + ks * (NV_KS / 2));
+    r.xs = *reinterpret_cast<const uint16_t*>(xsp + ks * 4);
+    r.ws = *reinterpret_cast<const uint16_t*>(wsp + ks * 4);
   };
-  const int dst = (wave * 2 + kb) * 64 + (lane & 31);
+  const int dst = (wave * 4 + 2 * kb) * 64 + (lane & 31);
   v16f acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -227,26 +231,32 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
   for (int ks = 0; ks < nks; ++ks) {
     load(std::min(ks + 1, nks - 1), nxt);
     {
-      v4u a0, a1, b0, b1;
+      v4u a0, a1, a2, a3, b0, b1, b2, b3;
       // gfx950's fp8 conversion decodes an OCP E4M3 byte exactly (subnormals
       // included): the same value as e4m3_value in one instruction
-      nv_dequant16(cur.xc, __builtin_amdgcn_cvt_f32_fp8((int)cur.xs, 0), a0, a1);
-      nv_dequant16(cur.wc, __builtin_amdgcn_cvt_f32_fp8((int)cur.ws, 0), b0, b1);
+      nv_dequant16(v2u{cur.xc[0], cur.xc[1]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.xs, 0), a0, a1);
+      nv_dequant16(v2u{cur.xc[2], cur.xc[3]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.xs, 1), a2, a3);
+      nv_dequant16(v2u{cur.wc[0], cur.wc[1]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.ws, 0), b0, b1);
+      nv_dequant16(v2u{cur.wc[2], cur.wc[3]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.ws, 1), b2, b3);
       xs_l[dst] = a0;
       xs_l[dst + 32] = a1;
+      xs_l[dst + 64] = a2;
+      xs_l[dst + 96] = a3;
       ws_l[dst] = b0;
       ws_l[dst + 32] = b1;
+      ws_l[dst + 64] = b2;
+      ws_l[dst + 96] = b3;
     }
     __syncthreads();
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
+    for (int k2 = 0; k2 < 4; ++k2) {
       v8bf af[4], bfr[2];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        af[t] = __builtin_bit_cast(v8bf, ws_l[((wn * 4 + t) * 2 + k2) * 64 + lane]);
+        af[t] = __builtin_bit_cast(v8bf, ws_l[((wn * 4 + t) * 4 + k2) * 64 + lane]);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        bfr[t] = __builtin_bit_cast(v8bf, xs_l[((wm * 2 + t) * 2 + k2) * 64 + lane]);
+        bfr[t] = __builtin_bit_cast(v8bf, xs_l[((wm * 2 + t) * 4 + k2) * 64 + lane]);
 #pragma unroll
       for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
