@@ -123,18 +123,22 @@ __global__ __launch_bounds__(256) void nvfp4_weight_quant_kernel(
 // A 256 x 256 output tile per workgroup (8 waves of 64 x 128, 2 x 4 MFMA
 // tiles each), K in steps of 64 (four blocks): every thread loads 16 bytes
 // of codes (two blocks of 16) and their two scale bytes of one X row and
-// one W row and dequantizes them to bf16 in LDS (the next step's codes and
-// scales are loaded while the current step runs), then each wave issues
-// 32 v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the
-// transposed accumulator layout of gemm_common.h).  Steps of 64 rather than
-// 32 halve the strided row loads and the barriers per K (14% less time at
-// the fused-projection shape; steps of 128 were slower again).  The
+// one W row and dequantizes them to bf16 in LDS, then each wave issues 32
+// v_mfma_f32_32x32x16_bf16 with the weight as the A operand (the transposed
+// accumulator layout of gemm_common.h).  LDS holds two steps: while the
+// waves' matrix instructions read step ks, each thread dequantizes step
+// ks + 1 (its codes loaded during step ks - 1) into the other buffer, so
+// the vector and matrix work overlap and one barrier per step separates
+// them.  Steps of 64 rather than 32 halve the strided row loads and the
+// barriers per K (14% less time at the fused-projection shape; steps of 128
+// were slower again), and the second buffer took another 5%.  The
 // dequantization is VALU work per element, so the tile is as large as the
 // registers allow: 128 elements dequantized per matrix instruction.
 // Epilogue: * g_x g_w, + T L2 on the same instruction (T as a bf16 hi/lo
 // split), + bias.
 constexpr int NV_BM = 256, NV_BN = 256, NV_KS = 64, NV_THREADS = 512;
-// LDS holds each operand tile in the matrix instruction's fragment order:
+// LDS holds each operand tile of a step in the matrix instruction's
+// fragment order:
 // 16-byte unit ((r / 32) * 4 + kb) * 64 + r % 32 + 32 * h holds row r's
 // eight values of half h of block kb of the step, so a wave reads a
 // fragment as 64 consecutive units and a thread writes each of its blocks
@@ -192,8 +196,8 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
     const float* __restrict__ gw, const float* __restrict__ T,
     const uint16_t* __restrict__ lora_up, const uint16_t* __restrict__ bias,
     void* __restrict__ Y) {
-  __shared__ v4u xs_l[NV_TILE_UNITS];
-  __shared__ v4u ws_l[NV_TILE_UNITS];
+  __shared__ v4u xs_l[2][NV_TILE_UNITS];
+  __shared__ v4u ws_l[2][NV_TILE_UNITS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.x * NV_BM;
@@ -225,46 +229,55 @@ __global__ __launch_bounds__(NV_THREADS) void nvfp4_gemm_kernel(
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
   const int nks = K / NV_KS;
-  NvRaw cur, nxt;
-  load(0, cur);
+  // dequantize a step's raw codes into buffer b; gfx950's fp8 conversion
+  // decodes an OCP E4M3 byte exactly (subnormals included): the same value
+  // as e4m3_value in one instruction
+  auto stage = [&](const NvRaw& r, int b) {
+    v4u a0, a1, a2, a3, b0, b1, b2, b3;
+    nv_dequant16(v2u{r.xc[0], r.xc[1]}, __builtin_amdgcn_cvt_f32_fp8((int)r.xs, 0), a0, a1);
+    nv_dequant16(v2u{r.xc[2], r.xc[3]}, __builtin_amdgcn_cvt_f32_fp8((int)r.xs, 1), a2, a3);
+    nv_dequant16(v2u{r.wc[0], r.wc[1]}, __builtin_amdgcn_cvt_f32_fp8((int)r.ws, 0), b0, b1);
+    nv_dequant16(v2u{r.wc[2], r.wc[3]}, __builtin_amdgcn_cvt_f32_fp8((int)r.ws, 1), b2, b3);
+    xs_l[b][dst] = a0;
+    xs_l[b][dst + 32] = a1;
+    xs_l[b][dst + 64] = a2;
+    xs_l[b][dst + 96] = a3;
+    ws_l[b][dst] = b0;
+    ws_l[b][dst + 32] = b1;
+    ws_l[b][dst + 64] = b2;
+    ws_l[b][dst + 96] = b3;
+  };
+  NvRaw nxt;
+  {
+    NvRaw r0;
+    load(0, r0);
+    load(std::min(1, nks - 1), nxt);
+    stage(r0, 0);
+  }
   const int l32 = lane & 31;
+  __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    load(std::min(ks + 1, nks - 1), nxt);
-    {
-      v4u a0, a1, a2, a3, b0, b1, b2, b3;
-      // gfx950's fp8 conversion decodes an OCP E4M3 byte exactly (subnormals
-      // included): the same value as e4m3_value in one instruction
-      nv_dequant16(v2u{cur.xc[0], cur.xc[1]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.xs, 0), a0, a1);
-      nv_dequant16(v2u{cur.xc[2], cur.xc[3]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.xs, 1), a2, a3);
-      nv_dequant16(v2u{cur.wc[0], cur.wc[1]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.ws, 0), b0, b1);
-      nv_dequant16(v2u{cur.wc[2], cur.wc[3]}, __builtin_amdgcn_cvt_f32_fp8((int)cur.ws, 1), b2, b3);
-      xs_l[dst] = a0;
-      xs_l[dst + 32] = a1;
-      xs_l[dst + 64] = a2;
-      xs_l[dst + 96] = a3;
-      ws_l[dst] = b0;
-      ws_l[dst + 32] = b1;
-      ws_l[dst + 64] = b2;
-      ws_l[dst + 96] = b3;
-    }
-    __syncthreads();
+    const int b = ks & 1;
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
       v8bf af[4], bfr[2];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        af[t] = __builtin_bit_cast(v8bf, ws_l[((wn * 4 + t) * 4 + k2) * 64 + lane]);
+        af[t] = __builtin_bit_cast(v8bf, ws_l[b][((wn * 4 + t) * 4 + k2) * 64 + lane]);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        bfr[t] = __builtin_bit_cast(v8bf, xs_l[((wm * 2 + t) * 4 + k2) * 64 + lane]);
+        bfr[t] = __builtin_bit_cast(v8bf, xs_l[b][((wm * 2 + t) * 4 + k2) * 64 + lane]);
 #pragma unroll
       for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
         for (int tc = 0; tc < 4; ++tc)
           acc[tr][tc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tc], bfr[tr], acc[tr][tc], 0, 0, 0);
     }
+    if (ks + 1 < nks) {
+      stage(nxt, b ^ 1);
+      load(std::min(ks + 2, nks - 1), nxt);
+    }
     __syncthreads();
-    cur = nxt;
   }
 
   const int kh = (lane >> 5) * 8;
